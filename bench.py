@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused dequantize-and-multiply path on one MI355X.
+
+One step = one pass of the decode workload: the three q4_0 GEMVs of a Llama-7B
+layer's shapes (4096x4096, 11008x4096, 4096x11008), batch 1, fp32 activations.
+Inputs are seeded synthetic planes, uploaded before timing; every step reads a
+different copy from a rotating pool of >= 1 GiB so that the 256 MB Infinity Cache
+cannot serve repeated reads (the weights come from HBM, as in decode).
+
+Prints ONE JSON line: value = algorithmic bytes (packed weights + scales + x + y)
+per step / time per step, in GB/s.  `roofline` covers the dominant kernel, timed
+with HIP events on the stream it runs on; `cpu_baseline` times the CPU oracle on
+a bounded sample of the same workload.  `secondary` carries the other workloads
+(q6_K GEMV, codebook MoE, additive GEMV, q6_K prefill GEMM) when they run.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
+POOL_BYTES = 1 << 30           # rotating pool: 4x the 256 MB Infinity Cache
+
+METRIC = "quantized GEMV HBM GB/s (% of peak); q6_K prefill GEMM int8 TOPS (% of peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only-primary", action="store_true", help="skip the secondary workloads")
+    return ap.parse_args()
+
+
+def dev_planes(planes: dict):
+    import torch
+    out = {}
+    for name, a in planes.items():
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.float16:
+            out[name] = torch.from_numpy(a.view(np.uint16).copy()).view(torch.float16).cuda()
+        else:
+            out[name] = torch.from_numpy(a.copy()).cuda()
+    return out
+
+
+def make_pool(qmv, fmt, n, k, seed, copies):
+    """`copies` distinct device copies of one generated matrix (device-to-device clones)."""
+    host = synth.gen_weights(fmt, n, k, seed=seed)
+    first = dev_planes(host)
+    pool = [qmv.QWeights(fmt, n, k, first)]
+    for _ in range(copies - 1):
+        pool.append(qmv.QWeights(fmt, n, k, {kk: v.clone() for kk, v in first.items()}))
+    return host, pool
+
+
+def time_launches(fn, count, warm=3):
+    """Average milliseconds per call of fn(i) over `count` calls, HIP events on the current stream."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(count):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / count
+
+
+def q4_0_workload(qmv, steps, warmup):
+    import torch
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]
+    per_set = sum(qmv.weight_bytes(synth.FMT_Q4_0, n, k) for n, k in shapes)
+    copies = max(2, -(-POOL_BYTES // per_set))
+    mats, xs, ys, algo = [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        _, pool = make_pool(qmv, synth.FMT_Q4_0, n, k, seed=i, copies=copies)
+        mats.append(pool)
+        xs.append(torch.from_numpy(synth.gen_x(1, k, seed=i)).cuda())
+        ys.append(torch.empty((1, n), dtype=torch.float32, device="cuda"))
+        algo.append(qmv.weight_bytes(synth.FMT_Q4_0, n, k) + 4 * k + 4 * n)
+
+    def step(i):
+        c = i % copies
+        for s in range(len(shapes)):
+            qmv.gemv(mats[s][c], xs[s], ys[s])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    bytes_step = sum(algo)
+    per_shape = []
+    for s, (n, k) in enumerate(shapes):
+        avg = time_launches(lambda i: qmv.gemv(mats[s][i % copies], xs[s], ys[s]), max(steps, 50))
+        per_shape.append({"shape": f"{n}x{k}", "bytes": algo[s], "avg_launch_ms": avg,
+                          "GBps": algo[s] / avg / 1e6, "frac": algo[s] / avg / 1e6 / HBM_PEAK_GBS,
+                          "path": (qmv.gemv(mats[s][0], xs[s], ys[s]), qmv.last_path())[1]})
+    torch.cuda.synchronize()
+    return {"ms_per_step": ms, "bytes_per_step": bytes_step, "GBps": bytes_step / ms / 1e6,
+            "copies": copies, "pool_bytes": copies * per_set, "shapes": per_shape}
+
+
+def cpu_baseline(seconds):
+    """The oracle on the same three matrices (all rows), repeated until `seconds` of work."""
+    import oracle
+    nth = max(1, min(16, os.cpu_count() or 1))
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]
+    mats, xs, nbytes = [], [], 0
+    for i, (n, k) in enumerate(shapes):
+        mats.append(oracle.Mat(synth.FMT_Q4_0, n, k, synth.gen_weights(synth.FMT_Q4_0, n, k, seed=i)))
+        xs.append(synth.gen_x(1, k, seed=i))
+        nbytes += (n * k // 32) * 18 + 4 * k + 4 * n
+    done, t0 = 0, time.perf_counter()
+    while True:
+        for m, x in zip(mats, xs):
+            oracle.gemv(m, x, oracle.F32, nthreads=nth)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": nbytes * done / el / 1e9, "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": f"{done} full pass(es) of the three q4_0 GEMVs (all rows), fp64 oracle, "
+                      f"{el:.1f} s, OpenMP over rows"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
+                          "(the path shards by output rows across GPUs, not measured here)"}))
+        sys.exit(2)
+    import torch
+    import bit_weight_quantized_dequant_amd as qmv
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    qmv.lib()
+    prim = q4_0_workload(qmv, a.steps, a.warmup)
+    dom = max(prim["shapes"], key=lambda s: s["avg_launch_ms"])
+    out = {
+        "metric": METRIC,
+        "value": round(prim["GBps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(prim["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "q4_0 GEMV batch 1, Llama-7B decode shapes 4096x4096 + 11008x4096 + "
+                               "4096x11008, fp32 x, rotating HBM pool",
+                   "batch": 1, "pool_bytes": prim["pool_bytes"], "pool_copies": prim["copies"],
+                   "bytes_per_step": prim["bytes_per_step"]},
+        "frac_of_peak": round(prim["GBps"] / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": f"q4_0 GEMV {dom['shape']} ({dom['path']})",
+                     "achieved": round(dom["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom["frac"], 4), "traffic": None},
+        "shapes": prim["shapes"],
+    }
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

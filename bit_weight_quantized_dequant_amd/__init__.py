@@ -1,0 +1,242 @@
+"""qmv -- fused dequantize-and-multiply of block-quantized weights on MI355X (gfx950).
+
+A thin ctypes binding over libqmv.so, whose C ABI is declared in include/qmv.h.
+This module only marshals arguments: every step of the computation runs in the
+library's HIP kernels.  PyTorch is used for device memory and the current stream.
+If libqmv.so is missing the binding raises; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+__all__ = [
+    "Q4_0", "Q6_K", "CB4", "AQ2X8", "F32", "BF16", "QmvError", "QWeights", "lib", "plane_bytes",
+    "weight_bytes", "validate", "gemv", "dequant", "quant_act", "workspace_bytes", "gemm",
+    "gemm_q8", "partials", "moe_ffn", "last_path", "strerror", "PLANES",
+]
+
+Q4_0, Q6_K, CB4, AQ2X8 = 1, 2, 3, 4
+F32, BF16 = 0, 1
+MAX_BATCH = 8
+
+# Plane names per format, in the order of the descriptor fields they fill.
+PLANES = {
+    Q4_0: {"qs": "codes", "d": "scales"},
+    Q6_K: {"ql": "codes", "qh": "codes_hi", "sc": "scales", "d": "super"},
+    CB4: {"idx": "codes", "cb": "codebook"},
+    AQ2X8: {"codes": "codes", "s": "scales", "cbk": "codebook"},
+}
+_PLANE_ID = {"codes": 0, "codes_hi": 1, "scales": 2, "super": 3, "codebook": 4}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmv.so")
+
+
+class QmvError(RuntimeError):
+    def __init__(self, code: int, call: str):
+        self.code = code
+        super().__init__(f"{call}: {strerror(code)} ({code})")
+
+
+class _W(C.Structure):
+    _fields_ = [("fmt", C.c_int32), ("n", C.c_int64), ("k", C.c_int64), ("codes", C.c_void_p),
+                ("codes_hi", C.c_void_p), ("scales", C.c_void_p), ("super", C.c_void_p),
+                ("codebook", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libqmv.so (built in-tree by build.py); raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libqmv.so not built ({LIB_PATH}); run "
+                              "`python bit_weight_quantized_dequant_amd/build.py`")
+        L = C.CDLL(LIB_PATH)
+        P, I32, I64 = C.c_void_p, C.c_int32, C.c_int64
+        L.qmv_plane_bytes.restype = I64
+        L.qmv_plane_bytes.argtypes = [I32, I64, I64, I32]
+        L.qmv_weight_bytes.restype = I64
+        L.qmv_weight_bytes.argtypes = [I32, I64, I64]
+        L.qmv_validate.restype = C.c_int
+        L.qmv_validate.argtypes = [P, I32, I32]
+        L.qmv_gemv.restype = C.c_int
+        L.qmv_gemv.argtypes = [P, I32, P, I32, P, P]
+        L.qmv_dequant.restype = C.c_int
+        L.qmv_dequant.argtypes = [P, P, P]
+        L.qmm_quant_act.restype = C.c_int
+        L.qmm_quant_act.argtypes = [P, I32, I64, P, P, P]
+        L.qmm_workspace_bytes.restype = I64
+        L.qmm_workspace_bytes.argtypes = [P, I32]
+        L.qmm_gemm.restype = C.c_int
+        L.qmm_gemm.argtypes = [P, I32, P, P, P, I64, P]
+        L.qmm_gemm_q8.restype = C.c_int
+        L.qmm_gemm_q8.argtypes = [P, I32, P, P, P, P]
+        L.qmm_partials.restype = C.c_int
+        L.qmm_partials.argtypes = [P, I32, P, P, P]
+        L.qmv_moe_ffn.restype = C.c_int
+        L.qmv_moe_ffn.argtypes = [P, P, P, I32, P, I32, P, I32, P, P, P]
+        L.qmv_last_path.restype = C.c_char_p
+        L.qmv_last_path.argtypes = []
+        L.qmv_strerror.restype = C.c_char_p
+        L.qmv_strerror.argtypes = [C.c_int]
+        L.qmv_version.restype = C.c_char_p
+        L.qmv_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().qmv_strerror(code).decode()
+
+
+def last_path() -> str:
+    return lib().qmv_last_path().decode()
+
+
+def plane_bytes(fmt: int, n: int, k: int, plane: str) -> int:
+    return lib().qmv_plane_bytes(fmt, n, k, _PLANE_ID[plane])
+
+
+def weight_bytes(fmt: int, n: int, k: int) -> int:
+    return lib().qmv_weight_bytes(fmt, n, k)
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+class QWeights:
+    """A quantized matrix on the device: format, shape and its plane tensors.
+
+    `planes` maps the format's plane names (see PLANES) to device tensors (or raw
+    integer device addresses).  The object keeps references to them.
+    """
+
+    def __init__(self, fmt: int, n: int, k: int, planes: dict):
+        self.fmt, self.n, self.k = fmt, n, k
+        self.planes = dict(planes)
+        fields = {f: 0 for f in ("codes", "codes_hi", "scales", "super", "codebook")}
+        for name, field in PLANES[fmt].items():
+            fields[field] = _ptr(self.planes.get(name))
+        self._s = _W(fmt, n, k, *(fields[f] for f in ("codes", "codes_hi", "scales", "super", "codebook")))
+
+    @property
+    def ref(self):
+        return C.byref(self._s)
+
+    def nbytes(self) -> int:
+        return weight_bytes(self.fmt, self.n, self.k)
+
+
+def _check(rc: int, call: str):
+    if rc != 0:
+        raise QmvError(rc, call)
+
+
+def validate(w: QWeights, m: int = 1, xt: int = F32) -> int:
+    return lib().qmv_validate(w.ref, m, xt)
+
+
+def _xt_of(x) -> int:
+    import torch
+    if x.dtype == torch.float32:
+        return F32
+    if x.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {x.dtype}")
+
+
+def gemv(w: QWeights, x, y=None, stream=None):
+    """y[m][n] = W x[m] for x of shape [m][k] (or [k]); returns y (fp32)."""
+    import torch
+    squeeze = x.dim() == 1
+    x2 = x.reshape(1, -1) if squeeze else x
+    m = x2.shape[0]
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
+    _check(lib().qmv_gemv(w.ref, m, _ptr(x2), _xt_of(x2), _ptr(y), _stream(stream)), "qmv_gemv")
+    return y[0] if squeeze else y
+
+
+def dequant(w: QWeights, out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((w.n, w.k), dtype=torch.float32, device="cuda")
+    _check(lib().qmv_dequant(w.ref, _ptr(out), _stream(stream)), "qmv_dequant")
+    return out
+
+
+def quant_act(x, xq=None, xs=None, stream=None):
+    import torch
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    _check(lib().qmm_quant_act(_ptr(x), m, k, _ptr(xq), _ptr(xs), _stream(stream)), "qmm_quant_act")
+    return xq, xs
+
+
+def workspace_bytes(w: QWeights, m: int) -> int:
+    return lib().qmm_workspace_bytes(w.ref, m)
+
+
+def gemm(w: QWeights, x, y=None, ws=None, stream=None):
+    import torch
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
+    need = workspace_bytes(w, m)
+    if need < 0:
+        raise QmvError(need, "qmm_workspace_bytes")
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().qmm_gemm(w.ref, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)), "qmm_gemm")
+    return y
+
+
+def gemm_q8(w: QWeights, xq, xs, y=None, stream=None):
+    import torch
+    m = xq.shape[0]
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=xq.device)
+    _check(lib().qmm_gemm_q8(w.ref, m, _ptr(xq), _ptr(xs), _ptr(y), _stream(stream)), "qmm_gemm_q8")
+    return y
+
+
+def partials(w: QWeights, xq, out=None, stream=None):
+    import torch
+    m = xq.shape[0]
+    if out is None:
+        out = torch.empty((m, w.n, w.k // 32), dtype=torch.int32, device=xq.device)
+    _check(lib().qmm_partials(w.ref, m, _ptr(xq), _ptr(out), _stream(stream)), "qmm_partials")
+    return out
+
+
+def moe_ffn(gate: QWeights, up: QWeights, down: QWeights, n_experts: int, ids, x, h=None, y=None,
+            stream=None):
+    """Routed-expert FFN for one token: returns (h [n_ids][d_ff], y [n_ids][d_model])."""
+    import torch
+    n_ids = ids.numel()
+    if h is None:
+        h = torch.empty((n_ids, gate.n), dtype=torch.float32, device=x.device)
+    if y is None:
+        y = torch.empty((n_ids, down.n), dtype=torch.float32, device=x.device)
+    _check(lib().qmv_moe_ffn(gate.ref, up.ref, down.ref, n_experts, _ptr(ids), n_ids, _ptr(x),
+                             _xt_of(x), _ptr(h), _ptr(y), _stream(stream)), "qmv_moe_ffn")
+    return h, y

@@ -1,0 +1,277 @@
+// api.cpp -- the C ABI of libqmv: host-side validation, size queries, dispatch and
+// path labels.  Validation is pure host code (no HIP call, no dereference of device
+// pointers) so every error path can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "qmv_internal.h"
+
+namespace qmv {
+
+namespace {
+thread_local char g_last_path[160] = "";
+
+bool debug_on() {
+    static const bool on = [] {
+        const char *e = std::getenv("QMV_DEBUG");
+        return e && std::strcmp(e, "0") != 0 && e[0] != '\0';
+    }();
+    return on;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int block_of(int32_t fmt) {
+    switch (fmt) {
+    case QMV_Q4_0: return 32;
+    case QMV_Q6_K: return 256;
+    case QMV_CB4: return 128;
+    case QMV_AQ2X8: return 8;
+    }
+    return 0;
+}
+}  // namespace
+
+const DeviceInfo &device_info() {
+    static DeviceInfo info = [] {
+        DeviceInfo d{65536, 256};
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            int v = 0;
+            if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+                d.lds_per_block = v;
+            if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+                d.num_cus = v;
+        }
+        return d;
+    }();
+    return info;
+}
+
+// Read on every call (unlike QMV_DEBUG) so a test can switch variants in one process.
+const char *forced_path() {
+    const char *e = std::getenv("QMV_FORCE_PATH");
+    return e ? e : "";
+}
+
+int finish_launch(const char *call, const qmv_weights *w, int m, const char *path) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        std::fprintf(stderr, "qmv: %s launch failed: %s\n", call, hipGetErrorString(e));
+        return QMV_ERR_HIP;
+    }
+    std::snprintf(g_last_path, sizeof g_last_path, "%s", path);
+    if (debug_on())
+        std::fprintf(stderr, "qmv: %s fmt=%d n=%lld k=%lld m=%d path=%s\n", call, w ? w->fmt : 0,
+                     w ? (long long)w->n : 0LL, w ? (long long)w->k : 0LL, m, path);
+    return QMV_OK;
+}
+
+}  // namespace qmv
+
+using namespace qmv;
+
+extern "C" {
+
+int64_t qmv_plane_bytes(int32_t fmt, int64_t n, int64_t k, int32_t plane) {
+    const int blk = block_of(fmt);
+    if (!blk) return QMV_ERR_FORMAT;
+    if (n <= 0 || k <= 0 || k % blk) return QMV_ERR_SHAPE;
+    switch (fmt) {
+    case QMV_Q4_0:
+        if (plane == QMV_PLANE_CODES) return n * k / 2;
+        if (plane == QMV_PLANE_SCALES) return n * (k / 32) * 2;
+        break;
+    case QMV_Q6_K:
+        if (plane == QMV_PLANE_CODES) return n * k / 2;
+        if (plane == QMV_PLANE_CODES_HI) return n * k / 4;
+        if (plane == QMV_PLANE_SCALES) return n * (k / 16);
+        if (plane == QMV_PLANE_SUPER) return n * (k / 256) * 2;
+        break;
+    case QMV_CB4:
+        if (plane == QMV_PLANE_CODES) return n * k / 2;
+        if (plane == QMV_PLANE_CODEBOOK) return n * (k / 128) * 32;
+        break;
+    case QMV_AQ2X8:
+        if (plane == QMV_PLANE_CODES) return n * (k / 8) * 2;
+        if (plane == QMV_PLANE_SCALES) return n * 2;
+        if (plane == QMV_PLANE_CODEBOOK) return 2 * 256 * 8 * 2;
+        break;
+    }
+    if (plane < 0 || plane > QMV_PLANE_CODEBOOK) return QMV_ERR_SHAPE;
+    return 0;
+}
+
+int64_t qmv_weight_bytes(int32_t fmt, int64_t n, int64_t k) {
+    int64_t total = 0;
+    for (int p = 0; p <= QMV_PLANE_CODEBOOK; p++) {
+        const int64_t b = qmv_plane_bytes(fmt, n, k, p);
+        if (b < 0) return b;
+        total += b;
+    }
+    return total;
+}
+
+int qmv_validate(const qmv_weights *w, int32_t m, int32_t xt) {
+    if (!w) return QMV_ERR_NULL;
+    const int blk = block_of(w->fmt);
+    if (!blk) return QMV_ERR_FORMAT;
+    if (w->n <= 0 || w->k <= 0 || w->k % blk) return QMV_ERR_SHAPE;
+    if (xt != QMV_F32 && xt != QMV_BF16) return QMV_ERR_DTYPE;
+    if (m < 1 || m > QMV_MAX_BATCH) return QMV_ERR_BATCH;
+    const void *need[5] = {w->codes, nullptr, nullptr, nullptr, nullptr};
+    switch (w->fmt) {
+    case QMV_Q4_0: need[1] = w->scales; break;
+    case QMV_Q6_K: need[1] = w->codes_hi; need[2] = w->scales; need[3] = w->super; break;
+    case QMV_CB4: need[1] = w->codebook; break;
+    case QMV_AQ2X8: need[1] = w->scales; need[2] = w->codebook; break;
+    }
+    const int nneed = w->fmt == QMV_Q6_K ? 4 : (w->fmt == QMV_AQ2X8 ? 3 : 2);
+    for (int i = 0; i < nneed; i++)
+        if (!need[i]) return QMV_ERR_NULL;
+    for (int i = 0; i < nneed; i++)
+        if (!aligned16(need[i])) return QMV_ERR_ALIGN;
+    if (w->n > INT32_MAX || w->k > INT32_MAX) return QMV_ERR_LIMIT;
+    return QMV_OK;
+}
+
+int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *y, void *stream) {
+    int rc = qmv_validate(w, m, xt);
+    if (rc) return rc;
+    if (!x || !y) return QMV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y)) return QMV_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    const char *path = nullptr;
+    switch (w->fmt) {
+    case QMV_Q4_0: path = launch_gemv_q4_0(w, m, x, xt, y, s); break;
+    case QMV_Q6_K: path = launch_gemv_q6k(w, m, x, xt, y, s); break;
+    case QMV_CB4: path = launch_gemv_cb4(w, m, x, xt, y, s); break;
+    case QMV_AQ2X8: path = launch_gemv_aq(w, m, x, xt, y, s); break;
+    }
+    if (!path) return QMV_ERR_LIMIT;
+    return finish_launch("qmv_gemv", w, m, path);
+}
+
+int qmv_dequant(const qmv_weights *w, float *out, void *stream) {
+    int rc = qmv_validate(w, 1, QMV_F32);
+    if (rc) return rc;
+    if (!out) return QMV_ERR_NULL;
+    if (!aligned16(out)) return QMV_ERR_ALIGN;
+    const char *path = launch_dequant(w, out, (hipStream_t)stream);
+    if (!path) return QMV_ERR_LIMIT;
+    return finish_launch("qmv_dequant", w, 1, path);
+}
+
+int qmm_quant_act(const float *x, int32_t m, int64_t k, int8_t *xq, float *xs, void *stream) {
+    if (!x || !xq || !xs) return QMV_ERR_NULL;
+    if (m < 1) return QMV_ERR_BATCH;
+    if (k <= 0 || k % 32) return QMV_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(xs)) return QMV_ERR_ALIGN;
+    const char *path = launch_quant_act(x, m, k, xq, xs, (hipStream_t)stream);
+    if (!path) return QMV_ERR_LIMIT;
+    return finish_launch("qmm_quant_act", nullptr, m, path);
+}
+
+int64_t qmm_workspace_bytes(const qmv_weights *w, int32_t m) {
+    if (!w) return QMV_ERR_NULL;
+    if (w->fmt != QMV_Q6_K) return QMV_ERR_FORMAT;
+    if (w->n <= 0 || w->k <= 0 || w->k % 256) return QMV_ERR_SHAPE;
+    if (m < 1) return QMV_ERR_BATCH;
+    // xq int8 [m][k], then xs fp32 [m][k/32] at a 256-byte aligned offset.
+    const int64_t xq = ((int64_t)m * w->k + 255) / 256 * 256;
+    return xq + (int64_t)m * (w->k / 32) * 4;
+}
+
+static int check_gemm(const qmv_weights *w, int32_t m) {
+    int rc = qmv_validate(w, 1, QMV_F32);
+    if (rc) return rc;
+    if (w->fmt != QMV_Q6_K) return QMV_ERR_FORMAT;
+    if (m < 1) return QMV_ERR_BATCH;
+    return QMV_OK;
+}
+
+int qmm_gemm_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *xs, float *y,
+                void *stream) {
+    int rc = check_gemm(w, m);
+    if (rc) return rc;
+    if (!xq || !xs || !y) return QMV_ERR_NULL;
+    if (!aligned16(xq) || !aligned16(xs) || !aligned16(y)) return QMV_ERR_ALIGN;
+    const char *path = launch_gemm_q6k(w, m, xq, xs, y, nullptr, (hipStream_t)stream);
+    if (!path) return QMV_ERR_LIMIT;
+    return finish_launch("qmm_gemm_q8", w, m, path);
+}
+
+int qmm_partials(const qmv_weights *w, int32_t m, const int8_t *xq, int32_t *i32, void *stream) {
+    int rc = check_gemm(w, m);
+    if (rc) return rc;
+    if (!xq || !i32) return QMV_ERR_NULL;
+    if (!aligned16(xq) || !aligned16(i32)) return QMV_ERR_ALIGN;
+    const char *path = launch_gemm_q6k(w, m, xq, nullptr, nullptr, i32, (hipStream_t)stream);
+    if (!path) return QMV_ERR_LIMIT;
+    return finish_launch("qmm_partials", w, m, path);
+}
+
+int qmm_gemm(const qmv_weights *w, int32_t m, const float *x, float *y, void *ws, int64_t ws_bytes,
+             void *stream) {
+    int rc = check_gemm(w, m);
+    if (rc) return rc;
+    if (!x || !y) return QMV_ERR_NULL;
+    const int64_t need = qmm_workspace_bytes(w, m);
+    if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
+    if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws & 255u)) return QMV_ERR_ALIGN;
+    int8_t *xq = (int8_t *)ws;
+    float *xs = (float *)((char *)ws + ((int64_t)m * w->k + 255) / 256 * 256);
+    const char *p1 = launch_quant_act(x, m, w->k, xq, xs, (hipStream_t)stream);
+    if (!p1) return QMV_ERR_LIMIT;
+    rc = finish_launch("qmm_quant_act", w, m, p1);
+    if (rc) return rc;
+    const char *p2 = launch_gemm_q6k(w, m, xq, xs, y, nullptr, (hipStream_t)stream);
+    if (!p2) return QMV_ERR_LIMIT;
+    return finish_launch("qmm_gemm", w, m, p2);
+}
+
+int qmv_moe_ffn(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,
+                int32_t n_experts, const int32_t *ids, int32_t n_ids, const void *x, int32_t xt,
+                float *h, float *y, void *stream) {
+    int rc;
+    if ((rc = qmv_validate(gate, 1, xt)) || (rc = qmv_validate(up, 1, xt)) ||
+        (rc = qmv_validate(down, 1, QMV_F32)))
+        return rc;
+    if (gate->fmt != up->fmt || gate->n != up->n || gate->k != up->k || down->k != gate->n ||
+        down->n != gate->k)
+        return QMV_ERR_SHAPE;
+    if (n_experts < 1) return QMV_ERR_SHAPE;
+    if (n_ids < 1 || n_ids > 64) return QMV_ERR_BATCH;
+    if (!ids || !x || !h || !y) return QMV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(h) || !aligned16(y) || ((uintptr_t)ids & 3u)) return QMV_ERR_ALIGN;
+    const char *path = launch_moe_ffn(gate, up, down, n_experts, ids, n_ids, x, xt, h, y,
+                                      (hipStream_t)stream);
+    if (!path) return QMV_ERR_LIMIT;
+    return finish_launch("qmv_moe_ffn", gate, n_ids, path);
+}
+
+const char *qmv_last_path(void) { return g_last_path; }
+
+const char *qmv_strerror(int code) {
+    switch (code) {
+    case QMV_OK: return "ok";
+    case QMV_ERR_NULL: return "a required pointer is NULL";
+    case QMV_ERR_SHAPE: return "bad shape: n, k must be positive and k a multiple of the format's block";
+    case QMV_ERR_FORMAT: return "unknown or unsupported weight format";
+    case QMV_ERR_DTYPE: return "unknown activation dtype";
+    case QMV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QMV_ERR_BATCH: return "batch size out of range";
+    case QMV_ERR_WORKSPACE: return "workspace missing or too small";
+    case QMV_ERR_HIP: return "HIP launch failed";
+    case QMV_ERR_LIMIT: return "size beyond the kernels' supported limit";
+    }
+    return "unknown status";
+}
+
+const char *qmv_version(void) { return "qmv 0.1 gfx950"; }
+
+}  // extern "C"

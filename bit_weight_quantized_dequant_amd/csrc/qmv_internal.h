@@ -1,0 +1,43 @@
+// qmv_internal.h -- host-side declarations shared by the libqmv translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qmv.h"
+
+namespace qmv {
+
+// Device facts read once per process (thread-safe static init).
+struct DeviceInfo {
+    int lds_per_block;  // bytes of LDS one workgroup may use
+    int num_cus;
+};
+const DeviceInfo &device_info();
+
+// Records the label of the launched variant (thread-local) and prints it when
+// QMV_DEBUG=1.  Returns QMV_OK or QMV_ERR_HIP after checking hipGetLastError.
+int finish_launch(const char *call, const qmv_weights *w, int m, const char *path);
+
+// Optional forced variant for tests (QMV_FORCE_PATH); empty string when unset.
+const char *forced_path();
+
+// Kernel launchers.  Arguments are already validated; each returns the label of the
+// variant it launched, or nullptr when the shape is outside what it supports.
+const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt, float *y,
+                             hipStream_t s);
+const char *launch_gemv_q6k(const qmv_weights *w, int m, const void *x, int xt, float *y,
+                            hipStream_t s);
+const char *launch_gemv_cb4(const qmv_weights *w, int m, const void *x, int xt, float *y,
+                            hipStream_t s);
+const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, float *y,
+                           hipStream_t s);
+const char *launch_dequant(const qmv_weights *w, float *out, hipStream_t s);
+const char *launch_quant_act(const float *x, int m, int64_t k, int8_t *xq, float *xs, hipStream_t s);
+const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *xq, const float *xs, float *y,
+                            int32_t *partials, hipStream_t s);
+const char *launch_moe_ffn(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,
+                           int n_experts, const int32_t *ids, int n_ids, const void *x, int xt,
+                           float *h, float *y, hipStream_t s);
+
+}  // namespace qmv

@@ -1,0 +1,200 @@
+/*
+ * qmv.h -- C ABI of libqmv: fused dequantize-and-multiply of block-quantized
+ * weights on MI355X (gfx950).
+ *
+ * The operations (cited by page title and section):
+ *   - the batch-1 decode GEMV y = W x over quantized W, a weight-byte stream
+ *     whose speed is bytes over bandwidth with a per-format unpack tax
+ *     (quantprobe LAWS.md, Law 4 and its L-15 amendment);
+ *   - the q6_K prefill GEMM, an int8 contraction of expanded q6_K weights
+ *     against per-32 int8 quantized activations ("57 · r54 —
+ *     MINFER_MMQ_Q6K_EXP", §2.1 and §2.3);
+ *   - the 4-bit 16-entry codebook and 2-bit additive formats ("Chasing x100",
+ *     "The kernel is ready" and the quality table).
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers unless a comment says otherwise.
+ *     The caller allocates and owns every buffer; the library allocates no
+ *     device memory and keeps no per-matrix state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); all
+ *     GPU work is enqueued asynchronously on it.  Kernel faults surface at the
+ *     caller's next synchronization.
+ *   - Return value: QMV_OK (0) or a negative QMV_ERR_* code.  Arguments are
+ *     validated on the host before any HIP call; on a validation error nothing
+ *     is enqueued.  No C++ exception crosses this ABI.
+ *   - Weight planes are row-major over output rows n, 16-byte aligned, with no
+ *     padding between rows (layouts below).  Activations x are row-major
+ *     [m][k]; outputs y are fp32 row-major [m][n].
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats. */
+enum {
+    QMV_Q4_0 = 1,  /* 32 weights per block: 16 code bytes + fp16 d; w = d*(q-8)                  */
+    QMV_Q6_K = 2,  /* 256 per super-block: ql 128 B, qh 64 B, 16 int8 sc, fp16 d;
+                      w = d*sc[e/16]*(q-32), q = low nibble | 2 high bits << 4                  */
+    QMV_CB4 = 3,   /* 4-bit index into a 16-entry fp16 codebook per 128 weights along k         */
+    QMV_AQ2X8 = 4  /* per 8 weights two 8-bit codes into two 256x8 fp16 codebooks, summed,
+                      times an fp16 per-row scale                                               */
+};
+
+/* Activation element types. */
+enum { QMV_F32 = 0, QMV_BF16 = 1 };
+
+/* Status codes. */
+enum {
+    QMV_OK = 0,
+    QMV_ERR_NULL = -1,      /* a required pointer is NULL                                        */
+    QMV_ERR_SHAPE = -2,     /* n, k <= 0, or k not a multiple of the format's block             */
+    QMV_ERR_FORMAT = -3,    /* unknown format, or an operation the format does not support       */
+    QMV_ERR_DTYPE = -4,     /* unknown activation dtype                                          */
+    QMV_ERR_ALIGN = -5,     /* a plane, x or y pointer is not 16-byte aligned                   */
+    QMV_ERR_BATCH = -6,     /* m (batch rows) out of range                                       */
+    QMV_ERR_WORKSPACE = -7, /* workspace NULL or smaller than qmm_workspace_bytes()             */
+    QMV_ERR_HIP = -8,       /* a HIP call or kernel launch failed                                */
+    QMV_ERR_LIMIT = -9      /* a size beyond what the kernels support (see each call)            */
+};
+
+#define QMV_MAX_BATCH 8
+
+/*
+ * One quantized weight matrix W (n rows = outputs, k columns = inputs).
+ *
+ *   fmt        codes                    codes_hi            scales               super            codebook
+ *   Q4_0       qs u8[n][k/32][16]       NULL                d f16[n][k/32]       NULL             NULL
+ *   Q6_K       ql u8[n][k/256][128]     qh u8[n][k/256][64] sc i8[n][k/256][16]  d f16[n][k/256]  NULL
+ *   CB4        idx u8[n][k/2]           NULL                NULL                 NULL             cb f16[n][k/128][16]
+ *   AQ2X8      codes u8[n][k/8][2]      NULL                s f16[n]             NULL             cbk f16[2][256][8]
+ *
+ * Element order inside the packed planes:
+ *   Q4_0 : code byte j of a block holds weight j (bits 0-3) and weight j+16 (bits 4-7).
+ *   Q6_K : in a super-block, weight e has half h=e/128, r=e%128, t=r/32, l=r%32; its low
+ *          nibble is ql[64h+l+32(t&1)] bits 4(t>>1)..+3 and its high bits are
+ *          qh[32h+l] bits 2t..2t+1 ("57 · r54 — MINFER_MMQ_Q6K_EXP", §2.1 recombination).
+ *   CB4  : index byte i holds index 2i (bits 0-3) and index 2i+1 (bits 4-7).
+ *   AQ2X8: group g of row n stores c1 then c2; weight 8g+j = s[n]*(C1[c1][j]+C2[c2][j]),
+ *          C1 = cbk[0], C2 = cbk[1].
+ * The same matrix stored as raw blocks (18 B per q4_0 block, 210 B per q6_K super-block)
+ * has exactly the same bytes; these planes are that array split by field so that every
+ * field can be read with aligned 128-bit loads.
+ */
+typedef struct {
+    int32_t fmt;
+    int64_t n, k;
+    const void *codes;
+    const void *codes_hi;
+    const void *scales;
+    const void *super;
+    const void *codebook;
+} qmv_weights;
+
+/* Plane selectors for qmv_plane_bytes. */
+enum { QMV_PLANE_CODES = 0, QMV_PLANE_CODES_HI = 1, QMV_PLANE_SCALES = 2, QMV_PLANE_SUPER = 3,
+       QMV_PLANE_CODEBOOK = 4 };
+
+/* Host only (no HIP call).  Bytes of one plane of an n x k matrix in format fmt
+ * (0 for a plane the format does not use), or a negative QMV_ERR_* code. */
+int64_t qmv_plane_bytes(int32_t fmt, int64_t n, int64_t k, int32_t plane);
+
+/* Host only.  Sum of qmv_plane_bytes over all planes: the bytes a GEMV must stream. */
+int64_t qmv_weight_bytes(int32_t fmt, int64_t n, int64_t k);
+
+/* Host only (no HIP call, no dereference of device pointers).  Checks the
+ * descriptor for a GEMV with batch m and activation dtype xt: format, shape,
+ * required planes non-NULL and 16-byte aligned, 1 <= m <= QMV_MAX_BATCH. */
+int qmv_validate(const qmv_weights *w, int32_t m, int32_t xt);
+
+/*
+ * Decode GEMV: y[b][i] = sum_j W[i][j] * x[b][j] for b < m (Law 4's weight-byte
+ * stream; L-15: the per-format unpack cost is the only other term).
+ *   w   : weights (see qmv_weights); x: device [m][k] of dtype xt (QMV_F32 or QMV_BF16),
+ *         16-byte aligned; y: device fp32 [m][n], 16-byte aligned.
+ *   m   : 1..QMV_MAX_BATCH.  Each weight block is decoded once for all m rows.
+ *   Accumulation is fp32; weights are formed exactly from their fields.
+ *   Errors: any QMV_ERR_* from qmv_validate; QMV_ERR_NULL for x/y; QMV_ERR_LIMIT
+ *   when m*k exceeds what one workgroup stages (m*k <= 24576); QMV_ERR_HIP.
+ */
+int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *y, void *stream);
+
+/*
+ * Dequantize W to dense fp32 out[n][k] (device).  Every q4_0, q6_K and CB4
+ * weight is exactly representable in fp32 and is written exactly; AQ2X8 weights
+ * are s*(C1+C2) rounded once to fp32.  Used to check the unpack stage alone.
+ */
+int qmv_dequant(const qmv_weights *w, float *out, void *stream);
+
+/*
+ * Per-32 int8 activation quantizer (the q6_K GEMM's activation side):
+ * for each row and each 32-element block, xs = max|x| / 127 and
+ * xq = clamp(round-half-away-from-zero(x / xs), -127, 127) in IEEE binary32;
+ * an all-zero block gives xs = 0, xq = 0.
+ *   x: fp32 [m][k]; xq: int8 [m][k]; xs: fp32 [m][k/32]; k % 32 == 0, m >= 1.
+ */
+int qmm_quant_act(const float *x, int32_t m, int64_t k, int8_t *xq, float *xs, void *stream);
+
+/* Workspace bytes qmm_gemm needs for m activation rows (xq and xs), or < 0 on error. */
+int64_t qmm_workspace_bytes(const qmv_weights *w, int32_t m);
+
+/*
+ * q6_K prefill GEMM: y[r][i] = sum_s d[i][s] * sum_{c in s} xs[r][c] * I32[r][i][c],
+ * I32[r][i][c] = sum over the 32 weights of activation block c of
+ * sc[i][j/16] * (q[i][j] - 32) * xq[r][j], computed exactly in int32 by int8 MFMA,
+ * then scaled and accumulated in fp32 ("57 · r54 — MINFER_MMQ_Q6K_EXP", §2.1: the
+ * in-kernel ql/qh expansion into centred int8).
+ *   w: QMV_Q6_K only; x: fp32 [m][k]; y: fp32 [m][n]; ws: device workspace of at least
+ *   qmm_workspace_bytes(w, m) bytes (holds xq and xs; contents on return unspecified).
+ *   Runs qmm_quant_act, then the contraction.  m >= 1; k % 256 == 0.
+ */
+int qmm_gemm(const qmv_weights *w, int32_t m, const float *x, float *y, void *ws, int64_t ws_bytes,
+             void *stream);
+
+/* The contraction of qmm_gemm alone, on already quantized activations
+ * (xq int8 [m][k], xs fp32 [m][k/32]). */
+int qmm_gemm_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *xs, float *y,
+                void *stream);
+
+/* Debug / verification: the exact int32 partials I32[r][i][c] (int32 [m][n][k/32])
+ * produced by the same MFMA code path that qmm_gemm_q8 uses. */
+int qmm_partials(const qmv_weights *w, int32_t m, const int8_t *xq, int32_t *i32, void *stream);
+
+/*
+ * Mixture-of-experts FFN over routed experts (batch 1 decode):
+ *   for each listed expert e = ids[j]:  h[j] = SiLU(G_e x) * (U_e x),  y[j] = D_e h[j]
+ * with SiLU(z) = z / (1 + e^-z).  No routing weights are applied; the caller
+ * combines y[j].
+ *   gate, up : descriptors of expert 0 (n = d_ff, k = d_model); down: of expert 0
+ *              (n = d_model, k = d_ff).  Expert e's planes follow expert 0's
+ *              contiguously: plane(e) = plane(0) + e * qmv_plane_bytes(...).
+ *   n_experts: experts stored; ids: device int32 [n_ids]; ids outside
+ *              [0, n_experts) produce NaN rows (no weight is read for them).
+ *   x : device [d_model] of dtype xt; h: device fp32 [n_ids][d_ff] (written);
+ *   y : device fp32 [n_ids][d_model].  1 <= n_ids <= 64.
+ */
+int qmv_moe_ffn(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,
+                int32_t n_experts, const int32_t *ids, int32_t n_ids, const void *x, int32_t xt,
+                float *h, float *y, void *stream);
+
+/* Label of the kernel variant the calling thread's last successful call launched
+ * (a thread-local string owned by the library).  With QMV_DEBUG=1 in the
+ * environment every call also prints "qmv: <call> fmt=.. n=.. k=.. m=.. path=.."
+ * to stderr. */
+const char *qmv_last_path(void);
+
+/* Static description of a status code. */
+const char *qmv_strerror(int code);
+
+/* Library version string. */
+const char *qmv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMV_H */

@@ -1,0 +1,90 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+the host-side validation and size queries behave as include/qmv.h states."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import bit_weight_quantized_dequant_amd as qmv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qm[mv]_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = qmv.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(L, name), name
+    assert qmv.lib().qmv_version().decode().startswith("qmv")
+
+
+def test_plane_bytes_match_the_format_definitions():
+    # q6_K: 210 bytes per 256 weights; 256 x 1024 -> 215,040 B
+    assert qmv.weight_bytes(qmv.Q6_K, 256, 1024) == 215040
+    assert qmv.weight_bytes(qmv.Q6_K, 1, 256) == 210
+    # q4_0: 18 bytes per 32 weights
+    assert qmv.weight_bytes(qmv.Q4_0, 4096, 4096) == 9437184
+    assert qmv.weight_bytes(qmv.Q4_0, 11008, 4096) == 25362432
+    assert qmv.weight_bytes(qmv.Q4_0, 1, 32) == 18
+    # 4-bit codebook: 0.75 byte per weight
+    assert qmv.weight_bytes(qmv.CB4, 2048, 7168) == 11010048
+    # 2-bit additive: 2 bytes per 8 weights + 2 B per row + 8 KiB of codebooks
+    assert qmv.plane_bytes(qmv.AQ2X8, 14336, 4096, "codes") == 14680064
+    assert qmv.weight_bytes(qmv.AQ2X8, 14336, 4096) == 14680064 + 2 * 14336 + 8192
+    assert qmv.plane_bytes(qmv.Q4_0, 4, 32, "codebook") == 0
+    assert qmv.weight_bytes(qmv.Q6_K, 4, 100) == -2
+    assert qmv.weight_bytes(9, 4, 256) == -3
+
+
+def _fake(fmt, n, k, **over):
+    base = 1 << 20
+    planes = {name: base + 4096 * i for i, name in enumerate(qmv.PLANES[fmt])}
+    planes.update(over)
+    return qmv.QWeights(fmt, n, k, planes)
+
+
+@pytest.mark.parametrize("fmt,k", [(qmv.Q4_0, 64), (qmv.Q6_K, 512), (qmv.CB4, 256), (qmv.AQ2X8, 16)])
+def test_validate_accepts_well_formed_descriptors(fmt, k):
+    assert qmv.validate(_fake(fmt, 8, k), 1, qmv.F32) == 0
+    assert qmv.validate(_fake(fmt, 8, k), 8, qmv.BF16) == 0
+
+
+def test_validate_error_codes():
+    L = qmv.lib()
+    assert L.qmv_validate(None, 1, 0) == -1
+    assert qmv.validate(_fake(qmv.Q4_0, 8, 48)) == -2          # k not a multiple of 32
+    assert qmv.validate(_fake(qmv.Q4_0, 0, 64)) == -2          # n <= 0
+    assert qmv.validate(_fake(qmv.Q6_K, 8, 128)) == -2         # k not a multiple of 256
+    w = _fake(qmv.Q4_0, 8, 64)
+    w._s.fmt = 7
+    assert qmv.validate(w) == -3
+    assert qmv.validate(_fake(qmv.Q4_0, 8, 64), 1, 5) == -4
+    assert qmv.validate(_fake(qmv.Q4_0, 8, 64, d=(1 << 20) + 8)) == -5
+    assert qmv.validate(_fake(qmv.Q6_K, 8, 256, qh=0)) == -1
+    assert qmv.validate(_fake(qmv.Q4_0, 8, 64), 0) == -6
+    assert qmv.validate(_fake(qmv.Q4_0, 8, 64), 9) == -6
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
+        assert qmv.strerror(code) and qmv.strerror(code) != "unknown status"
+
+
+def test_calls_reject_bad_arguments_before_any_gpu_work():
+    L = qmv.lib()
+    w = _fake(qmv.Q4_0, 8, 64)
+    assert L.qmv_gemv(w.ref, 1, None, 0, 1 << 20, None) == -1
+    assert L.qmv_gemv(w.ref, 1, (1 << 20) + 4, 0, 1 << 20, None) == -5
+    assert L.qmm_gemm(w.ref, 4, 1 << 20, 1 << 20, 1 << 20, 1 << 20, None) == -3   # q4_0 has no GEMM
+    q6 = _fake(qmv.Q6_K, 8, 256)
+    need = L.qmm_workspace_bytes(q6.ref, 4)
+    assert need == 4 * 256 + 4 * 8 * 4
+    assert L.qmm_gemm(q6.ref, 4, 1 << 20, 1 << 20, 1 << 20, need - 1, None) == -7
+    assert L.qmm_quant_act(1 << 20, 2, 48, 1 << 20, 1 << 20, None) == -2
+    assert L.qmv_moe_ffn(None, None, None, 1, None, 1, None, 0, None, None, None) == -1
