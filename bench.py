@@ -68,16 +68,36 @@ def make_pool(qmv, fmt, n, k, seed, copies):
     return host, pool
 
 
-def time_launches(fn, count, warm=3):
-    """Average milliseconds per call of fn(i) over `count` calls, HIP events on the current stream."""
+def graph_of(fn, count):
+    """A HIP graph (torch.cuda.CUDAGraph) that replays fn(0) .. fn(count-1) back to back.
+
+    The library enqueues plain kernel launches on the current stream, so stream capture
+    records them; replaying the graph removes the per-launch host overhead of Python."""
     import torch
-    for i in range(warm):
-        fn(i)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(min(count, 3)):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, count):
+    """Milliseconds per item of one replay of graph g holding `count` items (HIP events
+    recorded on the stream the graph replays on)."""
+    import torch
+    g.replay()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    for i in range(count):
-        fn(i)
+    g.replay()
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / count
@@ -101,23 +121,27 @@ def q4_0_workload(qmv, steps, warmup):
         for s in range(len(shapes)):
             qmv.gemv(mats[s][c], xs[s], ys[s])
 
-    for i in range(warmup):
-        step(i)
+    # warm-up steps, then exactly `steps` timed steps, each set captured in one graph
+    gw = graph_of(lambda i: step(i + 1000), max(1, warmup))
+    gt = graph_of(step, steps)
+    gw.replay()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    for i in range(steps):
-        step(i)
+    gt.replay()
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     bytes_step = sum(algo)
     per_shape = []
     for s, (n, k) in enumerate(shapes):
-        avg = time_launches(lambda i: qmv.gemv(mats[s][i % copies], xs[s], ys[s]), max(steps, 50))
+        R = max(steps, 60)
+        g = graph_of(lambda i, s=s: qmv.gemv(mats[s][i % copies], xs[s], ys[s]), R)
+        avg = time_graph(g, R)
+        qmv.gemv(mats[s][0], xs[s], ys[s])
         per_shape.append({"shape": f"{n}x{k}", "bytes": algo[s], "avg_launch_ms": avg,
                           "GBps": algo[s] / avg / 1e6, "frac": algo[s] / avg / 1e6 / HBM_PEAK_GBS,
-                          "path": (qmv.gemv(mats[s][0], xs[s], ys[s]), qmv.last_path())[1]})
+                          "path": qmv.last_path()})
     torch.cuda.synchronize()
     return {"ms_per_step": ms, "bytes_per_step": bytes_step, "GBps": bytes_step / ms / 1e6,
             "copies": copies, "pool_bytes": copies * per_set, "shapes": per_shape}

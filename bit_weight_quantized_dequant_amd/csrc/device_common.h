@@ -24,14 +24,59 @@ QMV_DEV float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 // The two binary16 halves of a dword, as floats.  Used on dwords whose halves hold
 // small integers q as binary16 subnormals (bit pattern q, value q * 2^-24): the
 // conversion is exact, and the compiler folds it into v_fma_mix_f32.
+QMV_DEV qmv_h2 as_h2(uint32_t v) { return __builtin_bit_cast(qmv_h2, v); }
+
+// (a & mask) | bits in one v_and_or_b32.  gfx950 VOP3 encodings take no literal and at
+// most one scalar operand, so the compiler otherwise splits this into v_and + v_or with
+// literals; here mask and bits live in (loop-invariant) VGPRs.
+QMV_DEV uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask), "v"(bits));
+    return r;
+}
 QMV_DEV float lo_h(uint32_t v) { return (float)__builtin_bit_cast(qmv_h2, v).x; }
 QMV_DEV float hi_h(uint32_t v) { return (float)__builtin_bit_cast(qmv_h2, v).y; }
 
-// Sum over the 64 lanes of a wavefront; every lane receives the total.
+// DPP move of a float within a row of 16 lanes (or row broadcast); rows masked off by
+// RM, or lanes whose source is out of range, contribute 0.
+template <int CTRL, int RM = 0xF>
+QMV_DEV float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, RM, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront with DPP (xor-1, xor-2, half-row mirror, row mirror,
+// then row broadcasts 15 and 31); the total is read from lane 63 and returned uniformly.
 QMV_DEV float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    v += dpp_f<0xB1>(v);         // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);         // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);        // row_half_mirror
+    v += dpp_f<0x140>(v);        // row_mirror: every lane holds its row-of-16 sum
+    v += dpp_f<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_f<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Sum over aligned groups of 8 lanes; every lane of the group receives the group total.
+QMV_DEV float sum8(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
     return v;
+}
+
+// Sum over aligned groups of G lanes (G = 2, 4, ..., 64) with xor shuffles.
+QMV_DEV float group_sum(float v, int G) {
+    for (int o = G >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Four consecutive activations starting at element i (16-byte aligned) as floats.
+template <int XT>
+QMV_DEV float4 ld_act4(const void *x, int64_t i) {
+    if (XT == 0) return *(const float4 *)((const float *)x + i);
+    const uint2 v = *(const uint2 *)((const uint16_t *)x + i);
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
 }
 
 // Load one activation element of type XT (0 = fp32, 1 = bf16 bits) as float.

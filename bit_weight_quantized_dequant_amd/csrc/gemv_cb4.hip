@@ -1,0 +1,259 @@
+// gemv_cb4.hip -- 4-bit codebook GEMV and the routed-expert FFN built on it (gfx950).
+//
+// Format ("Chasing x100": a 4-bit codebook format with K=16 entries, decoded by a fused
+// GEMV; the routed experts of a mixture dominate the bytes per token): every 128
+// consecutive weights of a row share one 16-entry fp16 codebook, and each weight is a
+// 4-bit index into it.  Index byte i holds indices 2i (bits 0-3) and 2i+1 (bits 4-7).
+//
+// The page's CPU kernel decodes with one byte-shuffle per 32 weights; on gfx950 the
+// table lookup is an LDS gather instead:
+//   * the workgroup stages the activations once into LDS as fp32 (blocks of 32 with a
+//     4-float pad, so lanes reading consecutive blocks with ds_read_b128 do not collide);
+//   * each wave copies its row's codebooks into its own LDS slice (coalesced 16-byte
+//     loads), so one ds_read_u16 returns the fp16 weight for an index;
+//   * v_fma_mix_f32 multiplies that fp16 value by the fp32 activation (exact product),
+//     so the only rounding is the fp32 accumulation;
+//   * lane l owns the 32-weight chunks l, l+64, ... of the row (16 index bytes = one
+//     128-bit load); the 64 partials are summed with DPP.
+// The same kernel runs three jobs: a plain GEMV (one row per wave), the fused gate/up
+// stage of the expert FFN (a wave computes row r of G_e and of U_e and writes
+// SiLU(g) * u), and the down stage (y_e = D_e h_e), with the expert id read on the
+// device and its planes found at e * plane_bytes from expert 0's.
+#include "device_common.h"
+#include "qmv_internal.h"
+
+namespace qmv {
+namespace {
+
+constexpr int WG = 512;
+constexpr int WAVES = WG / 64;
+constexpr int XS = 36;
+
+enum { JOB_GEMV = 0, JOB_GATEUP = 1, JOB_DOWN = 2 };
+
+struct Cb4Args {
+    const uint8_t *idx0, *idx1;  // index planes (expert 0): first matrix, second (gate/up: up)
+    const uint16_t *cb0, *cb1;   // codebook planes
+    int64_t idx_stride, cb_stride;  // bytes / entries between experts
+    const void *x;               // activations: [M][k] (GEMV, GATEUP) or h [n_ids][k] (DOWN)
+    float *y;                    // GEMV: [M][n]; GATEUP: h [n_ids][n]; DOWN: y [n_ids][n]
+    const int32_t *ids;
+    int n, k, n_experts;
+};
+
+template <int M, int XT>
+__device__ void stage_x(const void *x, int k, float *sx) {
+    const int total = M * (k >> 2);
+    for (int c = threadIdx.x; c < total; c += WG)
+        *(float4 *)(sx + (c >> 3) * XS + (c & 7) * 4) = ld_act4<XT>(x, (int64_t)c * 4);
+}
+
+// Copy one row's codebooks (ngroups x 16 fp16 = ngroups * 32 bytes) into LDS (wave-local).
+QMV_DEV void stage_tables(const uint16_t *cb, int ngroups, uint16_t *tab, int lane) {
+    const uint4 *src = (const uint4 *)cb;
+    uint4 *dst = (uint4 *)tab;
+    for (int i = lane; i < ngroups * 2; i += 64) dst[i] = src[i];
+}
+
+// base + byte `B` of v, in one v_add_u32 with an SDWA byte select on the second source.
+template <int B>
+QMV_DEV uint32_t add_byte(uint32_t base, uint32_t v) {
+    uint32_t r;
+    if (B == 0) asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(base), "v"(v));
+    if (B == 1) asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(base), "v"(v));
+    if (B == 2) asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(base), "v"(v));
+    if (B == 3) asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(base), "v"(v));
+    return r;
+}
+
+// fp16 LDS word at byte address a, as float.
+QMV_DEV float lds_h(uint32_t a) {
+    return h2f(*(const __attribute__((address_space(3))) uint16_t *)(uintptr_t)a);
+}
+
+// sum over one 32-weight chunk: cb[idx] * x, with the chunk's table at LDS byte address tb.
+// The byte offsets 2*idx of a dword's eight indices are formed with two masks (even and
+// odd nibbles, one per byte lane); each lookup is then one SDWA add and one ds_read_u16.
+QMV_DEV float chunk_dot(uint4 q, uint32_t tb, const float *xb) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const float4 x0 = *(const float4 *)(xb + 8 * j), x1 = *(const float4 *)(xb + 8 * j + 4);
+        const uint32_t ev = (w[j] << 1) & 0x1E1E1E1Eu;  // 2 * index of weights 0, 2, 4, 6
+        const uint32_t od = (w[j] >> 3) & 0x1E1E1E1Eu;  // 2 * index of weights 1, 3, 5, 7
+        a = fmaf(lds_h(add_byte<0>(tb, ev)), x0.x, a);
+        b = fmaf(lds_h(add_byte<0>(tb, od)), x0.y, b);
+        a = fmaf(lds_h(add_byte<1>(tb, ev)), x0.z, a);
+        b = fmaf(lds_h(add_byte<1>(tb, od)), x0.w, b);
+        a = fmaf(lds_h(add_byte<2>(tb, ev)), x1.x, a);
+        b = fmaf(lds_h(add_byte<2>(tb, od)), x1.y, b);
+        a = fmaf(lds_h(add_byte<3>(tb, ev)), x1.z, a);
+        b = fmaf(lds_h(add_byte<3>(tb, od)), x1.w, b);
+    }
+    return a + b;
+}
+
+template <int CPL>
+struct RowCodes {
+    uint4 q[CPL];
+};
+
+template <int CPL>
+QMV_DEV void load_row(RowCodes<CPL> &r, const uint8_t *idx_row, int nchunk, int lane, bool valid) {
+#pragma unroll
+    for (int u = 0; u < CPL; u++) {
+        const int c = lane + 64 * u;
+        r.q[u] = (valid && c < nchunk) ? ld_stream16(idx_row + 16 * (int64_t)c) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int CPL>
+QMV_DEV float row_dot(const RowCodes<CPL> &r, const uint16_t *tab, const float *sx, int nchunk, int lane) {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < CPL; u++) {
+        const int c = lane + 64 * u;
+        if (c < nchunk)
+            acc += chunk_dot(r.q[u], (uint32_t)(uintptr_t)(tab + (c >> 2) * 16), sx + c * XS);
+    }
+    return acc;
+}
+
+// GEMV job: grid.x over row blocks; one row per wave.
+// GATEUP job: grid.x over row blocks, grid.y = expert slot j; x is the token's activations.
+// DOWN job: grid.x over row blocks, grid.y = expert slot j; x is h (fp32) [n_ids][k].
+template <int JOB, int M, int CPL, int XT>
+__global__ void __launch_bounds__(WG) cb4_kernel(Cb4Args a) {
+    extern __shared__ float lds[];
+    const int k = a.k, ngroups = k >> 7, nchunk = k >> 5;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * WAVES + wave;
+    constexpr int NT = JOB == JOB_GATEUP ? 2 : 1;  // tables (rows) per wave
+    float *sx = lds;
+    uint16_t *tabs = (uint16_t *)(lds + M * (k >> 5) * XS);
+    uint16_t *tab0 = tabs + wave * NT * ngroups * 16;
+    uint16_t *tab1 = tab0 + ngroups * 16;
+
+    int64_t e = 0;
+    bool ok_expert = true;
+    const void *x = a.x;
+    if (JOB != JOB_GEMV) {
+        const int32_t id = a.ids[blockIdx.y];
+        ok_expert = id >= 0 && id < a.n_experts;
+        e = ok_expert ? id : 0;
+        if (JOB == JOB_DOWN) x = (const float *)a.x + (int64_t)blockIdx.y * k;
+    }
+    const bool valid = ok_expert && row < a.n;
+
+    // activations first (vector loads return in order), then codes, then tables
+    stage_x<M, (JOB == JOB_DOWN ? 0 : XT)>(x, k, sx);
+    RowCodes<CPL> r0, r1;
+    const uint8_t *i0 = a.idx0 + e * a.idx_stride + (int64_t)row * (k >> 1);
+    load_row<CPL>(r0, i0, nchunk, lane, valid);
+    if (JOB == JOB_GATEUP) {
+        const uint8_t *i1 = a.idx1 + e * a.idx_stride + (int64_t)row * (k >> 1);
+        load_row<CPL>(r1, i1, nchunk, lane, valid);
+    }
+    if (valid) {
+        stage_tables(a.cb0 + e * a.cb_stride + (int64_t)row * ngroups * 16, ngroups, tab0, lane);
+        if (JOB == JOB_GATEUP)
+            stage_tables(a.cb1 + e * a.cb_stride + (int64_t)row * ngroups * 16, ngroups, tab1, lane);
+    }
+    __syncthreads();
+
+    if (JOB == JOB_GEMV) {
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float t = wave_sum(row_dot<CPL>(r0, tab0, sx + m * nchunk * XS, nchunk, lane));
+            if (lane == 0 && valid) a.y[(int64_t)m * a.n + row] = t;
+        }
+        return;
+    }
+    float *out = a.y + (int64_t)blockIdx.y * a.n;
+    if (JOB == JOB_GATEUP) {
+        const float g = wave_sum(row_dot<CPL>(r0, tab0, sx, nchunk, lane));
+        const float u = wave_sum(row_dot<CPL>(r1, tab1, sx, nchunk, lane));
+        if (lane == 0 && row < a.n) out[row] = ok_expert ? g / (1.f + expf(-g)) * u : __builtin_nanf("");
+    } else {
+        const float t = wave_sum(row_dot<CPL>(r0, tab0, sx, nchunk, lane));
+        if (lane == 0 && row < a.n) out[row] = ok_expert ? t : __builtin_nanf("");
+    }
+}
+
+template <int JOB, int M, int CPL, int XT>
+void launch(const Cb4Args &a, int slots, hipStream_t s) {
+    constexpr int NT = JOB == JOB_GATEUP ? 2 : 1;
+    const size_t lds = (size_t)M * (a.k >> 5) * XS * 4 + (size_t)WAVES * NT * (a.k >> 7) * 32;
+    hipLaunchKernelGGL((cb4_kernel<JOB, M, CPL, XT>), dim3((a.n + WAVES - 1) / WAVES, slots), dim3(WG), lds, s, a);
+}
+
+template <int JOB, int M, int XT>
+bool dispatch_cpl(int cpl, const Cb4Args &a, int slots, hipStream_t s) {
+    switch (cpl) {
+    case 1: launch<JOB, M, 1, XT>(a, slots, s); return true;
+    case 2: launch<JOB, M, 2, XT>(a, slots, s); return true;
+    case 3: launch<JOB, M, 3, XT>(a, slots, s); return true;
+    case 4: launch<JOB, M, 4, XT>(a, slots, s); return true;
+    case 5: launch<JOB, M, 5, XT>(a, slots, s); return true;
+    case 6: launch<JOB, M, 6, XT>(a, slots, s); return true;
+    case 7: launch<JOB, M, 7, XT>(a, slots, s); return true;
+    case 8: launch<JOB, M, 8, XT>(a, slots, s); return true;
+    }
+    return false;
+}
+
+template <int XT>
+bool dispatch_m(int m, int cpl, const Cb4Args &a, hipStream_t s) {
+    switch (m) {
+    case 1: return dispatch_cpl<JOB_GEMV, 1, XT>(cpl, a, 1, s);
+    case 2: return dispatch_cpl<JOB_GEMV, 2, XT>(cpl, a, 1, s);
+    case 3: return dispatch_cpl<JOB_GEMV, 3, XT>(cpl, a, 1, s);
+    case 4: return dispatch_cpl<JOB_GEMV, 4, XT>(cpl, a, 1, s);
+    case 5: return dispatch_cpl<JOB_GEMV, 5, XT>(cpl, a, 1, s);
+    case 6: return dispatch_cpl<JOB_GEMV, 6, XT>(cpl, a, 1, s);
+    case 7: return dispatch_cpl<JOB_GEMV, 7, XT>(cpl, a, 1, s);
+    case 8: return dispatch_cpl<JOB_GEMV, 8, XT>(cpl, a, 1, s);
+    }
+    return false;
+}
+
+size_t lds_need(int m, int64_t k, int nt) { return (size_t)m * (k >> 5) * XS * 4 + (size_t)WAVES * nt * (k >> 7) * 32; }
+
+}  // namespace
+
+const char *launch_gemv_cb4(const qmv_weights *w, int m, const void *x, int xt, float *y, hipStream_t s) {
+    const int64_t k = w->k, nchunk = k / 32;
+    const int cpl = (int)((nchunk + 63) / 64);
+    if (cpl > 8 || (int64_t)m * k > 16384) return nullptr;
+    if ((int64_t)lds_need(m, k, 1) > device_info().lds_per_block) return nullptr;
+    Cb4Args a{(const uint8_t *)w->codes, nullptr, (const uint16_t *)w->codebook, nullptr, 0, 0, x, y, nullptr,
+              (int)w->n, (int)k, 1};
+    const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, cpl, a, s) : dispatch_m<1>(m, cpl, a, s);
+    return ok ? "cb4.lds-table.fma-mix" : nullptr;
+}
+
+// Routed-expert FFN over CB4 experts: gate/up/SiLU*mul, then down.
+const char *launch_moe_cb4(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,
+                           int n_experts, const int32_t *ids, int n_ids, const void *x, int xt, float *h,
+                           float *y, hipStream_t s) {
+    const int64_t dm = gate->k, dff = gate->n;
+    const int cpl1 = (int)((dm / 32 + 63) / 64), cpl2 = (int)((dff / 32 + 63) / 64);
+    if (cpl1 > 8 || cpl2 > 8 || dm > 16384 || dff > 16384) return nullptr;
+    if ((int64_t)lds_need(1, dm, 2) > device_info().lds_per_block ||
+        (int64_t)lds_need(1, dff, 1) > device_info().lds_per_block)
+        return nullptr;
+    const int64_t idx_gu = dff * dm / 2, cb_gu = dff * (dm / 128) * 16;
+    Cb4Args a1{(const uint8_t *)gate->codes, (const uint8_t *)up->codes, (const uint16_t *)gate->codebook,
+               (const uint16_t *)up->codebook, idx_gu, cb_gu, x, h, ids, (int)dff, (int)dm, n_experts};
+    const bool ok1 = xt == QMV_F32 ? dispatch_cpl<JOB_GATEUP, 1, 0>(cpl1, a1, n_ids, s)
+                                   : dispatch_cpl<JOB_GATEUP, 1, 1>(cpl1, a1, n_ids, s);
+    if (!ok1) return nullptr;
+    const int64_t idx_d = dm * dff / 2, cb_d = dm * (dff / 128) * 16;
+    Cb4Args a2{(const uint8_t *)down->codes, nullptr, (const uint16_t *)down->codebook, nullptr, idx_d, cb_d,
+               h, y, ids, (int)dm, (int)dff, n_experts};
+    if (!dispatch_cpl<JOB_DOWN, 1, 0>(cpl2, a2, n_ids, s)) return nullptr;
+    return "moe.cb4.gateup-silu+down";
+}
+
+}  // namespace qmv

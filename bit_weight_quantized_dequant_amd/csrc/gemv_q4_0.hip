@@ -9,13 +9,14 @@
 //   * Each lane owns whole blocks: one 128-bit load of 16 code bytes + one fp16 scale.
 //   * Activations for the workgroup are staged once into LDS as fp32, 32 per block
 //     (row stride 36 floats so that eight lanes reading eight blocks with ds_read_b128
-//     touch disjoint banks), together with each block's sum sum_k x[k].
-//   * The offset is folded per block: sum (q-8) x = sum q x - 8 sum x.
-//   * A dword of codes is split by masks 0x000F000F / 0x00F000F0 into pairs of binary16
-//     subnormals whose bit patterns are the codes (value q * 2^-24, or q * 2^-20 for the
-//     high nibble of a byte); v_fma_mix_f32 consumes a binary16 half directly, so each
-//     weight costs one FMA plus 5/8 of a bitwise op, and the products are exact.
-//   * The 64 lane partials of a row are summed across the wavefront.
+//     touch disjoint banks).  They are staged before the weight loads are issued:
+//     vector loads return in order, so staging after them would wait for every weight.
+//   * Centering is exact: a nibble is OR-ed under the binary16 exponent of 1024 (bits
+//     0-3) or of 256 with a quarter ulp (bits 4-7), and one packed half subtract turns
+//     the pair into (q - 8) or 4 (q - 8), exactly.  v_fma_mix_f32 then multiplies the
+//     binary16 half by the fp32 activation with an exact product, so a zero weight adds
+//     exactly zero and the rounding error is relative to sum |w||x|.
+//   * The 64 lane partials of a row are summed across the wavefront with DPP.
 #include <cstring>
 
 #include "device_common.h"
@@ -24,55 +25,48 @@
 namespace qmv {
 namespace {
 
-constexpr int WG = 512;  // threads per workgroup: 8 waves
+constexpr int WG = 512;  // threads per workgroup: 8 waves, one output row each
 constexpr int WAVES = WG / 64;
 constexpr int XS = 36;   // floats per staged 32-activation block
 
-// Stage x [M][k] into LDS: block (m, b) at sx[(m*nblk + b)*XS], its sum at ssum[m*nblk + b].
+// Stage x [M][k] into LDS: block (m, b) at sx[(m*nblk + b)*XS].  Each thread moves
+// coalesced 16-byte chunks.
 template <int M, int XT>
-__device__ void stage_x32(const void *x, int k, float *sx, float *ssum) {
-    const int nblk = k >> 5;
-    for (int i = threadIdx.x; i < M * nblk; i += WG) {
-        const int m = i / nblk, b = i - m * nblk;
-        float v[32];
-#pragma unroll
-        for (int j = 0; j < 4; j++) ld_act8<XT>(x, (int64_t)m * k + b * 32 + 8 * j, v + 8 * j);
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < 32; e++) s += v[e];
-        float4 *dst = (float4 *)(sx + i * XS);
-#pragma unroll
-        for (int j = 0; j < 8; j++) dst[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
-        ssum[i] = s;
-    }
+__device__ void stage_x32(const void *x, int k, float *sx) {
+    const int total = M * (k >> 2);
+    for (int c = threadIdx.x; c < total; c += WG)
+        *(float4 *)(sx + (c >> 3) * XS + (c & 7) * 4) = ld_act4<XT>(x, (int64_t)c * 4);
 }
 
-// sum_{i<32} q_i * x_i for one block (codes q in 4 dwords, staged x at xb), exact products.
+// sum_{i<32} (q_i - 8) * x_i for one block (codes in 4 dwords, staged x at xb); every
+// product is exact.
 QMV_DEV float dot_q4_mix(uint4 q, const float *xb) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    const qmv_h2 off_lo = {(_Float16)-1032.f, (_Float16)-1032.f};  // (1024 + q) - 1032 = q - 8
+    const qmv_h2 off_hi = {(_Float16)-288.f, (_Float16)-288.f};    // (256 + 4q) - 288 = 4 (q - 8)
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const float4 xl = *(const float4 *)(xb + 4 * i);       // weights 4i .. 4i+3
         const float4 xh = *(const float4 *)(xb + 16 + 4 * i);  // weights 16+4i .. 16+4i+3
         const uint32_t w8 = w[i] >> 8;
-        const uint32_t t0 = w[i] & 0x000F000Fu;  // byte 0 / byte 2, low nibbles   (x 2^-24)
-        const uint32_t t1 = w[i] & 0x00F000F0u;  // byte 0 / byte 2, high nibbles  (x 2^-20)
-        const uint32_t t2 = w8 & 0x000F000Fu;    // byte 1 / byte 3, low nibbles
-        const uint32_t t3 = w8 & 0x00F000F0u;    // byte 1 / byte 3, high nibbles
-        a0 = fmaf(lo_h(t0), xl.x, a0);
-        a0 = fmaf(hi_h(t0), xl.z, a0);
-        b0 = fmaf(lo_h(t2), xl.y, b0);
-        b0 = fmaf(hi_h(t2), xl.w, b0);
-        a1 = fmaf(lo_h(t1), xh.x, a1);
-        a1 = fmaf(hi_h(t1), xh.z, a1);
-        b1 = fmaf(lo_h(t3), xh.y, b1);
-        b1 = fmaf(hi_h(t3), xh.w, b1);
+        const qmv_h2 t0 = as_h2(and_or(w[i], 0x000F000Fu, 0x64006400u)) + off_lo;  // bytes 0, 2 low
+        const qmv_h2 t1 = as_h2(and_or(w[i], 0x00F000F0u, 0x5C005C00u)) + off_hi;  // bytes 0, 2 high
+        const qmv_h2 t2 = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) + off_lo;    // bytes 1, 3 low
+        const qmv_h2 t3 = as_h2(and_or(w8, 0x00F000F0u, 0x5C005C00u)) + off_hi;    // bytes 1, 3 high
+        a0 = fmaf((float)t0.x, xl.x, a0);
+        a0 = fmaf((float)t0.y, xl.z, a0);
+        b0 = fmaf((float)t2.x, xl.y, b0);
+        b0 = fmaf((float)t2.y, xl.w, b0);
+        a1 = fmaf((float)t1.x, xh.x, a1);
+        a1 = fmaf((float)t1.y, xh.z, a1);
+        b1 = fmaf((float)t3.x, xh.y, b1);
+        b1 = fmaf((float)t3.y, xh.w, b1);
     }
-    return (a0 + b0) * 16777216.0f + (a1 + b1) * 1048576.0f;
+    return (a0 + b0) + (a1 + b1) * 0.25f;
 }
 
-// Same sum with byte-to-float conversions (v_cvt_f32_ubyte*), kept as a reference variant.
+// Same centred sum with byte-to-float conversions (v_cvt_f32_ubyte*), a reference variant.
 QMV_DEV float dot_q4_cvt(uint4 q, const float *xb) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     float a = 0.f, b = 0.f;
@@ -81,119 +75,109 @@ QMV_DEV float dot_q4_cvt(uint4 q, const float *xb) {
         const float4 xl = *(const float4 *)(xb + 4 * i);
         const float4 xh = *(const float4 *)(xb + 16 + 4 * i);
         const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
-        a = fmaf((float)(lo & 0xFFu), xl.x, a);
-        a = fmaf((float)((lo >> 8) & 0xFFu), xl.y, a);
-        a = fmaf((float)((lo >> 16) & 0xFFu), xl.z, a);
-        a = fmaf((float)(lo >> 24), xl.w, a);
-        b = fmaf((float)(hi & 0xFFu), xh.x, b);
-        b = fmaf((float)((hi >> 8) & 0xFFu), xh.y, b);
-        b = fmaf((float)((hi >> 16) & 0xFFu), xh.z, b);
-        b = fmaf((float)(hi >> 24), xh.w, b);
+        a = fmaf((float)(lo & 0xFFu) - 8.f, xl.x, a);
+        a = fmaf((float)((lo >> 8) & 0xFFu) - 8.f, xl.y, a);
+        a = fmaf((float)((lo >> 16) & 0xFFu) - 8.f, xl.z, a);
+        a = fmaf((float)(lo >> 24) - 8.f, xl.w, a);
+        b = fmaf((float)(hi & 0xFFu) - 8.f, xh.x, b);
+        b = fmaf((float)((hi >> 8) & 0xFFu) - 8.f, xh.y, b);
+        b = fmaf((float)((hi >> 16) & 0xFFu) - 8.f, xh.z, b);
+        b = fmaf((float)(hi >> 24) - 8.f, xh.w, b);
     }
     return a + b;
 }
 
-// One wave computes rows row0 .. row0+rpw-1; lane l owns blocks l, l+64, ... of each row.
+// One wave computes one row; lane l owns blocks l, l+64, ... of it.  The activations are
+// staged before the weight loads are issued: vector loads return in order, so x staged
+// after the weights would wait for every weight byte before the first FMA.
 template <int M, int BPL, int XT, bool MIX>
 __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict__ qs,
                                                        const uint16_t *__restrict__ dsc,
                                                        const void *__restrict__ x,
-                                                       float *__restrict__ y, int n, int k, int rpw) {
+                                                       float *__restrict__ y, int n, int k) {
     extern __shared__ float lds[];
     const int nblk = k >> 5;
     float *sx = lds;
-    float *ssum = lds + M * nblk * XS;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row0 = (blockIdx.x * WAVES + wave) * rpw;
+    const int row = blockIdx.x * WAVES + wave;
+
+    stage_x32<M, XT>(x, k, sx);
 
     uint4 q[BPL];
     uint16_t dd[BPL];
-    auto load = [&](int row) {
-        const uint4 *qr = (const uint4 *)(qs + (int64_t)row * (k >> 1));
-        const uint16_t *dr = dsc + (int64_t)row * nblk;
+    const uint4 *qr = (const uint4 *)(qs + (int64_t)row * (k >> 1));
+    const uint16_t *dr = dsc + (int64_t)row * nblk;
 #pragma unroll
-        for (int u = 0; u < BPL; u++) {
-            const int b = lane + 64 * u;
-            if (b < nblk) {
-                q[u] = ld_stream16(qr + b);
-                dd[u] = dr[b];
-            } else {
-                q[u] = make_uint4(0, 0, 0, 0);
-                dd[u] = 0;
-            }
+    for (int u = 0; u < BPL; u++) {
+        const int b = lane + 64 * u;
+        if (row < n && b < nblk) {
+            q[u] = ld_stream16(qr + b);
+            dd[u] = dr[b];
+        } else {
+            q[u] = make_uint4(0, 0, 0, 0);
+            dd[u] = 0;
         }
-    };
-    if (row0 < n) load(row0);
-    stage_x32<M, XT>(x, k, sx, ssum);
+    }
     __syncthreads();
 
-    for (int r = 0; r < rpw; r++) {
-        const int row = row0 + r;
-        if (row >= n) break;
-        uint4 cq[BPL];
-        uint16_t cd[BPL];
+    float acc[M];
 #pragma unroll
-        for (int u = 0; u < BPL; u++) { cq[u] = q[u]; cd[u] = dd[u]; }
-        if (r + 1 < rpw && row + 1 < n) load(row + 1);
-        float acc[M];
+    for (int m = 0; m < M; m++) acc[m] = 0.f;
 #pragma unroll
-        for (int m = 0; m < M; m++) acc[m] = 0.f;
+    for (int u = 0; u < BPL; u++) {
+        const int b = lane + 64 * u;
+        if (b < nblk) {
+            const float d = h2f(dd[u]);
 #pragma unroll
-        for (int u = 0; u < BPL; u++) {
-            const int b = lane + 64 * u;
-            if (b < nblk) {
-                const float d = h2f(cd[u]);
-#pragma unroll
-                for (int m = 0; m < M; m++) {
-                    const float *xb = sx + (m * nblk + b) * XS;
-                    const float s = MIX ? dot_q4_mix(cq[u], xb) : dot_q4_cvt(cq[u], xb);
-                    acc[m] = fmaf(d, s - 8.f * ssum[m * nblk + b], acc[m]);
-                }
+            for (int m = 0; m < M; m++) {
+                const float *xb = sx + (m * nblk + b) * XS;
+                const float s = MIX ? dot_q4_mix(q[u], xb) : dot_q4_cvt(q[u], xb);
+                acc[m] = fmaf(d, s, acc[m]);
             }
         }
+    }
 #pragma unroll
-        for (int m = 0; m < M; m++) {
-            const float t = wave_sum(acc[m]);
-            if (lane == 0) y[(int64_t)m * n + row] = t;
-        }
+    for (int m = 0; m < M; m++) {
+        const float t = wave_sum(acc[m]);
+        if (lane == 0 && row < n) y[(int64_t)m * n + row] = t;
     }
 }
 
 template <int M, int BPL, int XT, bool MIX>
-void launch(const qmv_weights *w, const void *x, float *y, int rpw, hipStream_t s) {
+void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     const int n = (int)w->n, k = (int)w->k, nblk = k >> 5;
-    const size_t lds = (size_t)M * nblk * (XS + 1) * sizeof(float);
-    const int grid = (n + WAVES * rpw - 1) / (WAVES * rpw);
+    const size_t lds = (size_t)M * nblk * XS * sizeof(float);
+    const int grid = (n + WAVES - 1) / WAVES;
     hipLaunchKernelGGL((gemv_q4_0_kernel<M, BPL, XT, MIX>), dim3(grid), dim3(WG), lds, s,
-                       (const uint8_t *)w->codes, (const uint16_t *)w->scales, x, y, n, k, rpw);
+                       (const uint8_t *)w->codes, (const uint16_t *)w->scales, x, y, n, k);
 }
 
 template <int M, int XT, bool MIX>
-bool dispatch_bpl(int bpl, const qmv_weights *w, const void *x, float *y, int rpw, hipStream_t s) {
+bool dispatch_bpl(int bpl, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     switch (bpl) {
-    case 1: launch<M, 1, XT, MIX>(w, x, y, rpw, s); return true;
-    case 2: launch<M, 2, XT, MIX>(w, x, y, rpw, s); return true;
-    case 3: launch<M, 3, XT, MIX>(w, x, y, rpw, s); return true;
-    case 4: launch<M, 4, XT, MIX>(w, x, y, rpw, s); return true;
-    case 5: launch<M, 5, XT, MIX>(w, x, y, rpw, s); return true;
-    case 6: launch<M, 6, XT, MIX>(w, x, y, rpw, s); return true;
-    case 7: launch<M, 7, XT, MIX>(w, x, y, rpw, s); return true;
-    case 8: launch<M, 8, XT, MIX>(w, x, y, rpw, s); return true;
+    case 1: launch<M, 1, XT, MIX>(w, x, y, s); return true;
+    case 2: launch<M, 2, XT, MIX>(w, x, y, s); return true;
+    case 3: launch<M, 3, XT, MIX>(w, x, y, s); return true;
+    case 4: launch<M, 4, XT, MIX>(w, x, y, s); return true;
+    case 5: launch<M, 5, XT, MIX>(w, x, y, s); return true;
+    case 6: launch<M, 6, XT, MIX>(w, x, y, s); return true;
+    case 7: launch<M, 7, XT, MIX>(w, x, y, s); return true;
+    case 8: launch<M, 8, XT, MIX>(w, x, y, s); return true;
     }
     return false;
 }
 
 template <int XT, bool MIX>
-bool dispatch_m(int m, int bpl, const qmv_weights *w, const void *x, float *y, int rpw, hipStream_t s) {
+bool dispatch_m(int m, int bpl, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     switch (m) {
-    case 1: return dispatch_bpl<1, XT, MIX>(bpl, w, x, y, rpw, s);
-    case 2: return dispatch_bpl<2, XT, MIX>(bpl, w, x, y, rpw, s);
-    case 3: return dispatch_bpl<3, XT, MIX>(bpl, w, x, y, rpw, s);
-    case 4: return dispatch_bpl<4, XT, MIX>(bpl, w, x, y, rpw, s);
-    case 5: return dispatch_bpl<5, XT, MIX>(bpl, w, x, y, rpw, s);
-    case 6: return dispatch_bpl<6, XT, MIX>(bpl, w, x, y, rpw, s);
-    case 7: return dispatch_bpl<7, XT, MIX>(bpl, w, x, y, rpw, s);
-    case 8: return dispatch_bpl<8, XT, MIX>(bpl, w, x, y, rpw, s);
+    case 1: return dispatch_bpl<1, XT, MIX>(bpl, w, x, y, s);
+    case 2: return dispatch_bpl<2, XT, MIX>(bpl, w, x, y, s);
+    case 3: return dispatch_bpl<3, XT, MIX>(bpl, w, x, y, s);
+    case 4: return dispatch_bpl<4, XT, MIX>(bpl, w, x, y, s);
+    case 5: return dispatch_bpl<5, XT, MIX>(bpl, w, x, y, s);
+    case 6: return dispatch_bpl<6, XT, MIX>(bpl, w, x, y, s);
+    case 7: return dispatch_bpl<7, XT, MIX>(bpl, w, x, y, s);
+    case 8: return dispatch_bpl<8, XT, MIX>(bpl, w, x, y, s);
     }
     return false;
 }
@@ -205,20 +189,18 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
     const int64_t n = w->n, k = w->k, nblk = k / 32;
     const int bpl = (int)((nblk + 63) / 64);
     if (bpl > 8 || (int64_t)m * k > 16384 || n > INT32_MAX) return nullptr;
-    const size_t lds = (size_t)m * nblk * (XS + 1) * sizeof(float);
+    const size_t lds = (size_t)m * nblk * XS * sizeof(float);
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
-    // Rows per wave: keep at least ~2 workgroups per CU before giving a wave more rows.
-    const int64_t target_waves = (int64_t)device_info().num_cus * 2 * WAVES;
-    int rpw = (int)(n / target_waves);
-    rpw = rpw < 1 ? 1 : (rpw > 4 ? 4 : rpw);
-    const bool mix = strcmp(forced_path(), "q4_0.cvt") != 0;
+    const bool cvt = strcmp(forced_path(), "q4_0.cvt") == 0 && m == 1 && xt == QMV_F32;
     bool ok;
-    if (xt == QMV_F32)
-        ok = mix ? dispatch_m<0, true>(m, bpl, w, x, y, rpw, s) : dispatch_m<0, false>(m, bpl, w, x, y, rpw, s);
+    if (cvt)
+        ok = dispatch_bpl<1, 0, false>(bpl, w, x, y, s);
+    else if (xt == QMV_F32)
+        ok = dispatch_m<0, true>(m, bpl, w, x, y, s);
     else
-        ok = mix ? dispatch_m<1, true>(m, bpl, w, x, y, rpw, s) : dispatch_m<1, false>(m, bpl, w, x, y, rpw, s);
+        ok = dispatch_m<1, true>(m, bpl, w, x, y, s);
     if (!ok) return nullptr;
-    return mix ? "q4_0.lds-x.fma-mix" : "q4_0.lds-x.cvt-ubyte";
+    return cvt ? "q4_0.lds-x.cvt-ubyte" : "q4_0.lds-x.fma-mix";
 }
 
 }  // namespace qmv

@@ -111,3 +111,121 @@ def test_q4_0_limit_is_reported(qmv):
     with pytest.raises(qmv.QmvError) as e:
         qmv.gemv(W, x)
     assert e.value.code == -9
+
+
+# ------------------------------------------------------------------ q6_K
+
+Q6_SMALL = [(1, 256), (3, 512), (37, 1024), (64, 2048), (100, 4096), (20, 11008), (10, 16384), (5, 768)]
+
+
+@pytest.mark.parametrize("n,k", Q6_SMALL)
+def test_q6k_small_full_parity(qmv, n, k):
+    run_case(qmv, synth.FMT_Q6_K, n, k, 1, synth.DT_F32, seed=n + k)
+
+
+def test_q6k_parity_config_256x1024_seed0(qmv):
+    # the q6_K decode workload: 256 x 1024, four super-blocks per row, seed 0, all rows
+    err = run_case(qmv, synth.FMT_Q6_K, 256, 1024, 1, synth.DT_F32, seed=0,
+                   expect_path="q6_K.lds-x.fma-mix.rowgroup")
+    print("max |err| / sum|w||x| =", err)
+
+
+@pytest.mark.parametrize("m", [2, 4, 8])
+@pytest.mark.parametrize("xt", [synth.DT_F32, synth.DT_BF16])
+def test_q6k_batched(qmv, m, xt):
+    run_case(qmv, synth.FMT_Q6_K, 70, 2048, m, xt, seed=m + 100)
+
+
+@pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096)])
+def test_q6k_large_sampled(qmv, n, k):
+    run_case(qmv, synth.FMT_Q6_K, n, k, 1, synth.DT_F32, seed=0, rows=sample_rows(n))
+
+
+def test_q6k_unit_vector_returns_column_exactly(qmv):
+    import torch
+    n, k = 96, 2048
+    w = synth.gen_weights(synth.FMT_Q6_K, n, k, seed=7)
+    W = qweights(synth.FMT_Q6_K, n, k, w)
+    dense = oracle.dequant(oracle.Mat(synth.FMT_Q6_K, n, k, w))
+    assert np.array_equal(dense.astype(np.float32).astype(np.float64), dense)  # exact in fp32
+    for j in (0, 15, 16, 64, 100, 127, 128, 255, 256, 2047):
+        e = np.zeros((1, k), dtype=np.float32)
+        e[0, j] = 1.0
+        y = qmv.gemv(W, x_to_device(e, synth.DT_F32))
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy()[0], dense[:, j].astype(np.float32)), j
+
+
+def test_q6k_all_codes_32_give_zero(qmv):
+    import torch
+    n, k = 16, 1024
+    w = synth.gen_weights(synth.FMT_Q6_K, n, k, seed=3)
+    w["ql"][:] = 0x00
+    w["qh"][:] = 0xAA  # every 2-bit field = 2, so q = 0 | 2 << 4 = 32
+    W = qweights(synth.FMT_Q6_K, n, k, w)
+    y = qmv.gemv(W, x_to_device(synth.gen_x(1, k, seed=3), synth.DT_F32))
+    torch.cuda.synchronize()
+    assert np.all(y.cpu().numpy() == 0.0)
+
+
+def test_q4_0_all_codes_8_give_zero(qmv):
+    # every weight is d * (8 - 8) = 0, so sum |w||x| = 0 and the output must be exactly 0
+    import torch
+    n, k = 40, 4096
+    w = synth.gen_weights(synth.FMT_Q4_0, n, k, seed=2)
+    w["qs"][:] = 0x88
+    y = qmv.gemv(qweights(synth.FMT_Q4_0, n, k, w), x_to_device(synth.gen_x(1, k, seed=2), synth.DT_F32))
+    torch.cuda.synchronize()
+    assert np.all(y.cpu().numpy() == 0.0)
+
+
+def test_q4_0_near_degenerate_rows_stay_within_bound(qmv):
+    # rows that are zero except for a few weights: the error must stay relative to sum |w||x|
+    n, k = 32, 8192
+    w = synth.gen_weights(synth.FMT_Q4_0, n, k, seed=12)
+    w["qs"][:] = 0x88
+    rng = np.random.default_rng(12)
+    for r in range(n):
+        for b in rng.choice(k // 32, size=r % 4 + 1, replace=False):
+            w["qs"][r, b, rng.integers(16)] = rng.integers(256)
+    import torch
+    x = synth.gen_x(1, k, seed=12) * np.float32(100.0)
+    y = qmv.gemv(qweights(synth.FMT_Q4_0, n, k, w), x_to_device(x, synth.DT_F32))
+    torch.cuda.synchronize()
+    yr, b = oracle.gemv(oracle.Mat(synth.FMT_Q4_0, n, k, w), x)
+    assert_parity(y.cpu().numpy(), yr, b, "near-degenerate q4_0")
+
+
+# ------------------------------------------------------------- 4-bit codebook
+
+CB4_SMALL = [(1, 128), (9, 384), (64, 2048), (77, 7168), (50, 11008 // 128 * 128), (13, 16384)]
+
+
+@pytest.mark.parametrize("n,k", CB4_SMALL)
+@pytest.mark.parametrize("xt", [synth.DT_BF16, synth.DT_F32])
+def test_cb4_small_full_parity(qmv, n, k, xt):
+    run_case(qmv, synth.FMT_CB4, n, k, 1, xt, seed=n + k, expect_path="cb4.lds-table.fma-mix")
+
+
+@pytest.mark.parametrize("m", [2, 4])
+def test_cb4_batched(qmv, m):
+    run_case(qmv, synth.FMT_CB4, 40, 2048, m, synth.DT_BF16, seed=m + 7)
+
+
+@pytest.mark.parametrize("n,k", [(2048, 7168), (7168, 2048)])
+def test_cb4_expert_shapes_sampled(qmv, n, k):
+    run_case(qmv, synth.FMT_CB4, n, k, 1, synth.DT_BF16, seed=0, rows=sample_rows(n))
+
+
+def test_cb4_unit_vector_returns_codebook_entry_exactly(qmv):
+    import torch
+    n, k = 64, 1024
+    w = synth.gen_weights(synth.FMT_CB4, n, k, seed=11)
+    W = qweights(synth.FMT_CB4, n, k, w)
+    dense = oracle.dequant(oracle.Mat(synth.FMT_CB4, n, k, w)).astype(np.float32)
+    for j in (0, 1, 127, 128, 500, 1023):
+        e = np.zeros((1, k), dtype=np.float32)
+        e[0, j] = 1.0
+        y = qmv.gemv(W, x_to_device(e, synth.DT_F32))
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy()[0], dense[:, j]), j

@@ -1,0 +1,85 @@
+"""GPU checks of the unpack stage (dense dequantization) and of the int8 activation
+quantizer, both against the CPU oracle: bit-exact where the values are exact."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import qweights
+from test_oracle import load_golden
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qmv():
+    import torch
+    assert torch.cuda.is_available()
+    import bit_weight_quantized_dequant_amd as q
+    q.lib()
+    return q
+
+
+@pytest.mark.parametrize("fmt,n,k", [(synth.FMT_Q4_0, 33, 4096), (synth.FMT_Q6_K, 17, 2048),
+                                     (synth.FMT_CB4, 19, 1024), (synth.FMT_Q6_K, 256, 1024)])
+def test_dequant_bit_exact(qmv, fmt, n, k):
+    import torch
+    w = synth.gen_weights(fmt, n, k, seed=n)
+    out = qmv.dequant(qweights(fmt, n, k, w))
+    torch.cuda.synchronize()
+    assert qmv.last_path().startswith("dequant.")
+    ref = oracle.dequant(oracle.Mat(fmt, n, k, w))
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+    if fmt != synth.FMT_CB4:
+        codes = oracle.codes(oracle.Mat(fmt, n, k, w))
+        assert codes.min() >= 0 and codes.max() <= (15 if fmt == synth.FMT_Q4_0 else 63)
+
+
+def test_dequant_aq_within_two_roundings(qmv):
+    import torch
+    n, k = 23, 512
+    w = synth.gen_weights(synth.FMT_AQ2X8, n, k, seed=4)
+    out = qmv.dequant(qweights(synth.FMT_AQ2X8, n, k, w)).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    ref = oracle.dequant(oracle.Mat(synth.FMT_AQ2X8, n, k, w))
+    # s*(C1+C2): one rounding of the sum, one of the product (each <= 2^-24 relative)
+    s = w["s"].astype(np.float64)[:, None]
+    mag = s * (np.abs(w["cbk"][0][w["codes"][:, :, 0]].astype(np.float64)) +
+               np.abs(w["cbk"][1][w["codes"][:, :, 1]].astype(np.float64))).reshape(n, k)
+    assert np.all(np.abs(out - ref) <= 2.0 ** -23 * (mag + np.abs(ref)))
+
+
+def _quant_gpu(qmv, x):
+    import torch
+    xq, xs = qmv.quant_act(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    assert qmv.last_path() == "quant_act.dpp8"
+    return xq.cpu().numpy(), xs.cpu().numpy()
+
+
+@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (512, 4096), (512, 11008)])
+def test_quantizer_bit_exact_random(qmv, m, k):
+    x = synth.gen_x(m, k, seed=m + k)
+    xq, xs = _quant_gpu(qmv, x)
+    rq, rs = oracle.quant_act(x)
+    assert np.array_equal(xq, rq)
+    assert np.array_equal(xs.view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantizer_golden_and_edge_blocks(qmv):
+    g = load_golden("quant_act.txt")
+    rng = np.random.default_rng(5)
+    blocks = [np.array(g["a_x"], dtype=np.float32), np.zeros(32, np.float32),
+              np.array(g["c_x"], dtype=np.float32),
+              # ties after division: x = (j + 0.5) * xs for a power-of-two amax
+              (np.arange(32, dtype=np.float32) - 15.5) * np.float32(2.0) ** -3,
+              # tiny and huge magnitudes, a single nonzero, negative maximum
+              rng.standard_normal(32).astype(np.float32) * np.float32(1e-30),
+              rng.standard_normal(32).astype(np.float32) * np.float32(1e30),
+              np.eye(32, dtype=np.float32)[7] * np.float32(-3.0)]
+    x = np.concatenate(blocks)[None, :]
+    xq, xs = _quant_gpu(qmv, x)
+    rq, rs = oracle.quant_act(x)
+    assert np.array_equal(xq, rq)
+    assert np.array_equal(xs.view(np.uint32), rs.view(np.uint32))
+    assert xq[0, :32].tolist() == g["a_xq"] and xq[0, 64:96].tolist() == g["c_xq"]
