@@ -15,6 +15,12 @@ QMV_DEV uint4 ld_stream16(const void *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16 bytes from LDS at byte address a (16-byte aligned).
+QMV_DEV uint4 lds_ld16(uint32_t a) {
+    const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)a;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // IEEE binary16 bits -> float (exact; subnormals kept).
 QMV_DEV float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 

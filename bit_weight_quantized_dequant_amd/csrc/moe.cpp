@@ -1,12 +1,8 @@
-// moe.cpp-style dispatch and launchers for variants that are not built yet: an
-// unsupported combination reports "unsupported" so the C ABI returns QMV_ERR_LIMIT
-// instead of launching anything.
+// Format dispatch of the routed-expert FFN: an unsupported format combination reports
+// "unsupported" (nullptr) so the C ABI returns QMV_ERR_LIMIT instead of launching.
 #include "qmv_internal.h"
 
 namespace qmv {
-const char *launch_gemv_aq(const qmv_weights *, int, const void *, int, float *, hipStream_t) { return nullptr; }
-const char *launch_gemm_q6k(const qmv_weights *, int, const int8_t *, const float *, float *, int32_t *,
-                            hipStream_t) { return nullptr; }
 
 const char *launch_moe_ffn(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,
                            int n_experts, const int32_t *ids, int n_ids, const void *x, int xt, float *h,

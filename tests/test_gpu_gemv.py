@@ -229,3 +229,49 @@ def test_cb4_unit_vector_returns_codebook_entry_exactly(qmv):
         y = qmv.gemv(W, x_to_device(e, synth.DT_F32))
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy()[0], dense[:, j]), j
+
+
+# ------------------------------------------------------------- 2-bit additive
+
+AQ_SMALL = [(1, 8), (5, 24), (9, 64), (33, 1000), (64, 4096), (17, 4096 + 8), (40, 14336)]
+
+
+@pytest.mark.parametrize("n,k", AQ_SMALL)
+def test_aq_small_full_parity(qmv, n, k):
+    run_case(qmv, synth.FMT_AQ2X8, n, k, 1, synth.DT_BF16, seed=n + k, expect_path="aq2x8.lds-codebook.fma-mix")
+
+
+@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("n,k", [(14336, 4096), (4096, 14336)])
+def test_aq_config_shapes_sampled(qmv, m, n, k):
+    run_case(qmv, synth.FMT_AQ2X8, n, k, m, synth.DT_BF16, seed=0, rows=sample_rows(n))
+
+
+@pytest.mark.parametrize("m", [2, 3, 8])
+def test_aq_batched_f32(qmv, m):
+    run_case(qmv, synth.FMT_AQ2X8, 50, 2048, m, synth.DT_F32, seed=m + 3)
+
+
+def test_aq_cancelling_codebooks_give_zero(qmv):
+    # C2 = -C1: every weight is exactly 0 when c1 == c2, so the row must come out as 0
+    import torch
+    n, k = 24, 4096
+    w = synth.gen_weights(synth.FMT_AQ2X8, n, k, seed=5)
+    w["cbk"][1] = -w["cbk"][0]
+    w["codes"][:, :, 1] = w["codes"][:, :, 0]
+    y = qmv.gemv(qweights(synth.FMT_AQ2X8, n, k, w), x_to_device(synth.gen_x(1, k, synth.DT_BF16, seed=5), synth.DT_BF16))
+    torch.cuda.synchronize()
+    assert np.all(y.cpu().numpy() == 0.0)
+
+
+def test_aq_single_codebook_vq_case(qmv):
+    # C2 = 0 reduces the additive code to plain vector quantization
+    n, k = 32, 2048
+    w = synth.gen_weights(synth.FMT_AQ2X8, n, k, seed=6)
+    w["cbk"][1] = 0
+    import torch
+    x = synth.gen_x(1, k, synth.DT_BF16, seed=6)
+    y = qmv.gemv(qweights(synth.FMT_AQ2X8, n, k, w), x_to_device(x, synth.DT_BF16))
+    torch.cuda.synchronize()
+    yr, b = oracle.gemv(oracle.Mat(synth.FMT_AQ2X8, n, k, w), x, oracle.BF16)
+    assert_parity(y.cpu().numpy(), yr, b, "aq vq")
