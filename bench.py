@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only-primary", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--secondary", default="q6_K_gemv,cb4_moe,aq2x8,q6_K_gemm",
+                    help="comma-separated secondary workloads to run")
     return ap.parse_args()
 
 
@@ -59,13 +61,21 @@ def dev_planes(planes: dict):
 
 
 def make_pool(qmv, fmt, n, k, seed, copies):
-    """`copies` distinct device copies of one generated matrix (device-to-device clones)."""
+    """`copies` distinct device copies of one generated matrix: each plane is one
+    [copies, ...] tensor filled by device-side copies, and copy c is its slice c."""
+    import torch
     host = synth.gen_weights(fmt, n, k, seed=seed)
     first = dev_planes(host)
-    pool = [qmv.QWeights(fmt, n, k, first)]
-    for _ in range(copies - 1):
-        pool.append(qmv.QWeights(fmt, n, k, {kk: v.clone() for kk, v in first.items()}))
+    big = {name: torch.empty((copies, *t.shape), dtype=t.dtype, device="cuda") for name, t in first.items()}
+    for name, t in first.items():
+        big[name][:] = t
+    pool = [qmv.QWeights(fmt, n, k, {name: big[name][c] for name in big}) for c in range(copies)]
+    pool[0]._keep = big
     return host, pool
+
+
+def pool_copies(bytes_per_copy):
+    return max(2, -(-POOL_BYTES // bytes_per_copy))
 
 
 def graph_of(fn, count):
@@ -147,6 +157,103 @@ def q4_0_workload(qmv, steps, warmup):
             "copies": copies, "pool_bytes": copies * per_set, "shapes": per_shape}
 
 
+def gemv_workload(qmv, fmt, shapes, batch, xt, steps, label):
+    """Batch-`batch` GEMVs over `shapes` (one step = one GEMV per shape), rotating pool."""
+    import torch
+    per_set = sum(qmv.weight_bytes(fmt, n, k) for n, k in shapes)
+    copies = pool_copies(per_set)
+    mats, xs, ys, algo = [], [], [], []
+    xbytes = 4 if xt == synth.DT_F32 else 2
+    for i, (n, k) in enumerate(shapes):
+        _, pool = make_pool(qmv, fmt, n, k, seed=i, copies=copies)
+        mats.append(pool)
+        x = synth.gen_x(batch, k, xt, seed=i)
+        xd = torch.from_numpy(x).cuda() if xt == synth.DT_F32 else \
+            torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+        xs.append(xd)
+        ys.append(torch.empty((batch, n), dtype=torch.float32, device="cuda"))
+        algo.append(qmv.weight_bytes(fmt, n, k) + xbytes * batch * k + 4 * batch * n)
+
+    def step(i):
+        for s in range(len(shapes)):
+            qmv.gemv(mats[s][i % copies], xs[s], ys[s])
+
+    g = graph_of(step, steps)
+    ms = time_graph(g, steps)
+    qmv.gemv(mats[0][0], xs[0], ys[0])
+    gbs = sum(algo) / ms / 1e6
+    return {"workload": label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(ms, 5), "bytes_per_step": sum(algo), "pool_copies": copies,
+            "path": qmv.last_path(), "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"}}
+
+
+def moe_workload(qmv, tokens, label):
+    """Routed-expert FFN, batch 1: 256 experts of gate/up 2048x7168 and down 7168x2048
+    (4-bit codebook, one 16-entry fp16 codebook per 128 weights), top-8 per token.
+    The 8.46 GB expert set is resident; its bytes are drawn on the device with a seeded
+    generator (throughput does not depend on the values; parity is tested elsewhere)."""
+    import torch
+    E, dm, dff = 256, 7168, 2048
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+
+    def planes(n, k):
+        idx = torch.randint(0, 256, (E, n, k // 2), dtype=torch.uint8, device="cuda", generator=gen)
+        cb = torch.randn((E, n, k // 128, 16), device="cuda", generator=gen) * 0.02
+        cb = torch.sort(cb, dim=-1).values.to(torch.float16)
+        return {"idx": idx, "cb": cb}
+
+    G = qmv.QWeights(qmv.CB4, dff, dm, planes(dff, dm))
+    U = qmv.QWeights(qmv.CB4, dff, dm, planes(dff, dm))
+    D = qmv.QWeights(qmv.CB4, dm, dff, planes(dm, dff))
+    ids = torch.from_numpy(synth.gen_moe_ids(tokens, E, 8, seed=0)).cuda()
+    x = torch.from_numpy(synth.gen_x(tokens, dm, synth.DT_BF16, seed=0).view(np.int16).copy()).view(torch.bfloat16).cuda()
+    h = torch.empty((8, dff), dtype=torch.float32, device="cuda")
+    y = torch.empty((8, dm), dtype=torch.float32, device="cuda")
+    per_tok = 8 * (qmv.weight_bytes(qmv.CB4, dff, dm) * 2 + qmv.weight_bytes(qmv.CB4, dm, dff)) + 2 * dm + \
+        8 * dff * 4 * 2 + 8 * dm * 4
+
+    def step(i):
+        qmv.moe_ffn(G, U, D, E, ids[i % tokens], x[i % tokens], h, y)
+
+    g = graph_of(step, tokens)
+    ms = time_graph(g, tokens)
+    gbs = per_tok / ms / 1e6
+    return {"workload": label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "ms_per_token": round(ms, 5), "bytes_per_token": per_tok, "tokens": tokens,
+            "path": qmv.last_path(), "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"}}
+
+
+def gemm_workload(qmv, steps, label):
+    """q6_K prefill GEMM, M = 512 tokens, W 11008x4096 and 4096x11008: TOPS = 2 M N K / time,
+    for the int8 contraction alone (activations already quantized) and end to end."""
+    import torch
+    M = 512
+    out = {"workload": label, "unit": "TOPS", "shapes": []}
+    tot_ops, tot_ms, tot_ms_e2e = 0, 0.0, 0.0
+    for i, (n, k) in enumerate([(11008, 4096), (4096, 11008)]):
+        _, pool = make_pool(qmv, synth.FMT_Q6_K, n, k, seed=i, copies=4)
+        x = torch.from_numpy(synth.gen_x(M, k, seed=i)).cuda()
+        xq, xs = qmv.quant_act(x)
+        y = torch.empty((M, n), dtype=torch.float32, device="cuda")
+        ws = torch.empty(qmv.workspace_bytes(pool[0], M), dtype=torch.uint8, device="cuda")
+        R = max(8, steps // 4)
+        ms = time_graph(graph_of(lambda j: qmv.gemm_q8(pool[j % 4], xq, xs, y), R), R)
+        path = qmv.last_path()
+        ms2 = time_graph(graph_of(lambda j: qmv.gemm(pool[j % 4], x, y, ws), R), R)
+        ops = 2 * M * n * k
+        tot_ops += ops
+        tot_ms += ms
+        tot_ms_e2e += ms2
+        out["shapes"].append({"shape": f"{n}x{k}", "M": M, "ms": round(ms, 5), "TOPS": round(ops / ms / 1e9, 1),
+                              "ms_with_quantizer": round(ms2, 5), "path": path})
+    tops = tot_ops / tot_ms / 1e9
+    out.update({"value": round(tops, 1), "frac_of_peak": round(tops / INT8_PEAK_TOPS, 4),
+                "TOPS_with_quantizer": round(tot_ops / tot_ms_e2e / 1e9, 1),
+                "roofline": {"bound": "mfma", "peak": INT8_PEAK_TOPS, "unit": "TOPS"}})
+    return out
+
+
 def cpu_baseline(seconds):
     """The oracle on the same three matrices (all rows), repeated until `seconds` of work."""
     import oracle
@@ -207,6 +314,22 @@ def main():
                      "frac": round(dom["frac"], 4), "traffic": None},
         "shapes": prim["shapes"],
     }
+    if not a.only_primary:
+        sec = {}
+        want = set(a.secondary.split(","))
+        if "q6_K_gemv" in want:
+            sec["q6_K_gemv"] = gemv_workload(qmv, synth.FMT_Q6_K, [(256, 1024)], 1, synth.DT_F32, 200,
+                                             "q6_K GEMV batch 1, 256x1024, fp32 x")
+        if "cb4_moe" in want:
+            sec["cb4_moe"] = moe_workload(qmv, 64, "4-bit codebook MoE FFN, batch 1, 256 experts top-8, "
+                                                   "gate/up 2048x7168 + down 7168x2048, bf16 x")
+        for b in ((1, 4) if "aq2x8" in want else ()):
+            sec[f"aq2x8_gemv_b{b}"] = gemv_workload(qmv, synth.FMT_AQ2X8, [(14336, 4096), (4096, 14336)], b,
+                                                    synth.DT_BF16, 50,
+                                                    f"2-bit additive GEMV batch {b}, 14336x4096 + 4096x14336, bf16 x")
+        if "q6_K_gemm" in want:
+            sec["q6_K_gemm"] = gemm_workload(qmv, a.steps, "q6_K prefill GEMM, M=512, 11008x4096 + 4096x11008")
+        out["secondary"] = sec
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
     print(json.dumps(out))
