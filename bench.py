@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only-primary", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--secondary", default="q6_K_gemv,cb4_moe,aq2x8,q6_K_gemm",
                     help="comma-separated secondary workloads to run")
     return ap.parse_args()
@@ -254,6 +256,19 @@ def gemm_workload(qmv, steps, label):
     return out
 
 
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed PMC record, or None
+    when the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "q4_0_gemv_4096x11008_traffic.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])).hexdigest()
+    except (OSError, ValueError, KeyError):
+        return None
+    return rec["traffic_bytes_per_launch"] if h == rec["sources_sha256"] else None
+
+
 def cpu_baseline(seconds):
     """The oracle on the same three matrices (all rows), repeated until `seconds` of work."""
     import oracle
@@ -289,6 +304,12 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     qmv.lib()
+    if a.copy_ref:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     prim = q4_0_workload(qmv, a.steps, a.warmup)
     dom = max(prim["shapes"], key=lambda s: s["avg_launch_ms"])
     out = {
@@ -311,7 +332,8 @@ def main():
         "frac_of_peak": round(prim["GBps"] / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": f"q4_0 GEMV {dom['shape']} ({dom['path']})",
                      "achieved": round(dom["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom["frac"], 4), "traffic": None},
+                     "frac": round(dom["frac"], 4),
+                     "traffic": recorded_traffic() if dom["shape"] == "4096x11008" else None},
         "shapes": prim["shapes"],
     }
     if not a.only_primary:
