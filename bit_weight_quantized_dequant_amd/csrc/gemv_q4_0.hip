@@ -25,18 +25,7 @@
 namespace qmv {
 namespace {
 
-constexpr int WG = 512;  // threads per workgroup: 8 waves, one output row each
-constexpr int WAVES = WG / 64;
 constexpr int XS = 36;   // floats per staged 32-activation block
-
-// Stage x [M][k] into LDS: block (m, b) at sx[(m*nblk + b)*XS].  Each thread moves
-// coalesced 16-byte chunks.
-template <int M, int XT>
-__device__ void stage_x32(const void *x, int k, float *sx) {
-    const int total = M * (k >> 2);
-    for (int c = threadIdx.x; c < total; c += WG)
-        *(float4 *)(sx + (c >> 3) * XS + (c & 7) * 4) = ld_act4<XT>(x, (int64_t)c * 4);
-}
 
 // sum_{i<32} (q_i - 8) * x_i for one block (codes in 4 dwords, staged x at xb); every
 // product is exact.
@@ -87,28 +76,42 @@ QMV_DEV float dot_q4_cvt(uint4 q, const float *xb) {
     return a + b;
 }
 
-// One wave computes one row; lane l owns blocks l, l+64, ... of it.  The activations are
-// staged before the weight loads are issued: vector loads return in order, so x staged
-// after the weights would wait for every weight byte before the first FMA.
-template <int M, int BPL, int XT, bool MIX>
+// One wave computes one row; lane l owns blocks l, l+64, ... of it.
+//   * The activation loads are issued first and the first weight load right after them,
+//     before x is written to LDS: vector loads complete in issue order, so x (issued
+//     first) is not held back by weight bytes.
+//   * Then one weight load stays in flight per wave: block u+1 is requested when block u
+//     is consumed (sched_barrier keeps the compiler from hoisting the loads back into one
+//     burst).  Issued all at once, a wave's blocks land all over the global request queue
+//     and, completing in order, become usable only near the end of the stream, which
+//     pushed the whole unpack into a tail after the last byte.
+template <int WG, int M, int BPL, int XT, bool MIX>
 __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict__ qs,
                                                        const uint16_t *__restrict__ dsc,
                                                        const void *__restrict__ x,
                                                        float *__restrict__ y, int n, int k) {
     extern __shared__ float lds[];
+    constexpr int WAVES = WG / 64;
     const int nblk = k >> 5;
     float *sx = lds;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x * WAVES + wave;
 
-    stage_x32<M, XT>(x, k, sx);
+    // activations: XPT 16-byte chunks per thread; k <= 2048 * BPL, so M * k / 4 <= XPT * WG
+    constexpr int XPT = (M * BPL * 512 + WG - 1) / WG;
+    const int total = M * (k >> 2);
+    float4 xv[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; j++) {
+        const int c = threadIdx.x + j * WG;
+        xv[j] = c < total ? ld_act4<XT>(x, (int64_t)c * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 
     uint4 q[BPL];
     uint16_t dd[BPL];
     const uint4 *qr = (const uint4 *)(qs + (int64_t)row * (k >> 1));
     const uint16_t *dr = dsc + (int64_t)row * nblk;
-#pragma unroll
-    for (int u = 0; u < BPL; u++) {
+    auto load = [&](int u) {
         const int b = lane + 64 * u;
         if (row < n && b < nblk) {
             q[u] = ld_stream16(qr + b);
@@ -117,6 +120,12 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
             q[u] = make_uint4(0, 0, 0, 0);
             dd[u] = 0;
         }
+    };
+    load(0);
+#pragma unroll
+    for (int j = 0; j < XPT; j++) {
+        const int c = threadIdx.x + j * WG;
+        if (c < total) *(float4 *)(sx + (c >> 3) * XS + (c & 7) * 4) = xv[j];
     }
     __syncthreads();
 
@@ -125,6 +134,9 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
     for (int m = 0; m < M; m++) acc[m] = 0.f;
 #pragma unroll
     for (int u = 0; u < BPL; u++) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < BPL) load(u + 1);
+        __builtin_amdgcn_sched_barrier(0);
         const int b = lane + 64 * u;
         if (b < nblk) {
             const float d = h2f(dd[u]);
@@ -143,13 +155,19 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
     }
 }
 
+// 256-thread workgroups for short rows (more workgroups, x staged by fewer waves each),
+// 512 for long ones.
 template <int M, int BPL, int XT, bool MIX>
 void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     const int n = (int)w->n, k = (int)w->k, nblk = k >> 5;
     const size_t lds = (size_t)M * nblk * XS * sizeof(float);
-    const int grid = (n + WAVES - 1) / WAVES;
-    hipLaunchKernelGGL((gemv_q4_0_kernel<M, BPL, XT, MIX>), dim3(grid), dim3(WG), lds, s,
-                       (const uint8_t *)w->codes, (const uint16_t *)w->scales, x, y, n, k);
+    if (BPL <= 2) {
+        hipLaunchKernelGGL((gemv_q4_0_kernel<256, M, BPL, XT, MIX>), dim3((n + 3) / 4), dim3(256), lds, s,
+                           (const uint8_t *)w->codes, (const uint16_t *)w->scales, x, y, n, k);
+    } else {
+        hipLaunchKernelGGL((gemv_q4_0_kernel<512, M, BPL, XT, MIX>), dim3((n + 7) / 8), dim3(512), lds, s,
+                           (const uint8_t *)w->codes, (const uint16_t *)w->scales, x, y, n, k);
+    }
 }
 
 template <int M, int XT, bool MIX>
