@@ -25,10 +25,13 @@
 namespace qmv {
 namespace {
 
-constexpr int XS = 36;   // floats per staged 32-activation block
+constexpr int XS = 36;   // floats per staged 32-activation block (32 + 4 of padding)
+constexpr int XS4 = XS / 4;
+constexpr int MAX_CHUNKS = 4096;  // 16-byte activation chunks one workgroup stages (m*k <= 16384)
 
-// sum_{i<32} (q_i - 8) * x_i for one block (codes in 4 dwords, staged x at xb); every
-// product is exact.
+// sum_{i<32} (q_i - 8) * x_i for one block (codes in 4 dwords, activations in xb[0..31]).
+// Each (q - 8) is an exact binary16 half; v_fma_mix_f32 multiplies it by the fp32
+// activation inside a fused multiply-add, so the only roundings are those of the sums.
 QMV_DEV float dot_q4_mix(uint4 q, const float *xb) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     const qmv_h2 off_lo = {(_Float16)-1032.f, (_Float16)-1032.f};  // (1024 + q) - 1032 = q - 8
@@ -36,21 +39,19 @@ QMV_DEV float dot_q4_mix(uint4 q, const float *xb) {
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const float4 xl = *(const float4 *)(xb + 4 * i);       // weights 4i .. 4i+3
-        const float4 xh = *(const float4 *)(xb + 16 + 4 * i);  // weights 16+4i .. 16+4i+3
         const uint32_t w8 = w[i] >> 8;
         const qmv_h2 t0 = as_h2(and_or(w[i], 0x000F000Fu, 0x64006400u)) + off_lo;  // bytes 0, 2 low
         const qmv_h2 t1 = as_h2(and_or(w[i], 0x00F000F0u, 0x5C005C00u)) + off_hi;  // bytes 0, 2 high
         const qmv_h2 t2 = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) + off_lo;    // bytes 1, 3 low
         const qmv_h2 t3 = as_h2(and_or(w8, 0x00F000F0u, 0x5C005C00u)) + off_hi;    // bytes 1, 3 high
-        a0 = fmaf((float)t0.x, xl.x, a0);
-        a0 = fmaf((float)t0.y, xl.z, a0);
-        b0 = fmaf((float)t2.x, xl.y, b0);
-        b0 = fmaf((float)t2.y, xl.w, b0);
-        a1 = fmaf((float)t1.x, xh.x, a1);
-        a1 = fmaf((float)t1.y, xh.z, a1);
-        b1 = fmaf((float)t3.x, xh.y, b1);
-        b1 = fmaf((float)t3.y, xh.w, b1);
+        a0 = fmaf((float)t0.x, xb[4 * i + 0], a0);
+        a0 = fmaf((float)t0.y, xb[4 * i + 2], a0);
+        b0 = fmaf((float)t2.x, xb[4 * i + 1], b0);
+        b0 = fmaf((float)t2.y, xb[4 * i + 3], b0);
+        a1 = fmaf((float)t1.x, xb[16 + 4 * i + 0], a1);
+        a1 = fmaf((float)t1.y, xb[16 + 4 * i + 2], a1);
+        b1 = fmaf((float)t3.x, xb[16 + 4 * i + 1], b1);
+        b1 = fmaf((float)t3.y, xb[16 + 4 * i + 3], b1);
     }
     return (a0 + b0) + (a1 + b1) * 0.25f;
 }
@@ -61,45 +62,45 @@ QMV_DEV float dot_q4_cvt(uint4 q, const float *xb) {
     float a = 0.f, b = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const float4 xl = *(const float4 *)(xb + 4 * i);
-        const float4 xh = *(const float4 *)(xb + 16 + 4 * i);
         const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
-        a = fmaf((float)(lo & 0xFFu) - 8.f, xl.x, a);
-        a = fmaf((float)((lo >> 8) & 0xFFu) - 8.f, xl.y, a);
-        a = fmaf((float)((lo >> 16) & 0xFFu) - 8.f, xl.z, a);
-        a = fmaf((float)(lo >> 24) - 8.f, xl.w, a);
-        b = fmaf((float)(hi & 0xFFu) - 8.f, xh.x, b);
-        b = fmaf((float)((hi >> 8) & 0xFFu) - 8.f, xh.y, b);
-        b = fmaf((float)((hi >> 16) & 0xFFu) - 8.f, xh.z, b);
-        b = fmaf((float)(hi >> 24) - 8.f, xh.w, b);
+        a = fmaf((float)(lo & 0xFFu) - 8.f, xb[4 * i + 0], a);
+        a = fmaf((float)((lo >> 8) & 0xFFu) - 8.f, xb[4 * i + 1], a);
+        a = fmaf((float)((lo >> 16) & 0xFFu) - 8.f, xb[4 * i + 2], a);
+        a = fmaf((float)(lo >> 24) - 8.f, xb[4 * i + 3], a);
+        b = fmaf((float)(hi & 0xFFu) - 8.f, xb[16 + 4 * i + 0], b);
+        b = fmaf((float)((hi >> 8) & 0xFFu) - 8.f, xb[16 + 4 * i + 1], b);
+        b = fmaf((float)((hi >> 16) & 0xFFu) - 8.f, xb[16 + 4 * i + 2], b);
+        b = fmaf((float)(hi >> 24) - 8.f, xb[16 + 4 * i + 3], b);
     }
     return a + b;
 }
 
-// One wave computes one row; lane l owns blocks l, l+64, ... of it.
-//   * The activation loads are issued first and the first weight load right after them,
-//     before x is written to LDS: vector loads complete in issue order, so x (issued
-//     first) is not held back by weight bytes.
-//   * Then one weight load stays in flight per wave: block u+1 is requested when block u
-//     is consumed (sched_barrier keeps the compiler from hoisting the loads back into one
-//     burst).  Issued all at once, a wave's blocks land all over the global request queue
-//     and, completing in order, become usable only near the end of the stream, which
-//     pushed the whole unpack into a tail after the last byte.
+// One wave computes one row for all m activation rows; lane l owns blocks l, l+64, ...
+//   * The activation loads are issued first, then every weight load of the row (128-bit
+//     codes + the fp16 scale per block), then x is written to LDS.  The code is free of
+//     branches around loads: row and block indices are clamped (a lane past the row end
+//     re-reads the last block and its sum is dropped by a select), and activation chunks
+//     past the end are written to a junk slot after the staged blocks.  A branch around a
+//     load would split the block and make the compiler wait for that load on the spot,
+//     serialising the row into one memory round trip per block.
+//   * Vector loads complete in issue order, so the LDS writes wait for x only, and block u
+//     becomes usable as soon as loads 0..u have landed.
+//   * The 64 lane partials of a row are summed across the wavefront with DPP.
 template <int WG, int M, int BPL, int XT, bool MIX>
 __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict__ qs,
                                                        const uint16_t *__restrict__ dsc,
                                                        const void *__restrict__ x,
                                                        float *__restrict__ y, int n, int k) {
-    extern __shared__ float lds[];
+    extern __shared__ float4 sx4[];
     constexpr int WAVES = WG / 64;
+    constexpr int CH = M * BPL * 512 < MAX_CHUNKS ? M * BPL * 512 : MAX_CHUNKS;
+    constexpr int XPT = (CH + WG - 1) / WG;
     const int nblk = k >> 5;
-    float *sx = lds;
+    const int total = M * (k >> 2);  // 16-byte activation chunks, m-major; 8 per block
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x * WAVES + wave;
+    const int rowc = row < n ? row : n - 1;
 
-    // activations: XPT 16-byte chunks per thread; k <= 2048 * BPL, so M * k / 4 <= XPT * WG
-    constexpr int XPT = (M * BPL * 512 + WG - 1) / WG;
-    const int total = M * (k >> 2);
     float4 xv[XPT];
 #pragma unroll
     for (int j = 0; j < XPT; j++) {
@@ -109,23 +110,21 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
 
     uint4 q[BPL];
     uint16_t dd[BPL];
-    const uint4 *qr = (const uint4 *)(qs + (int64_t)row * (k >> 1));
-    const uint16_t *dr = dsc + (int64_t)row * nblk;
-    auto load = [&](int u) {
-        const int b = lane + 64 * u;
-        if (row < n && b < nblk) {
-            q[u] = ld_stream16(qr + b);
-            dd[u] = dr[b];
-        } else {
-            q[u] = make_uint4(0, 0, 0, 0);
-            dd[u] = 0;
-        }
-    };
-    load(0);
+    const uint4 *qr = (const uint4 *)(qs + (int64_t)rowc * (k >> 1));
+    const uint16_t *dr = dsc + (int64_t)rowc * nblk;
+#pragma unroll
+    for (int u = 0; u < BPL; u++) {
+        int b = lane + 64 * u;
+        b = b < nblk ? b : nblk - 1;
+        q[u] = ld_stream16(qr + b);
+        dd[u] = dr[b];
+    }
+
 #pragma unroll
     for (int j = 0; j < XPT; j++) {
         const int c = threadIdx.x + j * WG;
-        if (c < total) *(float4 *)(sx + (c >> 3) * XS + (c & 7) * 4) = xv[j];
+        const int cc = c < total ? c : total;  // chunk `total` is the junk slot
+        sx4[(cc >> 3) * XS4 + (cc & 7)] = xv[j];
     }
     __syncthreads();
 
@@ -134,18 +133,17 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
     for (int m = 0; m < M; m++) acc[m] = 0.f;
 #pragma unroll
     for (int u = 0; u < BPL; u++) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (u + 1 < BPL) load(u + 1);
-        __builtin_amdgcn_sched_barrier(0);
         const int b = lane + 64 * u;
-        if (b < nblk) {
-            const float d = h2f(dd[u]);
+        const int bc = b < nblk ? b : nblk - 1;
+        const float d = h2f(dd[u]);
 #pragma unroll
-            for (int m = 0; m < M; m++) {
-                const float *xb = sx + (m * nblk + b) * XS;
-                const float s = MIX ? dot_q4_mix(q[u], xb) : dot_q4_cvt(q[u], xb);
-                acc[m] = fmaf(d, s, acc[m]);
-            }
+        for (int m = 0; m < M; m++) {
+            float xb[32];
+#pragma unroll
+            for (int i = 0; i < 8; i++) *(float4 *)(xb + 4 * i) = sx4[(m * nblk + bc) * XS4 + i];
+            const float s = MIX ? dot_q4_mix(q[u], xb) : dot_q4_cvt(q[u], xb);
+            const float v = fmaf(d, s, acc[m]);
+            acc[m] = b < nblk ? v : acc[m];
         }
     }
 #pragma unroll
@@ -160,7 +158,7 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
 template <int M, int BPL, int XT, bool MIX>
 void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     const int n = (int)w->n, k = (int)w->k, nblk = k >> 5;
-    const size_t lds = (size_t)M * nblk * XS * sizeof(float);
+    const size_t lds = ((size_t)M * nblk * XS + 4) * sizeof(float);
     if (BPL <= 2) {
         hipLaunchKernelGGL((gemv_q4_0_kernel<256, M, BPL, XT, MIX>), dim3((n + 3) / 4), dim3(256), lds, s,
                            (const uint8_t *)w->codes, (const uint16_t *)w->scales, x, y, n, k);
@@ -207,7 +205,7 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
     const int64_t n = w->n, k = w->k, nblk = k / 32;
     const int bpl = (int)((nblk + 63) / 64);
     if (bpl > 8 || (int64_t)m * k > 16384 || n > INT32_MAX) return nullptr;
-    const size_t lds = (size_t)m * nblk * XS * sizeof(float);
+    const size_t lds = ((size_t)m * nblk * XS + 4) * sizeof(float);
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
     const bool cvt = strcmp(forced_path(), "q4_0.cvt") == 0 && m == 1 && xt == QMV_F32;
     bool ok;
