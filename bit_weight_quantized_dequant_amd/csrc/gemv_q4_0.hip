@@ -29,6 +29,15 @@ constexpr int XS = 36;   // floats per staged 32-activation block (32 + 4 of pad
 constexpr int XS4 = XS / 4;
 constexpr int MAX_CHUNKS = 4096;  // 16-byte activation chunks one workgroup stages (m*k <= 16384)
 
+// Activation chunks each thread stages: enough for m * k / 4 chunks at k <= 2048 * BPL.
+constexpr int xchunks_per_thread(int wg, int m, int bpl) {
+    return ((m * bpl * 512 < MAX_CHUNKS ? m * bpl * 512 : MAX_CHUNKS) + wg - 1) / wg;
+}
+// LDS bytes: every staged chunk slot (XPT * WG of them, 8 per padded 36-float block).
+constexpr size_t lds_bytes(int wg, int m, int bpl) {
+    return (size_t)xchunks_per_thread(wg, m, bpl) * wg / 8 * XS * sizeof(float);
+}
+
 // sum_{i<32} (q_i - 8) * x_i for one block (codes in 4 dwords, activations in xb[0..31]).
 // Each (q - 8) is an exact binary16 half; v_fma_mix_f32 multiplies it by the fp32
 // activation inside a fused multiply-add, so the only roundings are those of the sums.
@@ -93,8 +102,7 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
                                                        float *__restrict__ y, int n, int k) {
     extern __shared__ float4 sx4[];
     constexpr int WAVES = WG / 64;
-    constexpr int CH = M * BPL * 512 < MAX_CHUNKS ? M * BPL * 512 : MAX_CHUNKS;
-    constexpr int XPT = (CH + WG - 1) / WG;
+    constexpr int XPT = xchunks_per_thread(WG, M, BPL);
     const int nblk = k >> 5;
     const int total = M * (k >> 2);  // 16-byte activation chunks, m-major; 8 per block
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -105,7 +113,7 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
 #pragma unroll
     for (int j = 0; j < XPT; j++) {
         const int c = threadIdx.x + j * WG;
-        xv[j] = c < total ? ld_act4<XT>(x, (int64_t)c * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        xv[j] = ld_act4<XT>(x, (int64_t)(c < total ? c : total - 1) * 4);
     }
 
     uint4 q[BPL];
@@ -119,13 +127,12 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
         q[u] = ld_stream16(qr + b);
         dd[u] = dr[b];
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load is issued before the LDS writes wait on x
 
+    // chunk c -> block c >> 3, slot c & 7; chunks past the end land in the padding blocks
+    float4 *dst = sx4 + (threadIdx.x >> 3) * XS4 + (threadIdx.x & 7);
 #pragma unroll
-    for (int j = 0; j < XPT; j++) {
-        const int c = threadIdx.x + j * WG;
-        const int cc = c < total ? c : total;  // chunk `total` is the junk slot
-        sx4[(cc >> 3) * XS4 + (cc & 7)] = xv[j];
-    }
+    for (int j = 0; j < XPT; j++) dst[j * (WG / 8) * XS4] = xv[j];
     __syncthreads();
 
     float acc[M];
@@ -157,14 +164,15 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
 // 512 for long ones.
 template <int M, int BPL, int XT, bool MIX>
 void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
-    const int n = (int)w->n, k = (int)w->k, nblk = k >> 5;
-    const size_t lds = ((size_t)M * nblk * XS + 4) * sizeof(float);
+    const int n = (int)w->n, k = (int)w->k;
     if (BPL <= 2) {
-        hipLaunchKernelGGL((gemv_q4_0_kernel<256, M, BPL, XT, MIX>), dim3((n + 3) / 4), dim3(256), lds, s,
-                           (const uint8_t *)w->codes, (const uint16_t *)w->scales, x, y, n, k);
+        hipLaunchKernelGGL((gemv_q4_0_kernel<256, M, BPL, XT, MIX>), dim3((n + 3) / 4), dim3(256),
+                           lds_bytes(256, M, BPL), s, (const uint8_t *)w->codes,
+                           (const uint16_t *)w->scales, x, y, n, k);
     } else {
-        hipLaunchKernelGGL((gemv_q4_0_kernel<512, M, BPL, XT, MIX>), dim3((n + 7) / 8), dim3(512), lds, s,
-                           (const uint8_t *)w->codes, (const uint16_t *)w->scales, x, y, n, k);
+        hipLaunchKernelGGL((gemv_q4_0_kernel<512, M, BPL, XT, MIX>), dim3((n + 7) / 8), dim3(512),
+                           lds_bytes(512, M, BPL), s, (const uint8_t *)w->codes,
+                           (const uint16_t *)w->scales, x, y, n, k);
     }
 }
 
@@ -205,7 +213,7 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
     const int64_t n = w->n, k = w->k, nblk = k / 32;
     const int bpl = (int)((nblk + 63) / 64);
     if (bpl > 8 || (int64_t)m * k > 16384 || n > INT32_MAX) return nullptr;
-    const size_t lds = ((size_t)m * nblk * XS + 4) * sizeof(float);
+    const size_t lds = bpl <= 2 ? lds_bytes(256, m, bpl) : lds_bytes(512, m, bpl);
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
     const bool cvt = strcmp(forced_path(), "q4_0.cvt") == 0 && m == 1 && xt == QMV_F32;
     bool ok;
