@@ -41,19 +41,10 @@ struct Cb4Args {
     int n, k, n_experts;
 };
 
-template <int M, int XT>
-__device__ void stage_x(const void *x, int k, float *sx) {
-    const int total = M * (k >> 2);
-    for (int c = threadIdx.x; c < total; c += WG)
-        *(float4 *)(sx + (c >> 3) * XS + (c & 7) * 4) = ld_act4<XT>(x, (int64_t)c * 4);
-}
-
-// Copy one row's codebooks (ngroups x 16 fp16 = ngroups * 32 bytes) into LDS (wave-local).
-QMV_DEV void stage_tables(const uint16_t *cb, int ngroups, uint16_t *tab, int lane) {
-    const uint4 *src = (const uint4 *)cb;
-    uint4 *dst = (uint4 *)tab;
-    for (int i = lane; i < ngroups * 2; i += 64) dst[i] = src[i];
-}
+// Activation chunks (16 bytes each) a thread stages, and the LDS floats of the padded
+// x image: XPT * WG chunk slots in blocks of 8 (36 floats per block).
+constexpr int xpt_of(int m, int cpl) { return (m * cpl * 512 + WG - 1) / WG; }
+constexpr int x_floats(int m, int cpl) { return xpt_of(m, cpl) * WG / 8 * XS; }
 
 // base + byte `B` of v, in one v_add_u32 with an SDWA byte select on the second source.
 template <int B>
@@ -94,28 +85,57 @@ QMV_DEV float chunk_dot(uint4 q, uint32_t tb, const float *xb) {
     return a + b;
 }
 
+// One row's index chunks (lane l: chunks l, l+64, ...) and its codebooks (16 B pieces
+// lane, lane+64, ...; two pieces per 128-weight group), loaded with clamped indices so
+// that no branch sits around a load (a branch would make the compiler wait for the load
+// on the spot).
 template <int CPL>
-struct RowCodes {
+struct RowData {
     uint4 q[CPL];
+    uint4 t[(CPL + 1) / 2];
 };
 
+// Codebooks first: the barrier before the dots waits for them (vector loads complete in
+// issue order), while the index chunks may still be arriving.
 template <int CPL>
-QMV_DEV void load_row(RowCodes<CPL> &r, const uint8_t *idx_row, int nchunk, int lane, bool valid) {
+QMV_DEV void load_tables(RowData<CPL> &r, const uint16_t *cb_row, int nchunk, int lane) {
+    const int npieces = nchunk >> 1;  // 16-byte codebook pieces of the row
 #pragma unroll
-    for (int u = 0; u < CPL; u++) {
-        const int c = lane + 64 * u;
-        r.q[u] = (valid && c < nchunk) ? ld_stream16(idx_row + 16 * (int64_t)c) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < (CPL + 1) / 2; u++) {
+        const int i = lane + 64 * u;
+        r.t[u] = ld_stream16(cb_row + 8 * (int64_t)(i < npieces ? i : npieces - 1));
     }
 }
 
 template <int CPL>
-QMV_DEV float row_dot(const RowCodes<CPL> &r, const uint16_t *tab, const float *sx, int nchunk, int lane) {
+QMV_DEV void load_codes(RowData<CPL> &r, const uint8_t *idx_row, int nchunk, int lane) {
+#pragma unroll
+    for (int u = 0; u < CPL; u++) {
+        const int c = lane + 64 * u;
+        r.q[u] = ld_stream16(idx_row + 16 * (int64_t)(c < nchunk ? c : nchunk - 1));
+    }
+}
+
+template <int CPL>
+QMV_DEV void store_tables(const RowData<CPL> &r, uint16_t *tab, int nchunk, int lane) {
+    const int npieces = nchunk >> 1;
+#pragma unroll
+    for (int u = 0; u < (CPL + 1) / 2; u++) {
+        const int i = lane + 64 * u;
+        // a lane past the end rewrites the last piece with the same bytes
+        ((uint4 *)tab)[i < npieces ? i : npieces - 1] = r.t[u];
+    }
+}
+
+template <int CPL>
+QMV_DEV float row_dot(const RowData<CPL> &r, const uint16_t *tab, const float *sx, int nchunk, int lane) {
     float acc = 0.f;
 #pragma unroll
     for (int u = 0; u < CPL; u++) {
         const int c = lane + 64 * u;
-        if (c < nchunk)
-            acc += chunk_dot(r.q[u], (uint32_t)(uintptr_t)(tab + (c >> 2) * 16), sx + c * XS);
+        const int cc = c < nchunk ? c : nchunk - 1;
+        const float v = acc + chunk_dot(r.q[u], (uint32_t)(uintptr_t)(tab + (cc >> 2) * 16), sx + cc * XS);
+        acc = c < nchunk ? v : acc;
     }
     return acc;
 }
@@ -123,50 +143,57 @@ QMV_DEV float row_dot(const RowCodes<CPL> &r, const uint16_t *tab, const float *
 // GEMV job: grid.x over row blocks; one row per wave.
 // GATEUP job: grid.x over row blocks, grid.y = expert slot j; x is the token's activations.
 // DOWN job: grid.x over row blocks, grid.y = expert slot j; x is h (fp32) [n_ids][k].
+// Order of work: expert id and activation loads, then (once the id is known) every code
+// and codebook load of the wave's row(s), then the LDS writes, one barrier, the dots.
+// Rows past n and invalid expert ids read clamped (in-bounds) addresses; their outputs are
+// not written (rows) or are NaN (ids).
 template <int JOB, int M, int CPL, int XT>
 __global__ void __launch_bounds__(WG) cb4_kernel(Cb4Args a) {
-    extern __shared__ float lds[];
+    extern __shared__ float4 lds4[];
+    constexpr int XPT = xpt_of(M, CPL);
+    constexpr int XT_ = JOB == JOB_DOWN ? 0 : XT;
     const int k = a.k, ngroups = k >> 7, nchunk = k >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x * WAVES + wave;
+    const int rowc = row < a.n ? row : a.n - 1;
     constexpr int NT = JOB == JOB_GATEUP ? 2 : 1;  // tables (rows) per wave
-    float *sx = lds;
-    uint16_t *tabs = (uint16_t *)(lds + M * (k >> 5) * XS);
+    float *sx = (float *)lds4;
+    uint16_t *tabs = (uint16_t *)(sx + x_floats(M, CPL));
     uint16_t *tab0 = tabs + wave * NT * ngroups * 16;
     uint16_t *tab1 = tab0 + ngroups * 16;
 
-    int64_t e = 0;
-    bool ok_expert = true;
-    const void *x = a.x;
-    if (JOB != JOB_GEMV) {
-        const int32_t id = a.ids[blockIdx.y];
-        ok_expert = id >= 0 && id < a.n_experts;
-        e = ok_expert ? id : 0;
-        if (JOB == JOB_DOWN) x = (const float *)a.x + (int64_t)blockIdx.y * k;
+    int32_t id = 0;
+    if (JOB != JOB_GEMV) id = a.ids[blockIdx.y];
+    const void *x = JOB == JOB_DOWN ? (const void *)((const float *)a.x + (int64_t)blockIdx.y * k) : a.x;
+    const int total = M * (k >> 2);
+    float4 xv[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; j++) {
+        const int c = threadIdx.x + j * WG;
+        xv[j] = ld_act4<XT_>(x, (int64_t)(c < total ? c : total - 1) * 4);
     }
-    const bool valid = ok_expert && row < a.n;
 
-    // activations first (vector loads return in order), then codes, then tables
-    stage_x<M, (JOB == JOB_DOWN ? 0 : XT)>(x, k, sx);
-    RowCodes<CPL> r0, r1;
-    const uint8_t *i0 = a.idx0 + e * a.idx_stride + (int64_t)row * (k >> 1);
-    load_row<CPL>(r0, i0, nchunk, lane, valid);
-    if (JOB == JOB_GATEUP) {
-        const uint8_t *i1 = a.idx1 + e * a.idx_stride + (int64_t)row * (k >> 1);
-        load_row<CPL>(r1, i1, nchunk, lane, valid);
-    }
-    if (valid) {
-        stage_tables(a.cb0 + e * a.cb_stride + (int64_t)row * ngroups * 16, ngroups, tab0, lane);
-        if (JOB == JOB_GATEUP)
-            stage_tables(a.cb1 + e * a.cb_stride + (int64_t)row * ngroups * 16, ngroups, tab1, lane);
-    }
+    const bool ok_expert = JOB == JOB_GEMV || (id >= 0 && id < a.n_experts);
+    const int64_t e = ok_expert ? id : 0;
+    RowData<CPL> r0, r1;
+    load_tables<CPL>(r0, a.cb0 + e * a.cb_stride + (int64_t)rowc * ngroups * 16, nchunk, lane);
+    if (JOB == JOB_GATEUP) load_tables<CPL>(r1, a.cb1 + e * a.cb_stride + (int64_t)rowc * ngroups * 16, nchunk, lane);
+    load_codes<CPL>(r0, a.idx0 + e * a.idx_stride + (int64_t)rowc * (k >> 1), nchunk, lane);
+    if (JOB == JOB_GATEUP) load_codes<CPL>(r1, a.idx1 + e * a.idx_stride + (int64_t)rowc * (k >> 1), nchunk, lane);
+    __builtin_amdgcn_sched_barrier(0);  // every load is issued before the LDS writes wait
+
+    float4 *dst = lds4 + (threadIdx.x >> 3) * (XS / 4) + (threadIdx.x & 7);
+#pragma unroll
+    for (int j = 0; j < XPT; j++) dst[j * (WG / 8) * (XS / 4)] = xv[j];
+    store_tables<CPL>(r0, tab0, nchunk, lane);
+    if (JOB == JOB_GATEUP) store_tables<CPL>(r1, tab1, nchunk, lane);
     __syncthreads();
 
     if (JOB == JOB_GEMV) {
 #pragma unroll
         for (int m = 0; m < M; m++) {
             const float t = wave_sum(row_dot<CPL>(r0, tab0, sx + m * nchunk * XS, nchunk, lane));
-            if (lane == 0 && valid) a.y[(int64_t)m * a.n + row] = t;
+            if (lane == 0 && row < a.n) a.y[(int64_t)m * a.n + row] = t;
         }
         return;
     }
@@ -184,7 +211,7 @@ __global__ void __launch_bounds__(WG) cb4_kernel(Cb4Args a) {
 template <int JOB, int M, int CPL, int XT>
 void launch(const Cb4Args &a, int slots, hipStream_t s) {
     constexpr int NT = JOB == JOB_GATEUP ? 2 : 1;
-    const size_t lds = (size_t)M * (a.k >> 5) * XS * 4 + (size_t)WAVES * NT * (a.k >> 7) * 32;
+    const size_t lds = (size_t)x_floats(M, CPL) * 4 + (size_t)WAVES * NT * (a.k >> 7) * 32;
     hipLaunchKernelGGL((cb4_kernel<JOB, M, CPL, XT>), dim3((a.n + WAVES - 1) / WAVES, slots), dim3(WG), lds, s, a);
 }
 
@@ -218,7 +245,10 @@ bool dispatch_m(int m, int cpl, const Cb4Args &a, hipStream_t s) {
     return false;
 }
 
-size_t lds_need(int m, int64_t k, int nt) { return (size_t)m * (k >> 5) * XS * 4 + (size_t)WAVES * nt * (k >> 7) * 32; }
+size_t lds_need(int m, int64_t k, int nt) {
+    const int cpl = (int)((k / 32 + 63) / 64);
+    return (size_t)((m * cpl * 512 + WG - 1) / WG) * WG / 8 * XS * 4 + (size_t)WAVES * nt * (k >> 7) * 32;
+}
 
 }  // namespace
 

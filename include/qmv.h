@@ -174,7 +174,8 @@ int qmm_partials(const qmv_weights *w, int32_t m, const int8_t *xq, int32_t *i32
  *              (n = d_model, k = d_ff).  Expert e's planes follow expert 0's
  *              contiguously: plane(e) = plane(0) + e * qmv_plane_bytes(...).
  *   n_experts: experts stored; ids: device int32 [n_ids]; ids outside
- *              [0, n_experts) produce NaN rows (no weight is read for them).
+ *              [0, n_experts) produce NaN rows (their loads are redirected to
+ *              expert 0, which stays in bounds; none of those bytes is used).
  *   x : device [d_model] of dtype xt; h: device fp32 [n_ids][d_ff] (written);
  *   y : device fp32 [n_ids][d_model].  1 <= n_ids <= 64.
  */
