@@ -16,14 +16,19 @@
 //     [-3968, 4096] and is split exactly as w' = 64 h + l with l = w' & 63 in [0, 63]
 //     and h = w' >> 6 in [-62, 64], two int8 planes.  Two MFMAs per 32-block give
 //     C_H and C_L, and I32 = 64 C_H + C_L (one shift-add) is exact in int32.
-//   * K advances in steps of 128 (half a super-block) through double-buffered LDS:
-//     the raw codes and activation bytes of step s+1 are fetched into registers while
-//     step s runs on the matrix cores, then expanded (6-bit code -> w' -> h, l on packed
-//     16-bit lanes) into the other buffer; one barrier per step.  The expansion of a
-//     64-row tile is reused by the tile's 128 token columns.
+//   * K advances in steps of 64 (two activation blocks) through double-buffered LDS:
+//     the raw codes and activation bytes of a later step are fetched into registers while
+//     this step runs on the matrix cores, then expanded (6-bit code -> w' = sc (q - 32)
+//     by one packed 16-bit multiply-add -> h, l bytes) into the other buffer; one barrier
+//     per step.  Loads are unconditional (row and token indices clamped), so no branch
+//     makes the compiler wait for them early.
 //   * fp32 partial sums per super-block are scaled by d once.
-// Tile: 256 threads = 4 waves in a 2 (n) x 2 (m) grid; wave tile 32 n x 64 m = two
-// 32x32 MFMA tiles sharing the A fragments.
+// Tiles: 256 threads = 4 waves; 128 token columns per workgroup.  Wide matrices use
+// 64-row tiles (waves 2 (n) x 2 (m), wave tile 32 n x 64 m = two 32x32 MFMA tiles sharing
+// the A fragments; three workgroups per CU); narrow ones, which would leave CUs idle with
+// 64-row tiles, use 32-row tiles (waves 1 x 4, wave tile 32 x 32) with loads two steps
+// ahead.  The per-block epilogue (shift-add, convert, FMA on every 32x32 value) is the
+// VALU cost that bounds this kernel, not the matrix cores.
 //
 // MFMA operand layout used (32x32x32 i8): lane l supplies row (or column) l % 32 and
 // the 16 consecutive k of group l / 32; the accumulator's value v of lane l is
@@ -39,154 +44,203 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int TB = 256;
-constexpr int BN = 64;        // weight rows per workgroup tile
+constexpr int TB = 256;       // 4 waves
 constexpr int BM = 128;       // token columns per workgroup tile
-constexpr int RS = 128 + 16;  // LDS row stride (bytes) of the staged int8 planes (one K step)
+constexpr int KS = 64;        // k per step: two 32-activation blocks
+constexpr int RS = KS + 16;   // LDS row stride (bytes) of the staged int8 planes
 
-// (q0, q1, q2, q3) bytes of Q -> 4 exact w' = sc * (q - 32), split into h bytes and l bytes.
-QMV_DEV void expand4(uint32_t Q, uint32_t sc2, uint32_t &hb, uint32_t &lb) {
-    const uint32_t lo = __builtin_amdgcn_perm(0u, Q, 0x0C010C00u);  // (q0, q1) as 16-bit lanes
-    const uint32_t hi = __builtin_amdgcn_perm(0u, Q, 0x0C030C02u);  // (q2, q3)
-    const s16x2 c32 = {32, 32};
-    const s16x2 wlo = (__builtin_bit_cast(s16x2, lo) - c32) * __builtin_bit_cast(s16x2, sc2);
-    const s16x2 whi = (__builtin_bit_cast(s16x2, hi) - c32) * __builtin_bit_cast(s16x2, sc2);
-    const s16x2 hlo = wlo >> (s16x2){6, 6}, hhi = whi >> (s16x2){6, 6};
-    const uint32_t llo = __builtin_bit_cast(uint32_t, wlo) & 0x003F003Fu;
-    const uint32_t lhi = __builtin_bit_cast(uint32_t, whi) & 0x003F003Fu;
-    hb = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hhi), __builtin_bit_cast(uint32_t, hlo), 0x06040200u);
-    lb = __builtin_amdgcn_perm(lhi, llo, 0x06040200u);
-}
-
-// Raw inputs of one K step (128 weights per row) held in registers between the
-// prefetch and the expansion: this thread's 32 weights of one row and 64 activation bytes.
-struct StepRaw {
-    uint4 ql, qh, b[4];
-    uint32_t sca, scb;  // the two sub-scale bytes of this thread's runs, as loaded
-    uint32_t d;         // fp16 bits of this thread's row's super-block scale, as loaded
-    float4 xs4[2];  // activation scales of the step's four blocks, for the lane's two columns
+// Tile geometry: WN wave rows of 32 weight rows each, 4 / WN wave columns; a wave covers
+// 32 rows x TPW 32-token MFMA tiles (sharing its A fragments).
+template <int WN>
+struct Geo {
+    static constexpr int BN = 32 * WN;                 // weight rows per workgroup
+    static constexpr int WMC = 4 / WN;                 // wave columns
+    static constexpr int TPW = BM / (32 * WMC);        // token tiles per wave
+    static constexpr int TPR = TB / BN;                // expanding threads per row
+    static constexpr int W = KS / TPR;                 // weights each thread expands per step
+    static constexpr int LDS = 2 * (2 * BN + BM) * RS; // two buffers of sH, sL, sB
 };
 
-template <bool PARTIALS>
-__global__ void __launch_bounds__(TB, 2) gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh,
+// Four 6-bit codes (bytes of q) of one sub-block -> w' = sc * (q - 32) in [-4096, 4064],
+// split exactly as w' = 64 h + l (h = w' >> 6 in [-64, 63], l = w' & 63), packed as four h
+// bytes and four l bytes.  (w' << 2) keeps h in the high byte of each 16-bit lane.
+QMV_DEV void expand4(uint32_t q, uint32_t sc2, uint32_t c2, uint32_t &hb, uint32_t &lb) {
+    const uint32_t q01 = __builtin_amdgcn_perm(0u, q, 0x0C010C00u);  // (q0, q1) as 16-bit lanes
+    const uint32_t q23 = __builtin_amdgcn_perm(0u, q, 0x0C030C02u);
+    const s16x2 w01 = __builtin_bit_cast(s16x2, q01) * __builtin_bit_cast(s16x2, sc2) + __builtin_bit_cast(s16x2, c2);
+    const s16x2 w23 = __builtin_bit_cast(s16x2, q23) * __builtin_bit_cast(s16x2, sc2) + __builtin_bit_cast(s16x2, c2);
+    const uint32_t t01 = __builtin_bit_cast(uint32_t, w01 << (s16x2){2, 2});
+    const uint32_t t23 = __builtin_bit_cast(uint32_t, w23 << (s16x2){2, 2});
+    hb = __builtin_amdgcn_perm(t23, t01, 0x07050301u);
+    lb = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, w23), __builtin_bit_cast(uint32_t, w01), 0x06040200u) &
+         0x3F3F3F3Fu;
+}
+
+template <int NW> struct RawA;
+template <> struct RawA<16> { uint4 ql, qh; };
+template <> struct RawA<8> { uint2 ql, qh; };
+
+// Step st = 4 s + j covers weights [64 j, 64 j + 64) of super-block s: half h = j >> 1,
+// runs t = 2 (j & 1) + {0, 1}, each run 32 consecutive l.  Weight (h, t, l) has its low
+// nibble in ql[64 h + 32 (t & 1) + l] (bits 4 (t >> 1)..) and its high bits in
+// qh[32 h + l] (bits 2 t..); ql/qh bytes of a half serve both of its steps.
+template <int WN, bool PARTIALS, int PD>
+__global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh,
                                                          const int8_t *__restrict__ scp, const uint16_t *__restrict__ dp,
                                                          const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                          float *__restrict__ y, int32_t *__restrict__ part,
                                                          int M, int N, int K) {
-    __shared__ __attribute__((aligned(16))) uint8_t sH[2][BN * RS];
-    __shared__ __attribute__((aligned(16))) uint8_t sL[2][BN * RS];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BM * RS];
-    __shared__ __attribute__((aligned(16))) float sD[2][BN];
+    using G = Geo<WN>;
+    constexpr int BN = G::BN, TPW = G::TPW, NWT = G::W;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ float sD[2][BN];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % WN, wm = wave / WN;
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-    const int nsteps = K >> 7, nblk = K >> 5;
+    const int nsteps = K / KS, nblk = K >> 5;
     const int li = lane & 31, lg = lane >> 5;
 
-    // expansion role: row er of the tile, lane offset eo (0/16), run pair tp ({0,2} or {1,3})
-    const int er = tid >> 2, eo = tid & 1, tp = (tid >> 1) & 1;
-    const int erow = n0 + er;
-    const bool evalid = erow < N;
-
-    auto fetch = [&](int st, StepRaw &r) {
-        const int sb = st >> 1, h = st & 1;
-        if (evalid) {
-            r.ql = ld_stream16(ql + (int64_t)erow * (K >> 1) + sb * 128 + 64 * h + 32 * tp + 16 * eo);
-            r.qh = ld_stream16(qh + (int64_t)erow * (K >> 2) + sb * 64 + 32 * h + 16 * eo);
-            // raw bytes only: any arithmetic on them here would make the compiler wait
-            // for these loads now instead of at the expansion (loads return in order)
-            const uint8_t *scr = (const uint8_t *)scp + (int64_t)erow * (K >> 4) + sb * 16 + 8 * h + 2 * tp + eo;
-            r.sca = scr[0];
-            r.scb = scr[4];
-            r.d = dp[(int64_t)erow * (K >> 8) + sb];
-        } else {
-            r.ql = r.qh = make_uint4(0, 0, 0, 0);
-            r.sca = r.scb = 0;
-            r.d = 0;
-        }
+    // expansion role: row er, run tt of the step, first l of this thread's NWT weights
+    const int er = tid / G::TPR, ep = tid % G::TPR;
+    const int tt = (ep * NWT) >> 5, l0 = (ep * NWT) & 31;
+    const int erow = min(n0 + er, N - 1);
+    const uint8_t *qlr = ql + (int64_t)erow * (K >> 1) + 32 * tt + l0;
+    const uint8_t *qhr = qh + (int64_t)erow * (K >> 2) + l0;
+    const int8_t *scr = scp + (int64_t)erow * (K >> 4) + 2 * tt + (l0 >> 4);
+    const uint16_t *dr = dp + (int64_t)erow * (K >> 8);
+    // activation staging role: token bt, bytes [32 bo, 32 bo + 32) of the step
+    const int bt = tid >> 1, bo = tid & 1;
+    const int8_t *xr = xq + (int64_t)min(m0 + bt, M - 1) * K + 32 * bo;
+    // epilogue: the lane's token of each tile
+    int tok[TPW];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int c = tid + i * TB, rr = c >> 3, o = (c & 7) * 16;
-            const int m = m0 + rr;
-            r.b[i] = m < M ? *(const uint4 *)(xq + (int64_t)m * K + st * 128 + o) : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < TPW; t++) tok[t] = m0 + 32 * (wm * TPW + t) + li;
+
+    uint8_t *const sbase = smem;
+    auto sH = [&](int b) { return sbase + b * (2 * BN + BM) * RS; };
+    auto sL = [&](int b) { return sbase + b * (2 * BN + BM) * RS + BN * RS; };
+    auto sB = [&](int b) { return sbase + b * (2 * BN + BM) * RS + 2 * BN * RS; };
+
+    // raw inputs of one step, held in registers from the prefetch to the expansion; with a
+    // prefetch distance of 2 there are two sets, used by even and odd steps
+    struct Raw {
+        RawA<NWT> ra;
+        int scb;
+        uint32_t dbits;
+        uint4 rb0, rb1;
+        float2 xsv[TPW];
+    };
+
+    auto fetch = [&](int st, Raw &r) {
+        auto &ra = r.ra;
+        auto &scb = r.scb;
+        auto &dbits = r.dbits;
+        auto &rb0 = r.rb0;
+        auto &rb1 = r.rb1;
+        auto &xsv = r.xsv;
+        const int s = st >> 2, j = st & 3, h = j >> 1;
+        if ((j & 1) == 0) {  // a new half: its ql/qh bytes
+            if constexpr (NWT == 16) {
+                ra.ql = ld_stream16(qlr + 128 * s + 64 * h);
+                ra.qh = ld_stream16(qhr + 64 * s + 32 * h);
+            } else {
+                ra.ql = *(const uint2 *)(qlr + 128 * s + 64 * h);
+                ra.qh = *(const uint2 *)(qhr + 64 * s + 32 * h);
+            }
         }
+        scb = scr[16 * s + 8 * h + 4 * (j & 1)];
+        if (j == 0) dbits = dr[s];
+        rb0 = *(const uint4 *)(xr + st * KS);
+        rb1 = *(const uint4 *)(xr + st * KS + 16);
         if (!PARTIALS) {
 #pragma unroll
-            for (int t = 0; t < 2; t++) {
-                const int m = m0 + 64 * wm + 32 * t + li;
-                const float4 a = *(const float4 *)(xs + (int64_t)min(m, M - 1) * nblk + st * 4);
-                r.xs4[t] = m < M ? a : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            for (int t = 0; t < TPW; t++)
+                xsv[t] = *(const float2 *)(xs + (int64_t)min(tok[t], M - 1) * nblk + 2 * st);
         }
     };
 
-    auto store = [&](int st, const StepRaw &r, int buf) {
-        const uint32_t a4[4] = {r.ql.x, r.ql.y, r.ql.z, r.ql.w};
-        const uint32_t h4[4] = {r.qh.x, r.qh.y, r.qh.z, r.qh.w};
-#pragma unroll
-        for (int half = 0; half < 2; half++) {  // run t = tp (low nibbles), t = tp + 2 (high nibbles)
-            const int scv = (int)(int8_t)(half == 0 ? r.sca : r.scb);
-            const uint32_t sc2 = ((uint32_t)scv & 0xFFFFu) | ((uint32_t)scv << 16);
-            uint32_t hv[4], lv[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const uint32_t qhs = h4[i] >> (2 * tp);
-                const uint32_t q = half == 0 ? ((a4[i] & 0x0F0F0F0Fu) | ((qhs << 4) & 0x30303030u))
-                                             : (((a4[i] >> 4) & 0x0F0F0F0Fu) | (qhs & 0x30303030u));
-                expand4(q, sc2, hv[i], lv[i]);
-            }
-            const int kofs = 32 * (tp + 2 * half) + 16 * eo;
-            *(uint4 *)(&sH[buf][er * RS + kofs]) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-            *(uint4 *)(&sL[buf][er * RS + kofs]) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+    auto store = [&](int st, int buf, const Raw &r) {
+        const auto &ra = r.ra;
+        const int scb = r.scb;
+        const uint32_t dbits = r.dbits;
+        const uint4 rb0 = r.rb0, rb1 = r.rb1;
+        const int j = st & 3;
+        const int sh = 2 * (2 * (j & 1) + tt);  // qh bit offset of run t
+        const uint32_t sc16 = (uint32_t)scb & 0xFFFFu;
+        const uint32_t sc2 = sc16 | (sc16 << 16);
+        const uint32_t c16 = (uint32_t)(-32 * scb) & 0xFFFFu;
+        const uint32_t c2 = c16 | (c16 << 16);
+        constexpr int ND = NWT / 4;
+        uint32_t qlw[ND], qhw[ND], hv[ND], lv[ND];
+        if constexpr (NWT == 16) {
+            qlw[0] = ra.ql.x; qlw[1] = ra.ql.y; qlw[2] = ra.ql.z; qlw[3] = ra.ql.w;
+            qhw[0] = ra.qh.x; qhw[1] = ra.qh.y; qhw[2] = ra.qh.z; qhw[3] = ra.qh.w;
+        } else {
+            qlw[0] = ra.ql.x; qlw[1] = ra.ql.y;
+            qhw[0] = ra.qh.x; qhw[1] = ra.qh.y;
         }
-        if ((st & 1) == 0 && (tid & 3) == 0) sD[(st >> 1) & 1][er] = h2f((uint16_t)r.d);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int c = tid + i * TB, rr = c >> 3, o = (c & 7) * 16;
-            *(uint4 *)(&sB[buf][rr * RS + o]) = r.b[i];
+        for (int i = 0; i < ND; i++) {
+            const uint32_t nib = ((j & 1) ? qlw[i] >> 4 : qlw[i]) & 0x0F0F0F0Fu;
+            const uint32_t q = nib | (((qhw[i] >> sh) & 0x03030303u) << 4);
+            expand4(q, sc2, c2, hv[i], lv[i]);
         }
+        uint8_t *dh = sH(buf) + er * RS + 32 * tt + l0;
+        uint8_t *dl = sL(buf) + er * RS + 32 * tt + l0;
+        if constexpr (NWT == 16) {
+            *(uint4 *)dh = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+            *(uint4 *)dl = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+        } else {
+            *(uint2 *)dh = make_uint2(hv[0], hv[1]);
+            *(uint2 *)dl = make_uint2(lv[0], lv[1]);
+        }
+        if (j == 0 && ep == 0) sD[(st >> 2) & 1][er] = h2f((uint16_t)dbits);
+        uint8_t *db = sB(buf) + bt * RS + 32 * bo;
+        *(uint4 *)db = rb0;
+        *(uint4 *)(db + 16) = rb1;
     };
 
-    float accf[2][16], Y[2][16];
+    float accf[TPW][16], Y[TPW][16];
 #pragma unroll
-    for (int t = 0; t < 2; t++)
+    for (int t = 0; t < TPW; t++)
 #pragma unroll
         for (int v = 0; v < 16; v++) { Y[t][v] = 0.f; accf[t][v] = 0.f; }
 
-    StepRaw raw;
-    fetch(0, raw);
-    store(0, raw, 0);
-    __syncthreads();
-
-    for (int st = 0; st < nsteps; st++) {
+    // One step: compute st from LDS buffer st & 1 while the loads of a later step are in
+    // flight, then expand step st + 1 into the other buffer.  With PD = 1 the loads of
+    // st + 1 are issued at the top of st (one set of registers); with PD = 2 the loads of
+    // st + 2 go into the set step st has just released (two sets, alternating by parity,
+    // so the set is chosen at compile time).  The ql/qh bytes of a half are loaded by its
+    // first step; its second step reuses them.
+    auto step = [&](int st, Raw &cur, Raw &nxt) {
         const int buf = st & 1;
-        // this step's activation scales were fetched with its codes (loads return in
-        // order, so nothing issued after the prefetch below may be waited on here)
-        float xsv[2][4];
+        float xsc[TPW][2];
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-            xsv[t][0] = raw.xs4[t].x;
-            xsv[t][1] = raw.xs4[t].y;
-            xsv[t][2] = raw.xs4[t].z;
-            xsv[t][3] = raw.xs4[t].w;
+        for (int t = 0; t < TPW; t++) { xsc[t][0] = cur.xsv[t].x; xsc[t][1] = cur.xsv[t].y; }
+        if (PD == 1) {
+            if (st + 1 < nsteps) fetch(st + 1, cur);
+        } else {
+            if (st + 2 < nsteps) {
+                if ((st & 1) == 1) cur.ra = nxt.ra;  // st + 2 odd: same half as st + 1
+                fetch(st + 2, cur);
+            }
         }
-        if (st + 1 < nsteps) fetch(st + 1, raw);  // in flight during this step's MFMAs
 
 #pragma unroll
-        for (int cb = 0; cb < 4; cb++) {
+        for (int cb = 0; cb < 2; cb++) {
             const int ko = cb * 32 + 16 * lg;
-            const v4i aH = __builtin_bit_cast(v4i, *(const uint4 *)(&sH[buf][(32 * wn + li) * RS + ko]));
-            const v4i aL = __builtin_bit_cast(v4i, *(const uint4 *)(&sL[buf][(32 * wn + li) * RS + ko]));
+            const v4i aH = __builtin_bit_cast(v4i, *(const uint4 *)(sH(buf) + (32 * wn + li) * RS + ko));
+            const v4i aL = __builtin_bit_cast(v4i, *(const uint4 *)(sL(buf) + (32 * wn + li) * RS + ko));
 #pragma unroll
-            for (int t = 0; t < 2; t++) {
-                const int mc = 64 * wm + 32 * t + li;  // tile-local token column of this lane
-                const v4i b = __builtin_bit_cast(v4i, *(const uint4 *)(&sB[buf][mc * RS + ko]));
+            for (int t = 0; t < TPW; t++) {
+                const int mc = 32 * (wm * TPW + t) + li;  // tile-local token column of this lane
+                const v4i b = __builtin_bit_cast(v4i, *(const uint4 *)(sB(buf) + mc * RS + ko));
                 const v16i z = {};
                 const v16i cH = __builtin_amdgcn_mfma_i32_32x32x32_i8(aH, b, z, 0, 0, 0);
                 const v16i cL = __builtin_amdgcn_mfma_i32_32x32x32_i8(aL, b, z, 0, 0, 0);
                 if (PARTIALS) {
-                    const int m = m0 + mc, c = st * 4 + cb;
+                    const int m = tok[t], c = st * 2 + cb;
 #pragma unroll
                     for (int v = 0; v < 16; v++) {
                         const int n = n0 + 32 * wn + 8 * (v >> 2) + 4 * lg + (v & 3);
@@ -195,17 +249,18 @@ __global__ void __launch_bounds__(TB, 2) gemm_q6k_kernel(const uint8_t *__restri
                 } else {
 #pragma unroll
                     for (int v = 0; v < 16; v++)
-                        accf[t][v] = fmaf((float)((cH[v] << 6) + cL[v]), xsv[t][cb], accf[t][v]);
+                        accf[t][v] = fmaf((float)((cH[v] << 6) + cL[v]), xsc[t][cb], accf[t][v]);
                 }
             }
         }
-        if (!PARTIALS && (st & 1)) {  // end of a super-block: apply d once
+        if (!PARTIALS && (st & 3) == 3) {  // end of a super-block: apply d once
+            const float *dcur = sD[(st >> 2) & 1];
 #pragma unroll
             for (int g = 0; g < 4; g++) {
-                const float4 dv = *(const float4 *)(&sD[(st >> 1) & 1][32 * wn + 8 * g + 4 * lg]);
+                const float4 dv = *(const float4 *)(&dcur[32 * wn + 8 * g + 4 * lg]);
                 const float d4[4] = {dv.x, dv.y, dv.z, dv.w};
 #pragma unroll
-                for (int t = 0; t < 2; t++)
+                for (int t = 0; t < TPW; t++)
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         Y[t][4 * g + e] = fmaf(d4[e], accf[t][4 * g + e], Y[t][4 * g + e]);
@@ -213,13 +268,30 @@ __global__ void __launch_bounds__(TB, 2) gemm_q6k_kernel(const uint8_t *__restri
                     }
             }
         }
-        if (st + 1 < nsteps) store(st + 1, raw, buf ^ 1);
+        if (st + 1 < nsteps) store(st + 1, buf ^ 1, PD == 1 ? cur : nxt);
         __syncthreads();
+    };
+
+    Raw R0, R1;
+    fetch(0, R0);
+    if (PD == 2 && nsteps > 1) {
+        fetch(1, R1);
+        R1.ra = R0.ra;  // step 1 is the second step of half 0
+    }
+    store(0, 0, R0);
+    __syncthreads();
+    if (PD == 1) {
+        for (int st = 0; st < nsteps; st++) step(st, R0, R0);
+    } else {
+        for (int st = 0; st < nsteps; st += 2) {  // nsteps is a multiple of 4
+            step(st, R0, R1);
+            step(st + 1, R1, R0);
+        }
     }
     if (PARTIALS) return;
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-        const int m = m0 + 64 * wm + 32 * t + li;
+    for (int t = 0; t < TPW; t++) {
+        const int m = tok[t];
         if (m >= M) continue;
 #pragma unroll
         for (int g = 0; g < 4; g++) {
@@ -236,22 +308,35 @@ __global__ void __launch_bounds__(TB, 2) gemm_q6k_kernel(const uint8_t *__restri
     }
 }
 
+template <int WN, bool PARTIALS, int PD>
+void launch_tiles(const qmv_weights *w, int m, const int8_t *xq, const float *xs, float *y, int32_t *partials,
+                  hipStream_t s) {
+    using G = Geo<WN>;
+    const int64_t n = w->n, k = w->k;
+    const dim3 grid((unsigned)((n + G::BN - 1) / G::BN), (unsigned)((m + BM - 1) / BM));
+    hipLaunchKernelGGL((gemm_q6k_kernel<WN, PARTIALS, PD>), grid, dim3(TB), G::LDS, s, (const uint8_t *)w->codes,
+                       (const uint8_t *)w->codes_hi, (const int8_t *)w->scales, (const uint16_t *)w->super, xq, xs,
+                       y, partials, m, (int)n, (int)k);
+}
+
 }  // namespace
 
 const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *xq, const float *xs, float *y,
                             int32_t *partials, hipStream_t s) {
     const int64_t n = w->n, k = w->k;
     if (n > INT32_MAX || k > INT32_MAX || (int64_t)m * k > INT32_MAX) return nullptr;
-    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
+    // 64-row tiles when they give at least two workgroups per CU, else 32-row tiles
+    const int64_t tiles64 = ((n + 63) / 64) * ((m + BM - 1) / BM);
+    const bool wide = tiles64 >= 2 * (int64_t)device_info().num_cus;
     if (partials) {
-        hipLaunchKernelGGL(gemm_q6k_kernel<true>, grid, dim3(TB), 0, s, (const uint8_t *)w->codes,
-                           (const uint8_t *)w->codes_hi, (const int8_t *)w->scales, (const uint16_t *)w->super, xq,
-                           xs, y, partials, m, (int)n, (int)k);
+        if (wide) launch_tiles<2, true, 1>(w, m, xq, xs, y, partials, s);
+        else launch_tiles<1, true, 1>(w, m, xq, xs, y, partials, s);
         return "gemm.q6k.mfma-i8-32x32x32.hl-split.partials";
     }
-    hipLaunchKernelGGL(gemm_q6k_kernel<false>, grid, dim3(TB), 0, s, (const uint8_t *)w->codes,
-                       (const uint8_t *)w->codes_hi, (const int8_t *)w->scales, (const uint16_t *)w->super, xq, xs,
-                       y, partials, m, (int)n, (int)k);
+    // 64-row tiles keep the loads of the next step in flight (their register budget allows
+    // three workgroups per CU); 32-row tiles have registers for two steps ahead
+    if (wide) launch_tiles<2, false, 1>(w, m, xq, xs, y, partials, s);
+    else launch_tiles<1, false, 2>(w, m, xq, xs, y, partials, s);
     return "gemm.q6k.mfma-i8-32x32x32.hl-split";
 }
 
