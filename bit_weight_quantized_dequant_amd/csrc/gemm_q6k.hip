@@ -15,7 +15,8 @@
 //   * The sub-scale is folded into the weights: w' = sc * (q - 32) lies in
 //     [-3968, 4096] and is split exactly as w' = 64 h + l with l = w' & 63 in [0, 63]
 //     and h = w' >> 6 in [-62, 64], two int8 planes.  Two MFMAs per 32-block give
-//     C_H and C_L, and I32 = 64 C_H + C_L (one shift-add) is exact in int32.
+//     I32 = 64 C_H + C_L exactly in int32: the first gives C_H, which is shifted by 6 and
+//     handed to the second as its accumulator input.
 //   * K advances in steps of 64 (two activation blocks) through double-buffered LDS:
 //     the raw codes and activation bytes of a later step are fetched into registers while
 //     this step runs on the matrix cores, then expanded (6-bit code -> w' = sc (q - 32)
@@ -236,20 +237,21 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
             for (int t = 0; t < TPW; t++) {
                 const int mc = 32 * (wm * TPW + t) + li;  // tile-local token column of this lane
                 const v4i b = __builtin_bit_cast(v4i, *(const uint4 *)(sB(buf) + mc * RS + ko));
+                // I32 = 64 C_H + C_L: C_H is shifted (one VOP2 shift per value) and handed to
+                // the second MFMA as its accumulator input, which adds C_L exactly
                 const v16i z = {};
                 const v16i cH = __builtin_amdgcn_mfma_i32_32x32x32_i8(aH, b, z, 0, 0, 0);
-                const v16i cL = __builtin_amdgcn_mfma_i32_32x32x32_i8(aL, b, z, 0, 0, 0);
+                const v16i i32 = __builtin_amdgcn_mfma_i32_32x32x32_i8(aL, b, cH << 6, 0, 0, 0);
                 if (PARTIALS) {
                     const int m = tok[t], c = st * 2 + cb;
 #pragma unroll
                     for (int v = 0; v < 16; v++) {
                         const int n = n0 + 32 * wn + 8 * (v >> 2) + 4 * lg + (v & 3);
-                        if (m < M && n < N) part[((int64_t)m * N + n) * nblk + c] = (cH[v] << 6) + cL[v];
+                        if (m < M && n < N) part[((int64_t)m * N + n) * nblk + c] = i32[v];
                     }
                 } else {
 #pragma unroll
-                    for (int v = 0; v < 16; v++)
-                        accf[t][v] = fmaf((float)((cH[v] << 6) + cL[v]), xsc[t][cb], accf[t][v]);
+                    for (int v = 0; v < 16; v++) accf[t][v] = fmaf((float)i32[v], xsc[t][cb], accf[t][v]);
                 }
             }
         }
