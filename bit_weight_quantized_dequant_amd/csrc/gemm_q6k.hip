@@ -13,8 +13,8 @@
 //     (operand B = int8 activations), so each lane's column has one activation scale
 //     xs[m][c] per block: the block epilogue is one convert and one FMA per value.
 //   * The sub-scale is folded into the weights: w' = sc * (q - 32) lies in
-//     [-3968, 4096] and is split exactly as w' = 64 h + l with l = w' & 63 in [0, 63]
-//     and h = w' >> 6 in [-62, 64], two int8 planes.  Two MFMAs per 32-block give
+//     [-4064, 4096] and is split exactly as w' = 64 h + l with l = w' & 63 in [0, 63]
+//     and h = w' >> 6 in [-64, 64], two int8 planes.  Two MFMAs per 32-block give
 //     I32 = 64 C_H + C_L exactly in int32: the first gives C_H, which is shifted by 6 and
 //     handed to the second as its accumulator input.
 //   * K advances in steps of 64 (two activation blocks) through double-buffered LDS:
@@ -62,8 +62,8 @@ struct Geo {
     static constexpr int LDS = 2 * (2 * BN + BM) * RS; // two buffers of sH, sL, sB
 };
 
-// Four 6-bit codes (bytes of q) of one sub-block -> w' = sc * (q - 32) in [-4096, 4064],
-// split exactly as w' = 64 h + l (h = w' >> 6 in [-64, 63], l = w' & 63), packed as four h
+// Four 6-bit codes (bytes of q) of one sub-block -> w' = sc * (q - 32) in [-4064, 4096],
+// split exactly as w' = 64 h + l (h = w' >> 6 in [-64, 64], l = w' & 63), packed as four h
 // bytes and four l bytes.  (w' << 2) keeps h in the high byte of each 16-bit lane.
 QMV_DEV void expand4(uint32_t q, uint32_t sc2, uint32_t c2, uint32_t &hb, uint32_t &lb) {
     const uint32_t q01 = __builtin_amdgcn_perm(0u, q, 0x0C010C00u);  // (q0, q1) as 16-bit lanes
