@@ -35,6 +35,8 @@
 // the 16 consecutive k of group l / 32; the accumulator's value v of lane l is
 // C[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32].  A debug entry point writes the exact
 // I32 partials from this same code path, which pins the layout against the oracle.
+#include <cstring>
+
 #include "device_common.h"
 #include "qmv_internal.h"
 
@@ -337,8 +339,15 @@ const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *xq, const
     }
     // 64-row tiles keep the loads of the next step in flight (their register budget allows
     // three workgroups per CU); 32-row tiles have registers for two steps ahead
-    if (wide) launch_tiles<2, false, 1>(w, m, xq, xs, y, partials, s);
-    else launch_tiles<1, false, 2>(w, m, xq, xs, y, partials, s);
+    const char *fp = forced_path();  // test-only override of the prefetch distance
+    const int pd = strcmp(fp, "gemm.pd1") == 0 ? 1 : strcmp(fp, "gemm.pd2") == 0 ? 2 : (wide ? 1 : 2);
+    if (wide) {
+        if (pd == 1) launch_tiles<2, false, 1>(w, m, xq, xs, y, partials, s);
+        else launch_tiles<2, false, 2>(w, m, xq, xs, y, partials, s);
+    } else {
+        if (pd == 1) launch_tiles<1, false, 1>(w, m, xq, xs, y, partials, s);
+        else launch_tiles<1, false, 2>(w, m, xq, xs, y, partials, s);
+    }
     return "gemm.q6k.mfma-i8-32x32x32.hl-split";
 }
 
