@@ -160,6 +160,88 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
     }
 }
 
+// Batches whose activations do not fit one workgroup's LDS (m * k > 16384) and rows longer
+// than 16384: K is walked in chunks of 2048 (64 blocks, one per lane).  The wave's block of
+// chunk c + 1 is requested before the dots of chunk c, and each chunk's activations are
+// staged per workgroup of 4 rows, with the same branch-free loads (clamped indices) as the
+// one-shot kernel.
+constexpr int KC = 2048;
+
+template <int M, int XT>
+__global__ void __launch_bounds__(256) gemv_q4_0_chunked_kernel(const uint8_t *__restrict__ qs,
+                                                                const uint16_t *__restrict__ dsc,
+                                                                const void *__restrict__ x,
+                                                                float *__restrict__ y, int n, int k) {
+    extern __shared__ float4 sx4[];
+    constexpr int WG = 256, XPT = M * (KC / 4) / WG;
+    const int nblk = k >> 5, nch = (nblk + 63) >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * 4 + wave;
+    const int rowc = row < n ? row : n - 1;
+    const uint4 *qr = (const uint4 *)(qs + (int64_t)rowc * (k >> 1));
+    const uint16_t *dr = dsc + (int64_t)rowc * nblk;
+
+    uint4 qc = ld_stream16(qr + (lane < nblk ? lane : nblk - 1));
+    uint16_t dc = dr[lane < nblk ? lane : nblk - 1];
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; m++) acc[m] = 0.f;
+    for (int c = 0; c < nch; c++) {
+        const int k0 = c * KC;
+        const int kq = min(KC, k - k0) >> 2;  // 16-byte activation chunks of this K chunk, per row
+        float4 xv[XPT];
+#pragma unroll
+        for (int j = 0; j < XPT; j++) {
+            const int cc = threadIdx.x + j * WG, m = cc >> 9, e = cc & 511;
+            xv[j] = ld_act4<XT>(x, (int64_t)m * k + k0 + 4 * (e < kq ? e : kq - 1));
+        }
+        int bn = (c + 1) * 64 + lane;  // next chunk's block (clamped on the last chunk)
+        bn = bn < nblk ? bn : nblk - 1;
+        const uint4 qn = ld_stream16(qr + bn);
+        const uint16_t dn = dr[bn];
+        __builtin_amdgcn_sched_barrier(0);
+        if (c) __syncthreads();  // the previous chunk's activations are consumed
+#pragma unroll
+        for (int j = 0; j < XPT; j++) {
+            const int cc = threadIdx.x + j * WG, m = cc >> 9, e = cc & 511;
+            sx4[(m * 64 + (e >> 3)) * XS4 + (e & 7)] = xv[j];
+        }
+        __syncthreads();
+        const int b = c * 64 + lane;
+        const float d = h2f(dc);
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            float xb[32];
+#pragma unroll
+            for (int i = 0; i < 8; i++) *(float4 *)(xb + 4 * i) = sx4[(m * 64 + lane) * XS4 + i];
+            const float v = fmaf(d, dot_q4_mix(qc, xb), acc[m]);
+            acc[m] = b < nblk ? v : acc[m];
+        }
+        qc = qn;
+        dc = dn;
+    }
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        const float t = wave_sum(acc[m]);
+        if (lane == 0 && row < n) y[(int64_t)m * n + row] = t;
+    }
+}
+
+template <int XT>
+bool launch_chunked(int m, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
+    const int n = (int)w->n, k = (int)w->k;
+    const dim3 grid((n + 3) / 4);
+    const size_t lds = (size_t)m * 64 * XS * sizeof(float);
+#define QMV_Q4C(MM)                                                                                          \
+    case MM:                                                                                                 \
+        hipLaunchKernelGGL((gemv_q4_0_chunked_kernel<MM, XT>), grid, dim3(256), lds, s,                      \
+                           (const uint8_t *)w->codes, (const uint16_t *)w->scales, x, y, n, k);             \
+        return true;
+    switch (m) { QMV_Q4C(1) QMV_Q4C(2) QMV_Q4C(3) QMV_Q4C(4) QMV_Q4C(5) QMV_Q4C(6) QMV_Q4C(7) QMV_Q4C(8) }
+#undef QMV_Q4C
+    return false;
+}
+
 // 256-thread workgroups for short rows (more workgroups, x staged by fewer waves each),
 // 512 for long ones.
 template <int M, int BPL, int XT, bool MIX>
@@ -212,7 +294,12 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
                              hipStream_t s) {
     const int64_t n = w->n, k = w->k, nblk = k / 32;
     const int bpl = (int)((nblk + 63) / 64);
-    if (bpl > 8 || (int64_t)m * k > 16384 || n > INT32_MAX) return nullptr;
+    if (n > INT32_MAX || k > INT32_MAX / 8) return nullptr;
+    if (bpl > 8 || (int64_t)m * k > 16384) {  // activations staged in K chunks
+        if ((int64_t)m * 64 * XS * (int64_t)sizeof(float) > device_info().lds_per_block) return nullptr;
+        const bool ok = xt == QMV_F32 ? launch_chunked<0>(m, w, x, y, s) : launch_chunked<1>(m, w, x, y, s);
+        return ok ? "q4_0.lds-x-chunked.fma-mix" : nullptr;
+    }
     const size_t lds = bpl <= 2 ? lds_bytes(256, m, bpl) : lds_bytes(512, m, bpl);
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
     const bool cvt = strcmp(forced_path(), "q4_0.cvt") == 0 && m == 1 && xt == QMV_F32;

@@ -104,13 +104,32 @@ def test_q4_0_deterministic_and_permutation_equivariant(qmv):
     assert np.array_equal(yp[0], y1[0, perm])
 
 
-def test_q4_0_limit_is_reported(qmv):
+@pytest.mark.parametrize("n,k,m,xt", [(4, 2048 * 9, 1, synth.DT_F32), (33, 2048 * 9 + 96, 1, synth.DT_F32),
+                                      (70, 11008, 2, synth.DT_F32), (70, 11008, 4, synth.DT_BF16),
+                                      (41, 11008, 8, synth.DT_F32), (9, 4096, 8, synth.DT_BF16), (3, 64, 8, synth.DT_F32)])
+def test_q4_0_k_chunked_batches(qmv, n, k, m, xt):
+    # activations beyond one workgroup's LDS (m * k > 16384, or k > 16384) go through the
+    # K-chunked kernel; the ragged last chunk and row tails are included
+    path = "q4_0.lds-x-chunked.fma-mix" if (m * k > 16384 or k > 16384) else "q4_0.lds-x.fma-mix"
+    run_case(qmv, synth.FMT_Q4_0, n, k, m, xt, seed=n + k + m, expect_path=path)
+
+
+def test_q4_0_chunked_unit_vector_returns_column_exactly(qmv):
     import torch
-    W = qweights(synth.FMT_Q4_0, 4, 2048 * 9, synth.gen_weights(synth.FMT_Q4_0, 4, 2048 * 9))
-    x = torch.zeros((1, 2048 * 9), dtype=torch.float32, device="cuda")
-    with pytest.raises(qmv.QmvError) as e:
-        qmv.gemv(W, x)
-    assert e.value.code == -9
+    n, k, m = 37, 11008, 3
+    w = synth.gen_weights(synth.FMT_Q4_0, n, k, seed=15)
+    W = qweights(synth.FMT_Q4_0, n, k, w)
+    dense = oracle.dequant(oracle.Mat(synth.FMT_Q4_0, n, k, w)).astype(np.float32)
+    cols = (0, 2047, 2048, 6000, 11007)
+    e = np.zeros((m, k), dtype=np.float32)
+    for r, j in enumerate(cols[:m]):
+        e[r, j] = 1.0
+    y = qmv.gemv(W, x_to_device(e, synth.DT_F32))
+    torch.cuda.synchronize()
+    assert qmv.last_path() == "q4_0.lds-x-chunked.fma-mix"
+    y = y.cpu().numpy()
+    for r, j in enumerate(cols[:m]):
+        assert np.array_equal(y[r], dense[:, j]), j
 
 
 # ------------------------------------------------------------------ q6_K
