@@ -8,6 +8,7 @@
 
 typedef _Float16 qmv_h2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 128-bit streaming load of read-once weight bytes (nontemporal: do not keep in cache).
 QMV_DEV uint4 ld_stream16(const void *p) {

@@ -245,6 +245,143 @@ bool dispatch_m(int m, int cpl, const Cb4Args &a, hipStream_t s) {
     return false;
 }
 
+// ---- K-chunked GEMV, for batches whose activations exceed one workgroup's LDS and for
+// rows longer than 16384.  K is walked 2048 weights at a time: per step a lane holds one
+// 32-weight index chunk (16 bytes) and four codebook entries (8 bytes; the wave's 64 lanes
+// together hold the step's 16 codebooks), the next step's are loaded while this one is
+// computed (two register sets alternate), and each looked-up weight is used for all M
+// activation rows.  One row per wave.
+constexpr int KCB = 2048;
+constexpr int RXS = 64 * XS;  // floats of one activation row's staged step
+
+struct StepData {
+    uint4 q;  // index chunk
+    uint2 t;  // codebook entries 4 lane .. 4 lane + 3 of the step
+};
+
+// Step c's bytes for this lane, with clamped (in-bounds) indices past the row's end.
+QMV_DEV void load_step(StepData &d, const uint8_t *idx_row, const uint16_t *cb_row, int c, int nchunk, int lane) {
+    const int ci = c * 64 + lane;
+    d.q = ld_stream16(idx_row + 16 * (int64_t)(ci < nchunk ? ci : nchunk - 1));
+    const int ne = (nchunk >> 2) * 16, ei = c * 256 + 4 * lane;
+    const u32x2 v = __builtin_nontemporal_load((const u32x2 *)(cb_row + (ei < ne ? ei : ne - 4)));
+    d.t = make_uint2(v.x, v.y);
+}
+
+// s[m] += sum over one 32-weight chunk of cb[idx] * x[m]; activation row m at xb + m RXS.
+template <int M>
+QMV_DEV void chunk_dot_m(uint4 q, uint32_t tb, const float *xb, float (&s)[M]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint32_t ev = (w[j] << 1) & 0x1E1E1E1Eu;
+        const uint32_t od = (w[j] >> 3) & 0x1E1E1E1Eu;
+        const float v[8] = {lds_h(add_byte<0>(tb, ev)), lds_h(add_byte<0>(tb, od)),
+                            lds_h(add_byte<1>(tb, ev)), lds_h(add_byte<1>(tb, od)),
+                            lds_h(add_byte<2>(tb, ev)), lds_h(add_byte<2>(tb, od)),
+                            lds_h(add_byte<3>(tb, ev)), lds_h(add_byte<3>(tb, od))};
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float4 x0 = *(const float4 *)(xb + m * RXS + 8 * j);
+            const float4 x1 = *(const float4 *)(xb + m * RXS + 8 * j + 4);
+            float a = s[m];
+            a = fmaf(v[0], x0.x, a);
+            a = fmaf(v[1], x0.y, a);
+            a = fmaf(v[2], x0.z, a);
+            a = fmaf(v[3], x0.w, a);
+            a = fmaf(v[4], x1.x, a);
+            a = fmaf(v[5], x1.y, a);
+            a = fmaf(v[6], x1.z, a);
+            s[m] = fmaf(v[7], x1.w, a);
+        }
+    }
+}
+
+// Per step: the activation loads (thread t loads piece t of each batch row), the next
+// step's weight loads, the LDS writes (activations in padded 32-float blocks; the wave's
+// codebook slice), a barrier, the dots.
+template <int M, int XT>
+__global__ void __launch_bounds__(WG) cb4_chunked_kernel(const uint8_t *__restrict__ idx,
+                                                         const uint16_t *__restrict__ cb,
+                                                         const void *__restrict__ x,
+                                                         float *__restrict__ y, int n, int k) {
+    extern __shared__ float4 lds4[];
+    float *sx = (float *)lds4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint16_t *tab = (uint16_t *)(sx + M * RXS) + wave * 256;
+    const int nchunk = k >> 5, nst = (nchunk + 63) / 64;
+    const int row = blockIdx.x * WAVES + wave;
+    const int rowc = row < n ? row : n - 1;
+    const uint8_t *idx_row = idx + (int64_t)rowc * (k >> 1);
+    const uint16_t *cb_row = cb + (int64_t)rowc * (k >> 7) * 16;
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; m++) acc[m] = 0.f;
+    auto step = [&](int c, const StepData &use, StepData &fill) {
+        const int k0 = c * KCB;
+        const int kq = min(KCB, k - k0) >> 2;  // 16-byte pieces of this step, per row
+        const int t = threadIdx.x < kq ? threadIdx.x : kq - 1;
+        float4 xv[M];
+#pragma unroll
+        for (int m = 0; m < M; m++) xv[m] = ld_act4<XT>(x, (int64_t)m * k + k0 + 4 * t);
+        load_step(fill, idx_row, cb_row, c + 1, nchunk, lane);
+        __builtin_amdgcn_sched_barrier(0);  // every load is issued before the LDS writes wait
+        if (c) __syncthreads();  // the previous step's activations and tables are consumed
+#pragma unroll
+        for (int m = 0; m < M; m++)
+            *(float4 *)(sx + m * RXS + (threadIdx.x >> 3) * XS + (threadIdx.x & 7) * 4) = xv[m];
+        *(uint2 *)(tab + 4 * lane) = use.t;
+        __syncthreads();
+        const int ci = c * 64 + lane;
+        const int lc = ci < nchunk ? lane : nchunk - 1 - c * 64;
+        float s[M];
+#pragma unroll
+        for (int m = 0; m < M; m++) s[m] = 0.f;
+        chunk_dot_m<M>(use.q, (uint32_t)(uintptr_t)(tab + (lc >> 2) * 16), sx + lc * XS, s);
+        // the dots are computed here, not sunk into a branch over the valid lanes (which
+        // would keep every activation read of the step live at once)
+#pragma unroll
+        for (int m = 0; m < M; m++) asm volatile("" : "+v"(s[m]));
+#pragma unroll
+        for (int m = 0; m < M; m++) acc[m] = ci < nchunk ? acc[m] + s[m] : acc[m];
+    };
+    StepData d0, d1;
+    load_step(d0, idx_row, cb_row, 0, nchunk, lane);
+    for (int c = 0; c < nst; c += 2) {
+        step(c, d0, d1);
+        if (c + 1 < nst) step(c + 1, d1, d0);
+    }
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        const float v = wave_sum(acc[m]);
+        if (lane == 0 && row < n) y[(int64_t)m * n + row] = v;
+    }
+}
+
+constexpr size_t chunked_lds(int m) { return (size_t)m * RXS * 4 + (size_t)WAVES * 256 * 2; }
+
+template <int M, int XT>
+void launch_chunked(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
+    const int n = (int)w->n, k = (int)w->k;
+    hipLaunchKernelGGL((cb4_chunked_kernel<M, XT>), dim3((n + WAVES - 1) / WAVES), dim3(WG), chunked_lds(M), s,
+                       (const uint8_t *)w->codes, (const uint16_t *)w->codebook, x, y, n, k);
+}
+
+template <int XT>
+bool dispatch_chunked(int m, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
+    switch (m) {
+    case 1: launch_chunked<1, XT>(w, x, y, s); return true;
+    case 2: launch_chunked<2, XT>(w, x, y, s); return true;
+    case 3: launch_chunked<3, XT>(w, x, y, s); return true;
+    case 4: launch_chunked<4, XT>(w, x, y, s); return true;
+    case 5: launch_chunked<5, XT>(w, x, y, s); return true;
+    case 6: launch_chunked<6, XT>(w, x, y, s); return true;
+    case 7: launch_chunked<7, XT>(w, x, y, s); return true;
+    case 8: launch_chunked<8, XT>(w, x, y, s); return true;
+    }
+    return false;
+}
+
 size_t lds_need(int m, int64_t k, int nt) {
     const int cpl = (int)((k / 32 + 63) / 64);
     return (size_t)((m * cpl * 512 + WG - 1) / WG) * WG / 8 * XS * 4 + (size_t)WAVES * nt * (k >> 7) * 32;
@@ -255,8 +392,12 @@ size_t lds_need(int m, int64_t k, int nt) {
 const char *launch_gemv_cb4(const qmv_weights *w, int m, const void *x, int xt, float *y, hipStream_t s) {
     const int64_t k = w->k, nchunk = k / 32;
     const int cpl = (int)((nchunk + 63) / 64);
-    if (cpl > 8 || (int64_t)m * k > 16384) return nullptr;
-    if ((int64_t)lds_need(m, k, 1) > device_info().lds_per_block) return nullptr;
+    if (w->n > INT32_MAX || k > INT32_MAX / 8) return nullptr;
+    if (cpl > 8 || (int64_t)m * k > 16384 || (int64_t)lds_need(m, k, 1) > device_info().lds_per_block) {
+        if ((int64_t)chunked_lds(m) > device_info().lds_per_block) return nullptr;
+        const bool ok = xt == QMV_F32 ? dispatch_chunked<0>(m, w, x, y, s) : dispatch_chunked<1>(m, w, x, y, s);
+        return ok ? "cb4.lds-table-chunked.fma-mix" : nullptr;
+    }
     Cb4Args a{(const uint8_t *)w->codes, nullptr, (const uint16_t *)w->codebook, nullptr, 0, 0, x, y, nullptr,
               (int)w->n, (int)k, 1};
     const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, cpl, a, s) : dispatch_m<1>(m, cpl, a, s);

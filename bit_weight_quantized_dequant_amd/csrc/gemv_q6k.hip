@@ -12,10 +12,9 @@
 // fields of each qh byte give four runs t = 0..3 of 16 consecutive weights,
 // e = 128h + 32t + l0 + j, each under one sub-scale sc[8h + 2t + l0/16].
 //
-// Activations are staged once per workgroup into LDS in that same unit order
-// (64 floats per unit, 4 floats of padding so eight lanes reading eight
-// consecutive units with ds_read_b128 hit disjoint banks), before the weight loads
-// are issued.  Centering is exact: each 6-bit code is OR-ed under the binary16
+// Activations are staged per workgroup into LDS in that same unit order (64 floats
+// per unit, 4 floats of padding so eight lanes reading eight consecutive units with
+// ds_read_b128 hit disjoint banks), 64 units (4096 activations) of K at a time.  Centering is exact: each 6-bit code is OR-ed under the binary16
 // exponent of 1024 and one packed half subtract gives q - 32 exactly; v_fma_mix_f32
 // multiplies it by the fp32 activation exactly.  Per run the kernel applies its
 // sub-scale, and d once per unit.
@@ -27,21 +26,8 @@ namespace {
 
 constexpr int WG = 512;
 constexpr int WAVES = WG / 64;
-constexpr int US = 68;  // floats per staged 64-activation unit
-
-// Stage x [M][k] into LDS in unit order: unit u of row m at sx[(m*nu + u)*US], with
-// run t (16 floats) at +16t.  Threads move coalesced 16-byte chunks.
-template <int M, int XT>
-__device__ void stage_units(const void *x, int k, float *sx) {
-    const int nu = k >> 6, nq = k >> 2;
-    const int total = M * nq;
-    for (int c = threadIdx.x; c < total; c += WG) {
-        const int m = c / nq, e = (c - m * nq) * 4;
-        const int sb = e >> 8, h = (e >> 7) & 1, t = (e >> 5) & 3, odd = (e >> 4) & 1;
-        const int u = m * nu + 4 * sb + 2 * h + odd;
-        *(float4 *)(sx + u * US + 16 * t + (e & 15)) = ld_act4<XT>(x, (int64_t)c * 4);
-    }
-}
+constexpr int US = 68;    // floats per staged 64-activation unit
+constexpr int CUN = 64;   // units per K chunk (4096 activations)
 
 // sum_j (q_j - 32) x_j over the four bytes (values 0..63) of dword q and x[0..3], exact products.
 QMV_DEV float dot4_c32(uint32_t q, float4 xv, float acc) {
@@ -55,14 +41,27 @@ QMV_DEV float dot4_c32(uint32_t q, float4 xv, float acc) {
     return acc;
 }
 
+// Raw bytes of one unit (quarter super-block), as loaded.
 struct Unit {
     uint4 a, b, h;   // ql run (t=0 low / t=2 high), ql run (t=1 low / t=3 high), qh run
-    uint32_t sc4;    // the unit's four sub-scales, byte t = sc[8h + 2t + odd]
+    uint4 s16;       // the super-block's 16 sub-scales
     uint16_t d;
 };
 
-// sum over the unit's 64 weights of (q - 32) * sc * x, times d.
-QMV_DEV float unit_dot(const Unit &w, const float *xu) {
+QMV_DEV void load_unit(Unit &w, const uint8_t *ql, const uint8_t *qh, const int8_t *scp, const uint16_t *dp,
+                       int row, int k, int u) {
+    const int sb = u >> 2, h = (u >> 1) & 1, odd = u & 1;
+    const uint8_t *qlr = ql + (int64_t)row * (k >> 1) + sb * 128 + 64 * h + 16 * odd;
+    w.a = ld_stream16(qlr);
+    w.b = ld_stream16(qlr + 32);
+    w.h = ld_stream16(qh + (int64_t)row * (k >> 2) + sb * 64 + 32 * h + 16 * odd);
+    w.s16 = *(const uint4 *)(scp + (int64_t)row * (k >> 4) + sb * 16);
+    w.d = dp[(int64_t)row * (k >> 8) + sb];
+}
+
+// sum over unit u's 64 weights of (q - 32) * sc * x, times d.  The sub-scales are picked
+// from the raw super-block bytes here, where they are used, not next to the load.
+QMV_DEV float unit_dot(const Unit &w, int u, const float *xu) {
     const uint32_t A[4] = {w.a.x, w.a.y, w.a.z, w.a.w};
     const uint32_t B[4] = {w.b.x, w.b.y, w.b.z, w.b.w};
     const uint32_t H[4] = {w.h.x, w.h.y, w.h.z, w.h.w};
@@ -78,8 +77,11 @@ QMV_DEV float unit_dot(const Unit &w, const float *xu) {
         s2 = dot4_c32(q2, *(const float4 *)(xu + 32 + 4 * i), s2);
         s3 = dot4_c32(q3, *(const float4 *)(xu + 48 + 4 * i), s3);
     }
-    const float sc0 = (float)(int8_t)(w.sc4 & 0xFF), sc1 = (float)(int8_t)((w.sc4 >> 8) & 0xFF);
-    const float sc2 = (float)(int8_t)((w.sc4 >> 16) & 0xFF), sc3 = (float)(int8_t)(w.sc4 >> 24);
+    // sub-scales 8h + odd + {0, 2, 4, 6}: bytes odd and odd+2 of dwords 2h and 2h+1
+    const int h = (u >> 1) & 1, odd = u & 1;
+    const uint32_t lo = h ? w.s16.z : w.s16.x, hi = h ? w.s16.w : w.s16.y;
+    const float sc0 = (float)(int8_t)(lo >> (8 * odd)), sc1 = (float)(int8_t)(lo >> (8 * odd + 16));
+    const float sc2 = (float)(int8_t)(hi >> (8 * odd)), sc3 = (float)(int8_t)(hi >> (8 * odd + 16));
     float r = sc0 * s0;
     r = fmaf(sc1, s1, r);
     r = fmaf(sc2, s2, r);
@@ -88,10 +90,13 @@ QMV_DEV float unit_dot(const Unit &w, const float *xu) {
 }
 
 // Lane l of a wave: when G > 1 the wave covers G rows, lane l taking unit l % U of row
-// l / U (U = 64 / G units per row); when G == 1 it covers one row, lane l taking units
-// l, l+64, ... (UPL of them).  Activations are staged before the weight loads are issued
-// (vector loads return in order).
-template <int M, int UPL, int XT>
+// l / U (U = 64 / G units per row, the whole row in one chunk); when G == 1 it covers one
+// row and K is walked in chunks of 64 units, lane l taking unit l of each chunk.  Per
+// chunk: the activation loads, then the next chunk's unit loads (the current chunk's were
+// issued during the previous one), then the LDS writes, a barrier, the dots.  No branch
+// sits around a load (row and unit indices are clamped); activations of chunk row m, unit
+// slot j sit at sx[(m * 64 + j) * US], run t at +16 t.
+template <int M, int XT>
 __global__ void __launch_bounds__(WG) gemv_q6k_kernel(const uint8_t *__restrict__ ql,
                                                       const uint8_t *__restrict__ qh,
                                                       const int8_t *__restrict__ scp,
@@ -99,53 +104,54 @@ __global__ void __launch_bounds__(WG) gemv_q6k_kernel(const uint8_t *__restrict_
                                                       const void *__restrict__ x,
                                                       float *__restrict__ y, int n, int k, int G) {
     extern __shared__ float lds[];
-    const int nu = k >> 6, nsb = k >> 8;
+    constexpr int XPT = M * (CUN * 16) / WG;  // 16-byte activation pieces per thread per chunk
+    const int nu = k >> 6;
+    const int nch = G > 1 ? 1 : (nu + CUN - 1) / CUN;
     float *sx = lds;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int U = G > 1 ? 64 / G : nu;
-    const int sub = G > 1 ? lane / U : 0;
-    const int ul = G > 1 ? lane % U : lane;
+    const int U = G > 1 ? 64 / G : CUN;
+    const int sub = lane / U, ul = lane % U;
     const int row = (blockIdx.x * WAVES + wave) * G + sub;
-
-    stage_units<M, XT>(x, k, sx);
-
-    Unit wv[UPL];
-#pragma unroll
-    for (int j = 0; j < UPL; j++) {
-        const int u = ul + 64 * j;
-        if (row < n && u < nu) {
-            const int sb = u >> 2, h = (u >> 1) & 1, odd = u & 1;
-            const uint8_t *qlr = ql + (int64_t)row * (k >> 1) + sb * 128 + 64 * h + 16 * odd;
-            const uint8_t *qhr = qh + (int64_t)row * (k >> 2) + sb * 64 + 32 * h + 16 * odd;
-            wv[j].a = ld_stream16(qlr);
-            wv[j].b = ld_stream16(qlr + 32);
-            wv[j].h = ld_stream16(qhr);
-            const uint4 s16 = *(const uint4 *)(scp + (int64_t)row * (k >> 4) + sb * 16);
-            // sub-scales 8h + odd + {0, 2, 4, 6}: bytes odd and odd+2 of dwords 2h and 2h+1
-            const uint32_t lo = h ? s16.z : s16.x, hi = h ? s16.w : s16.y;
-            const uint32_t a0 = (lo >> (8 * odd)) & 0xFF, a1 = (lo >> (8 * odd + 16)) & 0xFF;
-            const uint32_t a2 = (hi >> (8 * odd)) & 0xFF, a3 = (hi >> (8 * odd + 16)) & 0xFF;
-            wv[j].sc4 = a0 | (a1 << 8) | (a2 << 16) | (a3 << 24);
-            wv[j].d = dp[(int64_t)row * nsb + sb];
-        } else {
-            wv[j].a = wv[j].b = wv[j].h = make_uint4(0, 0, 0, 0);
-            wv[j].sc4 = 0;
-            wv[j].d = 0;
-        }
-    }
-    __syncthreads();
-
+    const int rowc = row < n ? row : n - 1;
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; m++) acc[m] = 0.f;
+    // One chunk: its activation loads, then the next chunk's unit into `fill` (clamped to
+    // the row's last unit past the end), then the LDS writes and the dots with `use`.  Two
+    // register sets alternate, so no copy waits on the loads just issued.
+    auto step = [&](int c, const Unit &use, Unit &fill) {
+        const int k0 = c * CUN * 64;
+        const int kq = min(CUN * 64, k - k0) >> 2;  // 16-byte pieces of this chunk, per row
+        float4 xv[XPT];
 #pragma unroll
-    for (int j = 0; j < UPL; j++) {
-        const int u = ul + 64 * j;
-        if (u < nu) {
-#pragma unroll
-            for (int m = 0; m < M; m++)
-                acc[m] += unit_dot(wv[j], sx + (m * nu + u) * US);
+        for (int j = 0; j < XPT; j++) {
+            const int p = threadIdx.x + j * WG, m = p >> 10, e = p & 1023;
+            xv[j] = ld_act4<XT>(x, (int64_t)m * k + k0 + 4 * (e < kq ? e : kq - 1));
         }
+        const int un = (c + 1) * CUN + ul;
+        load_unit(fill, ql, qh, scp, dp, rowc, k, un < nu ? un : nu - 1);
+        __builtin_amdgcn_sched_barrier(0);  // every load is issued before the LDS writes wait
+        if (c) __syncthreads();  // the previous chunk's activations are consumed
+#pragma unroll
+        for (int j = 0; j < XPT; j++) {
+            const int p = threadIdx.x + j * WG, m = p >> 10, e = 4 * (p & 1023);
+            const int slot = 4 * (e >> 8) + 2 * ((e >> 7) & 1) + ((e >> 4) & 1);
+            *(float4 *)(sx + (m * CUN + slot) * US + 16 * ((e >> 5) & 3) + (e & 15)) = xv[j];
+        }
+        __syncthreads();
+        const int u = c * CUN + ul;
+        const int uc = u < nu ? u : nu - 1;
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float v = acc[m] + unit_dot(use, uc, sx + (m * CUN + (uc - c * CUN)) * US);
+            acc[m] = u < nu ? v : acc[m];
+        }
+    };
+    Unit w0, w1;
+    load_unit(w0, ql, qh, scp, dp, rowc, k, ul < nu ? ul : nu - 1);
+    for (int c = 0; c < nch; c += 2) {
+        step(c, w0, w1);
+        if (c + 1 < nch) step(c + 1, w1, w0);
     }
 #pragma unroll
     for (int m = 0; m < M; m++) {
@@ -154,39 +160,29 @@ __global__ void __launch_bounds__(WG) gemv_q6k_kernel(const uint8_t *__restrict_
     }
 }
 
-template <int M, int UPL, int XT>
+constexpr size_t lds_bytes(int m) { return (size_t)m * CUN * US * sizeof(float); }
+
+template <int M, int XT>
 void launch(const qmv_weights *w, const void *x, float *y, int G, hipStream_t s) {
-    const int n = (int)w->n, k = (int)w->k, nu = k >> 6;
-    const size_t lds = (size_t)M * nu * US * sizeof(float);
+    const int n = (int)w->n, k = (int)w->k;
     const int rows_per_wg = WAVES * G;
     const int grid = (n + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((gemv_q6k_kernel<M, UPL, XT>), dim3(grid), dim3(WG), lds, s,
+    hipLaunchKernelGGL((gemv_q6k_kernel<M, XT>), dim3(grid), dim3(WG), lds_bytes(M), s,
                        (const uint8_t *)w->codes, (const uint8_t *)w->codes_hi, (const int8_t *)w->scales,
                        (const uint16_t *)w->super, x, y, n, k, G);
 }
 
-template <int M, int XT>
-bool dispatch_upl(int upl, const qmv_weights *w, const void *x, float *y, int G, hipStream_t s) {
-    switch (upl) {
-    case 1: launch<M, 1, XT>(w, x, y, G, s); return true;
-    case 2: launch<M, 2, XT>(w, x, y, G, s); return true;
-    case 3: launch<M, 3, XT>(w, x, y, G, s); return true;
-    case 4: launch<M, 4, XT>(w, x, y, G, s); return true;
-    }
-    return false;
-}
-
 template <int XT>
-bool dispatch_m(int m, int upl, const qmv_weights *w, const void *x, float *y, int G, hipStream_t s) {
+bool dispatch_m(int m, const qmv_weights *w, const void *x, float *y, int G, hipStream_t s) {
     switch (m) {
-    case 1: return dispatch_upl<1, XT>(upl, w, x, y, G, s);
-    case 2: return dispatch_upl<2, XT>(upl, w, x, y, G, s);
-    case 3: return dispatch_upl<3, XT>(upl, w, x, y, G, s);
-    case 4: return dispatch_upl<4, XT>(upl, w, x, y, G, s);
-    case 5: return dispatch_upl<5, XT>(upl, w, x, y, G, s);
-    case 6: return dispatch_upl<6, XT>(upl, w, x, y, G, s);
-    case 7: return dispatch_upl<7, XT>(upl, w, x, y, G, s);
-    case 8: return dispatch_upl<8, XT>(upl, w, x, y, G, s);
+    case 1: launch<1, XT>(w, x, y, G, s); return true;
+    case 2: launch<2, XT>(w, x, y, G, s); return true;
+    case 3: launch<3, XT>(w, x, y, G, s); return true;
+    case 4: launch<4, XT>(w, x, y, G, s); return true;
+    case 5: launch<5, XT>(w, x, y, G, s); return true;
+    case 6: launch<6, XT>(w, x, y, G, s); return true;
+    case 7: launch<7, XT>(w, x, y, G, s); return true;
+    case 8: launch<8, XT>(w, x, y, G, s); return true;
     }
     return false;
 }
@@ -195,16 +191,12 @@ bool dispatch_m(int m, int upl, const qmv_weights *w, const void *x, float *y, i
 
 const char *launch_gemv_q6k(const qmv_weights *w, int m, const void *x, int xt, float *y, hipStream_t s) {
     const int64_t n = w->n, k = w->k, nu = k / 64;
-    if ((int64_t)m * k > 16384 || n > INT32_MAX) return nullptr;
-    const size_t lds = (size_t)m * nu * US * sizeof(float);
-    if ((int64_t)lds > device_info().lds_per_block) return nullptr;
+    if (n > INT32_MAX || k > INT32_MAX / 8) return nullptr;
+    if ((int64_t)lds_bytes(m) > device_info().lds_per_block) return nullptr;
     // G rows at a time when a row has fewer than 64 units and 64 is a multiple of them.
     int G = 1;
     if (nu < 64 && 64 % nu == 0) G = (int)(64 / nu);
-    const int upl = G > 1 ? 1 : (int)((nu + 63) / 64);
-    if (upl > 4) return nullptr;
-    const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, upl, w, x, y, G, s)
-                                  : dispatch_m<1>(m, upl, w, x, y, G, s);
+    const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, w, x, y, G, s) : dispatch_m<1>(m, w, x, y, G, s);
     if (!ok) return nullptr;
     return G > 1 ? "q6_K.lds-x.fma-mix.rowgroup" : "q6_K.lds-x.fma-mix";
 }

@@ -160,6 +160,35 @@ def test_q6k_large_sampled(qmv, n, k):
     run_case(qmv, synth.FMT_Q6_K, n, k, 1, synth.DT_F32, seed=0, rows=sample_rows(n))
 
 
+@pytest.mark.parametrize("n,k,m,xt", [(4, 32768, 1, synth.DT_F32), (33, 20480, 1, synth.DT_F32),
+                                      (70, 11008, 2, synth.DT_F32), (70, 11008, 4, synth.DT_BF16),
+                                      (41, 11008, 8, synth.DT_F32), (9, 4352, 8, synth.DT_BF16),
+                                      (17, 8192, 3, synth.DT_F32), (3, 256, 8, synth.DT_F32)])
+def test_q6k_k_chunked_batches(qmv, n, k, m, xt):
+    # K is walked 4096 activations at a time: one, two (even), three and five (odd) chunks,
+    # ragged last chunks (11008 = 2 * 4096 + 2816, 4352 = 4096 + 256), batches up to 8
+    path = "q6_K.lds-x.fma-mix.rowgroup" if k // 64 < 64 and 64 % (k // 64) == 0 else "q6_K.lds-x.fma-mix"
+    run_case(qmv, synth.FMT_Q6_K, n, k, m, xt, seed=n + k + m, expect_path=path)
+
+
+def test_q6k_chunked_unit_vector_returns_column_exactly(qmv):
+    import torch
+    n, k, m = 37, 11008, 5
+    w = synth.gen_weights(synth.FMT_Q6_K, n, k, seed=16)
+    W = qweights(synth.FMT_Q6_K, n, k, w)
+    dense = oracle.dequant(oracle.Mat(synth.FMT_Q6_K, n, k, w)).astype(np.float32)
+    cols = (0, 4095, 4096, 8200, 11007)  # chunk edges and the ragged last chunk
+    e = np.zeros((m, k), dtype=np.float32)
+    for r, j in enumerate(cols):
+        e[r, j] = 1.0
+    y = qmv.gemv(W, x_to_device(e, synth.DT_F32))
+    torch.cuda.synchronize()
+    assert qmv.last_path() == "q6_K.lds-x.fma-mix"
+    y = y.cpu().numpy()
+    for r, j in enumerate(cols):
+        assert np.array_equal(y[r], dense[:, j]), j
+
+
 def test_q6k_unit_vector_returns_column_exactly(qmv):
     import torch
     n, k = 96, 2048
@@ -234,6 +263,35 @@ def test_cb4_batched(qmv, m):
 @pytest.mark.parametrize("n,k", [(2048, 7168), (7168, 2048)])
 def test_cb4_expert_shapes_sampled(qmv, n, k):
     run_case(qmv, synth.FMT_CB4, n, k, 1, synth.DT_BF16, seed=0, rows=sample_rows(n))
+
+
+@pytest.mark.parametrize("n,k,m,xt", [(4, 32768, 1, synth.DT_F32), (33, 20480, 1, synth.DT_BF16),
+                                      (3, 16512, 1, synth.DT_F32), (70, 10880, 2, synth.DT_F32),
+                                      (41, 7168, 8, synth.DT_BF16), (9, 4224, 5, synth.DT_F32),
+                                      (2, 2176, 8, synth.DT_BF16), (17, 16384, 3, synth.DT_F32)])
+def test_cb4_k_chunked_batches(qmv, n, k, m, xt):
+    # K walked 2048 weights at a time: even and odd step counts, ragged last steps down to
+    # one 128-weight group (16512 = 8 * 2048 + 128, 4224 = 2 * 2048 + 128), batches up to 8
+    path = "cb4.lds-table-chunked.fma-mix" if (m * k > 16384 or k > 16384) else "cb4.lds-table.fma-mix"
+    run_case(qmv, synth.FMT_CB4, n, k, m, xt, seed=n + k + m, expect_path=path)
+
+
+def test_cb4_chunked_unit_vector_returns_codebook_entry_exactly(qmv):
+    import torch
+    n, k, m = 37, 10880, 5
+    w = synth.gen_weights(synth.FMT_CB4, n, k, seed=17)
+    W = qweights(synth.FMT_CB4, n, k, w)
+    dense = oracle.dequant(oracle.Mat(synth.FMT_CB4, n, k, w)).astype(np.float32)
+    cols = (0, 2047, 2048, 6001, 10879)  # step edges and the ragged last step
+    e = np.zeros((m, k), dtype=np.float32)
+    for r, j in enumerate(cols):
+        e[r, j] = 1.0
+    y = qmv.gemv(W, x_to_device(e, synth.DT_F32))
+    torch.cuda.synchronize()
+    assert qmv.last_path() == "cb4.lds-table-chunked.fma-mix"
+    y = y.cpu().numpy()
+    for r, j in enumerate(cols):
+        assert np.array_equal(y[r], dense[:, j]), j
 
 
 def test_cb4_unit_vector_returns_codebook_entry_exactly(qmv):
