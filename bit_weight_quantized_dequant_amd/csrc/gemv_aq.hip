@@ -144,7 +144,7 @@ bool dispatch_m(int m, const qmv_weights *w, const void *x, float *y, hipStream_
 }  // namespace
 
 const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, float *y, hipStream_t s) {
-    if (w->n > INT32_MAX || w->k > INT32_MAX) return nullptr;
+    if (w->n > INT32_MAX || w->k > INT32_MAX / 8) return nullptr;
     const size_t lds = 2048 * 4 + (size_t)m * 64 * XU * 4;
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
     const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, w, x, y, s) : dispatch_m<1>(m, w, x, y, s);

@@ -119,8 +119,10 @@ int qmv_validate(const qmv_weights *w, int32_t m, int32_t xt);
  *         16-byte aligned; y: device fp32 [m][n], 16-byte aligned.
  *   m   : 1..QMV_MAX_BATCH.  Each weight block is decoded once for all m rows.
  *   Accumulation is fp32; weights are formed exactly from their fields.
- *   Errors: any QMV_ERR_* from qmv_validate; QMV_ERR_NULL for x/y; QMV_ERR_LIMIT
- *   when m*k exceeds what one workgroup stages (m*k <= 24576); QMV_ERR_HIP.
+ *   Any n < 2^31 and k <= (2^31 - 1) / 8: activations that do not fit one workgroup's
+ *   LDS are walked along k in chunks.
+ *   Errors: any QMV_ERR_* from qmv_validate; QMV_ERR_NULL for x/y; QMV_ERR_LIMIT when n
+ *   or k is beyond those bounds; QMV_ERR_HIP.
  */
 int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *y, void *stream);
 
@@ -178,6 +180,8 @@ int qmm_partials(const qmv_weights *w, int32_t m, const int8_t *xq, int32_t *i32
  *              expert 0, which stays in bounds; none of those bytes is used).
  *   x : device [d_model] of dtype xt; h: device fp32 [n_ids][d_ff] (written);
  *   y : device fp32 [n_ids][d_model].  1 <= n_ids <= 64.
+ *   QMV_ERR_LIMIT when d_model or d_ff exceeds 16384 (an expert row is staged whole in
+ *   LDS).
  */
 int qmv_moe_ffn(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,
                 int32_t n_experts, const int32_t *ids, int32_t n_ids, const void *x, int32_t xt,
