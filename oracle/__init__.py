@@ -21,11 +21,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "qmv_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-Q4_0, Q6_K, CB4, AQ2X8 = 1, 2, 3, 4
+Q4_0, Q6_K, CB4, AQ2X8, CB8, AQ3X8 = 1, 2, 3, 4, 5, 6
 F32, BF16 = 0, 1
 
 _PLANES = {Q4_0: ("qs", "d"), Q6_K: ("ql", "qh", "sc", "d"), CB4: ("idx", "cb"),
-           AQ2X8: ("codes", "cbk", "s")}
+           AQ2X8: ("codes", "cbk", "s"), CB8: ("idx", "cb"), AQ3X8: ("codes", "cbk", "s")}
 
 
 def build(force: bool = True) -> str:

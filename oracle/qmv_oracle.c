@@ -15,8 +15,8 @@
  *     §3.2 / §3.3: a raw q6_K super-block is 210 bytes for 256 weights.
  *   - "Chasing x100", "The kernel is ready": GEMVs are checked against a
  *     bit-faithful CPU reference; the format round trip is exact; the 4-bit
- *     codebook has 16 entries (quality table, "K=16"); the 2-bit format is an
- *     additive code.
+ *     codebook has 16 entries (quality table, "K=16"), the 8-bit one 256
+ *     ("K=256"); the 2-bit and 3-bit formats are additive codes.
  *   - "LLMs on the Xiaomi TV Box", §11.5 E18: q4_0 costs 4.5 bits per weight
  *     (an fp16 scale per 32 4-bit codes).
  *   - quantprobe LAWS.md, Law 4: decode is a weight-byte stream (the GEMV).
@@ -36,7 +36,7 @@
 #include <omp.h>
 #endif
 
-enum { QO_Q4_0 = 1, QO_Q6_K = 2, QO_CB4 = 3, QO_AQ2X8 = 4 };
+enum { QO_Q4_0 = 1, QO_Q6_K = 2, QO_CB4 = 3, QO_AQ2X8 = 4, QO_CB8 = 5, QO_AQ3X8 = 6 };
 enum { QO_F32 = 0, QO_BF16 = 1 };
 
 /* One weight matrix, n rows (outputs) by k columns (inputs), as host planes.
@@ -44,7 +44,9 @@ enum { QO_F32 = 0, QO_BF16 = 1 };
  *   q6_K : p0 = ql  u8[n][k/256][128]  p1 = qh  u8[n][k/256][64]
  *          p2 = sc  i8[n][k/256][16]   p3 = d   f16[n][k/256]
  *   cb4  : p0 = idx u8[n][k/2]         p1 = cb  f16[n][k/128][16]
- *   aq2x8: p0 = codes u8[n][k/8][2]    p1 = cbk f16[2][256][8]   p2 = s f16[n]  */
+ *   aq2x8: p0 = codes u8[n][k/8][2]    p1 = cbk f16[2][256][8]   p2 = s f16[n]
+ *   cb8  : p0 = idx u8[n][k]           p1 = cb  f16[n][256]
+ *   aq3x8: p0 = codes u8[n][k/8][3]    p1 = cbk f16[3][256][8]   p2 = s f16[n]  */
 typedef struct {
     int32_t fmt;
     int64_t n, k;
@@ -121,11 +123,21 @@ int32_t qo_cb4_code(const qo_mat *m, int64_t row, int64_t col)
     return (col & 1) ? (byte >> 4) : (byte & 15);
 }
 
-/* 2-bit additive code: each 8-weight group stores (c1, c2), one byte each. */
+/* 8-bit codebook index, reading: one byte per weight, in k order. */
+int32_t qo_cb8_code(const qo_mat *m, int64_t row, int64_t col)
+{
+    return ((const uint8_t *)m->p0)[row * m->k + col];
+}
+
+/* Codebooks of an additive code: 2 (2-bit format) or 3 (3-bit format). */
+static int aq_books(const qo_mat *m) { return m->fmt == QO_AQ3X8 ? 3 : 2; }
+
+/* Additive codes: each 8-weight group stores one byte per codebook, c1 first. */
 int32_t qo_aq_code(const qo_mat *m, int64_t row, int64_t group, int which)
 {
-    const uint8_t *c = (const uint8_t *)m->p0 + row * (m->k / 8) * 2;
-    return c[group * 2 + which];
+    int nb = aq_books(m);
+    const uint8_t *c = (const uint8_t *)m->p0 + row * (m->k / 8) * nb;
+    return c[group * nb + which];
 }
 
 /* --------------------------------------------------------------- weights */
@@ -150,12 +162,19 @@ double qo_weight(const qo_mat *m, int64_t row, int64_t col)
         int64_t g = row * (m->k / 128) + col / 128;
         return f16_at(m->p1, g * 16 + qo_cb4_code(m, row, col));
     }
-    case QO_AQ2X8: {
+    case QO_AQ2X8:
+    case QO_AQ3X8: {
+        /* weight = s[row] * (sum over codebooks b of C_b[c_b][j]); the sum of two or three
+         * fp16 values and the product are exact in double */
         int64_t grp = col / 8, j = col % 8;
-        int c1 = qo_aq_code(m, row, grp, 0), c2 = qo_aq_code(m, row, grp, 1);
-        double v = f16_at(m->p1, (int64_t)c1 * 8 + j) + f16_at(m->p1, 2048 + (int64_t)c2 * 8 + j);
+        double v = 0.0;
+        for (int b = 0; b < aq_books(m); b++)
+            v += f16_at(m->p1, (int64_t)b * 2048 + (int64_t)qo_aq_code(m, row, grp, b) * 8 + j);
         return f16_at(m->p2, row) * v;
     }
+    case QO_CB8:
+        /* reading: one 256-entry codebook per output row */
+        return f16_at(m->p1, row * 256 + qo_cb8_code(m, row, col));
     }
     return NAN;
 }
@@ -168,7 +187,7 @@ void qo_dequant(const qo_mat *m, double *w)
             w[r * m->k + c] = qo_weight(m, r, c);
 }
 
-/* Exact integer codes (q4_0 / q6_K / cb4 fields) as int32[n][k]. */
+/* Exact integer codes (q4_0 / q6_K / cb4 / cb8 fields) as int32[n][k]. */
 void qo_codes(const qo_mat *m, int32_t *out)
 {
     for (int64_t r = 0; r < m->n; r++)
@@ -177,6 +196,7 @@ void qo_codes(const qo_mat *m, int32_t *out)
             if (m->fmt == QO_Q4_0) v = qo_q4_0_code(m, r, c);
             if (m->fmt == QO_Q6_K) v = qo_q6k_code(m, r, c);
             if (m->fmt == QO_CB4) v = qo_cb4_code(m, r, c);
+            if (m->fmt == QO_CB8) v = qo_cb8_code(m, r, c);
             out[r * m->k + c] = v;
         }
 }

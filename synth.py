@@ -14,10 +14,13 @@ Plane shapes (row-major, rows = output features n, columns = input features k):
   q6_K    ql u8 [N][K/256][128] qh u8 [N][K/256][64] sc i8 [N][K/256][16] d f16 [N][K/256]
   cb4     idx u8 [N][K/2]       cb f16 [N][K/128][16]
   aq2x8   codes u8 [N][K/8][2]  cbk f16 [2][256][8]  s f16 [N]
+  cb8     idx u8 [N][K]         cb f16 [N][256]
+  aq3x8   codes u8 [N][K/8][3]  cbk f16 [3][256][8]  s f16 [N]
 
 Value distributions follow the workload descriptions: q4_0 d = 0.02*U(0.5,1.5)/8;
 q6_K sc ~ U{1..127}, d = 1e-4*U(0.5,1.5); cb4 entries = sorted draws of N(0, 0.02);
-aq2x8 codebooks N(0, 0.01), row scale U(0.5, 1.5); activations N(0, 1).
+aq2x8 and aq3x8 codebooks N(0, 0.01), row scale U(0.5, 1.5); cb8 entries = sorted draws
+of N(0, 0.02) (the cb4 distribution, 256 per row); activations N(0, 1).
 N(0, s) means standard deviation s.
 
 Every plane has its own stream: SeedSequence([seed, tag, plane, extra...]) fed to
@@ -28,13 +31,13 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "FMT_Q4_0", "FMT_Q6_K", "FMT_CB4", "FMT_AQ2X8",
+    "FMT_Q4_0", "FMT_Q6_K", "FMT_CB4", "FMT_AQ2X8", "FMT_CB8", "FMT_AQ3X8",
     "DT_F32", "DT_BF16",
     "gen_weights", "gen_x", "gen_moe_ids", "rand_bytes", "f32_to_bf16_bits",
     "bf16_bits_to_f32", "plane_names",
 ]
 
-FMT_Q4_0, FMT_Q6_K, FMT_CB4, FMT_AQ2X8 = 1, 2, 3, 4
+FMT_Q4_0, FMT_Q6_K, FMT_CB4, FMT_AQ2X8, FMT_CB8, FMT_AQ3X8 = 1, 2, 3, 4, 5, 6
 DT_F32, DT_BF16 = 0, 1
 
 _PLANES = {
@@ -42,6 +45,8 @@ _PLANES = {
     FMT_Q6_K: ("ql", "qh", "sc", "d"),
     FMT_CB4: ("idx", "cb"),
     FMT_AQ2X8: ("codes", "cbk", "s"),
+    FMT_CB8: ("idx", "cb"),
+    FMT_AQ3X8: ("codes", "cbk", "s"),
 }
 
 
@@ -109,13 +114,20 @@ def gen_weights(fmt: int, n: int, k: int, seed: int = 0, expert: int = 0, matrix
         idx = rand_bytes(n * k // 2, *key, 1).reshape(n, k // 2)
         cb = np.sort(_rng(*key, 2).normal(0.0, 0.02, (ng, 16)), axis=1)
         return {"idx": idx, "cb": _f16(cb).reshape(n, k // 128, 16)}
-    if fmt == FMT_AQ2X8:
+    if fmt in (FMT_AQ2X8, FMT_AQ3X8):
         if k % 8:
-            raise ValueError("aq2x8 needs k % 8 == 0")
-        codes = rand_bytes(n * (k // 8) * 2, *key, 1).reshape(n, k // 8, 2)
-        cbk = _f16(_rng(*key, 2).normal(0.0, 0.01, (2, 256, 8)))
+            raise ValueError("additive codes need k % 8 == 0")
+        nb = 2 if fmt == FMT_AQ2X8 else 3
+        codes = rand_bytes(n * (k // 8) * nb, *key, 1).reshape(n, k // 8, nb)
+        cbk = _f16(_rng(*key, 2).normal(0.0, 0.01, (nb, 256, 8)))
         s = _f16(_rng(*key, 3).uniform(0.5, 1.5, n))
         return {"codes": codes, "cbk": cbk, "s": s}
+    if fmt == FMT_CB8:
+        if k % 16:
+            raise ValueError("cb8 needs k % 16 == 0")
+        idx = rand_bytes(n * k, *key, 1).reshape(n, k)
+        cb = np.sort(_rng(*key, 2).normal(0.0, 0.02, (n, 256)), axis=1)
+        return {"idx": idx, "cb": _f16(cb)}
     raise ValueError(f"unknown format {fmt}")
 
 

@@ -127,6 +127,27 @@ def test_aq_golden_group():
     assert oracle.dequant(m)[0].tolist() == [float(v) for v in g["weights"]]
 
 
+def test_cb8_golden_row():
+    g = load_golden("cb8_row.txt")
+    idx = np.array(g["idx"], dtype=np.uint8).reshape(1, 16)
+    cb = f16((np.arange(256) - 128) / 64.0).reshape(1, 256)
+    m = oracle.Mat(oracle.CB8, 1, 16, {"idx": idx, "cb": cb})
+    assert oracle.dequant(m)[0].tolist() == [float(v) for v in g["weights"]]
+    assert oracle.codes(m)[0].tolist() == g["idx"]
+
+
+def test_aq3_golden_group():
+    g = load_golden("aq3_group.txt")
+    codes = np.array([[[g["c1"], g["c2"], g["c3"]]]], dtype=np.uint8)
+    cbk = np.zeros((3, 256, 8), dtype=np.float16)
+    cbk[0, g["c1"]] = f16(np.arange(8) / 2.0)
+    cbk[1, g["c2"]] = f16(-0.25 * np.ones(8))
+    cbk[2, g["c3"]] = f16((8 - np.arange(8)) / 16.0)
+    s = np.array([g["s_bits"]], dtype=np.uint16).view(np.float16)
+    m = oracle.Mat(oracle.AQ3X8, 1, 8, {"codes": codes, "cbk": cbk, "s": s})
+    assert oracle.dequant(m)[0].tolist() == [float(v) for v in g["weights"]]
+
+
 # -------------------------------------------------------------- round trips
 
 def test_q4_0_round_trip_exhaustive():
@@ -180,6 +201,46 @@ def test_aq_every_code_pair_reaches_its_rows():
     assert np.array_equal(w, ref)
 
 
+def test_cb8_every_index_at_every_position():
+    # row v has index (v + p) % 256 at position p: every byte value at every position
+    n, k = 256, 512
+    q = np.array([[(v + p) % 256 for p in range(k)] for v in range(n)], dtype=np.int32)
+    cb = f16(np.arange(n)[:, None] * 0 + (np.arange(256)[None, :] - 100) / 32.0)
+    m = oracle.Mat(oracle.CB8, n, k, {"idx": q.astype(np.uint8), "cb": cb})
+    assert np.array_equal(oracle.codes(m), q)
+    assert np.array_equal(oracle.dequant(m), (q - 100) / 32.0)
+
+
+def test_aq3_every_code_triple_reaches_its_rows():
+    # C1[c][j] = c + j/8, C2[c][j] = -c*2^-10, C3[c][j] = c*2^-4 - j: each row's triple decodes
+    # to the numpy sum of the three fp16 table rows times s
+    n = 256
+    cbk = np.zeros((3, 256, 8), dtype=np.float64)
+    cbk[0] = np.arange(256)[:, None] + np.arange(8)[None, :] / 8.0
+    cbk[1] = -np.arange(256)[:, None] * 2.0 ** -10
+    cbk[2] = np.arange(256)[:, None] * 2.0 ** -4 - np.arange(8)[None, :]
+    cbk = f16(cbk)
+    r = np.arange(n)
+    codes = np.stack([r, (r * 37 + 11) % 256, (r * 101 + 3) % 256], axis=1).astype(np.uint8).reshape(n, 1, 3)
+    s = f16(0.5 + (r % 7) / 8.0)
+    m = oracle.Mat(oracle.AQ3X8, n, 8, {"codes": codes, "cbk": cbk, "s": s})
+    ref = (cbk[0, codes[:, 0, 0]].astype(np.float64) + cbk[1, codes[:, 0, 1]].astype(np.float64)
+           + cbk[2, codes[:, 0, 2]].astype(np.float64)) * s.astype(np.float64)[:, None]
+    assert np.array_equal(oracle.dequant(m), ref)
+
+
+def test_aq3_with_zero_third_codebook_is_the_two_codebook_format():
+    # C3 = 0 reduces the 3-bit code to the (separately pinned) 2-bit code over (c1, c2)
+    w3 = synth.gen_weights(synth.FMT_AQ3X8, 5, 96, seed=12)
+    w3["cbk"][2] = 0
+    w2 = {"codes": np.ascontiguousarray(w3["codes"][:, :, :2]), "cbk": np.ascontiguousarray(w3["cbk"][:2]),
+          "s": w3["s"]}
+    m3, m2 = oracle.Mat(oracle.AQ3X8, 5, 96, w3), oracle.Mat(oracle.AQ2X8, 5, 96, w2)
+    assert np.array_equal(oracle.dequant(m3), oracle.dequant(m2))
+    x = synth.gen_x(2, 96, synth.DT_BF16, seed=12)
+    assert np.array_equal(oracle.gemv(m3, x, oracle.BF16)[0], oracle.gemv(m2, x, oracle.BF16)[0])
+
+
 # --------------------------------------------------------- GEMV arithmetic
 
 def _dense_from_codes(fmt, q, planes):
@@ -197,10 +258,14 @@ def _dense_from_codes(fmt, q, planes):
         cb = planes["cb"].astype(np.float64)
         g = np.arange(k) // 128
         return cb[np.arange(n)[:, None], g[None, :], q]
+    if fmt == oracle.CB8:
+        n, k = q.shape
+        return planes["cb"].astype(np.float64)[np.arange(n)[:, None], q]
     raise ValueError
 
 
-@pytest.mark.parametrize("fmt,n,k", [(oracle.Q4_0, 13, 96), (oracle.Q6_K, 7, 512), (oracle.CB4, 9, 384)])
+@pytest.mark.parametrize("fmt,n,k", [(oracle.Q4_0, 13, 96), (oracle.Q6_K, 7, 512), (oracle.CB4, 9, 384),
+                                     (oracle.CB8, 11, 160)])
 @pytest.mark.parametrize("xt", [oracle.F32, oracle.BF16])
 def test_gemv_matches_numpy_matmul(fmt, n, k, xt):
     rng = np.random.default_rng(11)
@@ -212,9 +277,12 @@ def test_gemv_matches_numpy_matmul(fmt, n, k, xt):
         ql, qh = oracle.pack_q6k(q)
         planes = {"ql": ql, "qh": qh, "sc": rng.integers(-128, 128, (n, k // 256, 16)).astype(np.int8),
                   "d": f16(rng.uniform(1e-5, 1e-4, (n, k // 256)))}
-    else:
+    elif fmt == oracle.CB4:
         q = rng.integers(0, 16, (n, k)).astype(np.int32)
         planes = {"idx": oracle.pack_cb4(q), "cb": f16(np.sort(rng.normal(0, 0.02, (n, k // 128, 16)), axis=2))}
+    else:
+        q = rng.integers(0, 256, (n, k)).astype(np.int32)
+        planes = {"idx": q.astype(np.uint8), "cb": f16(np.sort(rng.normal(0, 0.02, (n, 256)), axis=1))}
     m = oracle.Mat(fmt, n, k, planes)
     W = _dense_from_codes(fmt, q, planes)
     assert np.array_equal(oracle.dequant(m), W)
@@ -246,6 +314,41 @@ def test_gemv_exact_rational_tiny():
             wv = s * (Fraction(float(w["cbk"][0, c1, j])) + Fraction(float(w["cbk"][1, c2, j])))
             exact += wv * Fraction(float(xd[c]))
         assert abs(Fraction(y[0, r]) - exact) <= Fraction(1e-14) * Fraction(b[0, r])
+
+
+def test_aq3_gemv_exact_rational_tiny():
+    w = synth.gen_weights(synth.FMT_AQ3X8, 3, 24, seed=4)
+    m = oracle.Mat(oracle.AQ3X8, 3, 24, w)
+    x = synth.gen_x(2, 24, synth.DT_F32, seed=4)
+    y, b = oracle.gemv(m, x, oracle.F32)
+    for bi in range(2):
+        for r in range(3):
+            s = Fraction(float(w["s"][r]))
+            exact = Fraction(0)
+            for c in range(24):
+                g, j = divmod(c, 8)
+                wv = s * sum(Fraction(float(w["cbk"][t, w["codes"][r, g, t], j])) for t in range(3))
+                exact += wv * Fraction(float(x[bi, c]))
+            assert abs(Fraction(y[bi, r]) - exact) <= Fraction(1e-14) * Fraction(b[bi, r])
+
+
+def test_cb8_closed_forms():
+    # one index per row: y = cb[row][v] * sum(x)   ("row-sum times scale"); x = e_j gives column j
+    n, k = 6, 64
+    v = np.array([0, 17, 128, 200, 255, 99])
+    cb = f16(np.sort(np.random.default_rng(3).normal(0, 0.02, (n, 256)), axis=1))
+    m = oracle.Mat(oracle.CB8, n, k, {"idx": np.repeat(v[:, None], k, axis=1).astype(np.uint8), "cb": cb})
+    x = synth.gen_x(1, k, seed=6)
+    y, _ = oracle.gemv(m, x)
+    sx = float(np.sum(x[0].astype(np.float64)))
+    for r in range(n):
+        assert abs(y[0, r] - float(cb[r, v[r]]) * sx) <= 1e-15 * float(np.sum(np.abs(x)))
+    w = synth.gen_weights(synth.FMT_CB8, 5, 48, seed=2)
+    m = oracle.Mat(oracle.CB8, 5, 48, w)
+    for j in (0, 13, 47):
+        e = np.zeros((1, 48), dtype=np.float32)
+        e[0, j] = 1.0
+        assert np.array_equal(oracle.gemv(m, e)[0][0], w["cb"].astype(np.float64)[np.arange(5), w["idx"][:, j]])
 
 
 def test_gemv_closed_forms():
