@@ -11,12 +11,12 @@ import ctypes as C
 import os
 
 __all__ = [
-    "Q4_0", "Q6_K", "CB4", "AQ2X8", "F32", "BF16", "QmvError", "QWeights", "lib", "plane_bytes",
+    "Q4_0", "Q6_K", "CB4", "AQ2X8", "CB8", "AQ3X8", "F32", "BF16", "QmvError", "QWeights", "lib", "plane_bytes",
     "weight_bytes", "validate", "gemv", "dequant", "quant_act", "workspace_bytes", "gemm",
     "gemm_q8", "partials", "moe_ffn", "last_path", "strerror", "PLANES",
 ]
 
-Q4_0, Q6_K, CB4, AQ2X8 = 1, 2, 3, 4
+Q4_0, Q6_K, CB4, AQ2X8, CB8, AQ3X8 = 1, 2, 3, 4, 5, 6
 F32, BF16 = 0, 1
 MAX_BATCH = 8
 
@@ -26,6 +26,8 @@ PLANES = {
     Q6_K: {"ql": "codes", "qh": "codes_hi", "sc": "scales", "d": "super"},
     CB4: {"idx": "codes", "cb": "codebook"},
     AQ2X8: {"codes": "codes", "s": "scales", "cbk": "codebook"},
+    CB8: {"idx": "codes", "cb": "codebook"},
+    AQ3X8: {"codes": "codes", "s": "scales", "cbk": "codebook"},
 }
 _PLANE_ID = {"codes": 0, "codes_hi": 1, "scales": 2, "super": 3, "codebook": 4}
 

@@ -31,6 +31,8 @@ int block_of(int32_t fmt) {
     case QMV_Q6_K: return 256;
     case QMV_CB4: return 128;
     case QMV_AQ2X8: return 8;
+    case QMV_CB8: return 64;
+    case QMV_AQ3X8: return 8;
     }
     return 0;
 }
@@ -97,9 +99,16 @@ int64_t qmv_plane_bytes(int32_t fmt, int64_t n, int64_t k, int32_t plane) {
         if (plane == QMV_PLANE_CODEBOOK) return n * (k / 128) * 32;
         break;
     case QMV_AQ2X8:
-        if (plane == QMV_PLANE_CODES) return n * (k / 8) * 2;
+    case QMV_AQ3X8: {
+        const int nc = fmt == QMV_AQ3X8 ? 3 : 2;
+        if (plane == QMV_PLANE_CODES) return n * (k / 8) * nc;
         if (plane == QMV_PLANE_SCALES) return n * 2;
-        if (plane == QMV_PLANE_CODEBOOK) return 2 * 256 * 8 * 2;
+        if (plane == QMV_PLANE_CODEBOOK) return nc * 256 * 8 * 2;
+        break;
+    }
+    case QMV_CB8:
+        if (plane == QMV_PLANE_CODES) return n * k;
+        if (plane == QMV_PLANE_CODEBOOK) return n * 256 * 2;
         break;
     }
     if (plane < 0 || plane > QMV_PLANE_CODEBOOK) return QMV_ERR_SHAPE;
@@ -128,9 +137,11 @@ int qmv_validate(const qmv_weights *w, int32_t m, int32_t xt) {
     case QMV_Q4_0: need[1] = w->scales; break;
     case QMV_Q6_K: need[1] = w->codes_hi; need[2] = w->scales; need[3] = w->super; break;
     case QMV_CB4: need[1] = w->codebook; break;
-    case QMV_AQ2X8: need[1] = w->scales; need[2] = w->codebook; break;
+    case QMV_AQ2X8:
+    case QMV_AQ3X8: need[1] = w->scales; need[2] = w->codebook; break;
+    case QMV_CB8: need[1] = w->codebook; break;
     }
-    const int nneed = w->fmt == QMV_Q6_K ? 4 : (w->fmt == QMV_AQ2X8 ? 3 : 2);
+    const int nneed = w->fmt == QMV_Q6_K ? 4 : (w->fmt == QMV_AQ2X8 || w->fmt == QMV_AQ3X8 ? 3 : 2);
     for (int i = 0; i < nneed; i++)
         if (!need[i]) return QMV_ERR_NULL;
     for (int i = 0; i < nneed; i++)
@@ -150,7 +161,9 @@ int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *
     case QMV_Q4_0: path = launch_gemv_q4_0(w, m, x, xt, y, s); break;
     case QMV_Q6_K: path = launch_gemv_q6k(w, m, x, xt, y, s); break;
     case QMV_CB4: path = launch_gemv_cb4(w, m, x, xt, y, s); break;
-    case QMV_AQ2X8: path = launch_gemv_aq(w, m, x, xt, y, s); break;
+    case QMV_AQ2X8:
+    case QMV_AQ3X8: path = launch_gemv_aq(w, m, x, xt, y, s); break;
+    case QMV_CB8: path = launch_gemv_cb8(w, m, x, xt, y, s); break;
     }
     if (!path) return QMV_ERR_LIMIT;
     return finish_launch("qmv_gemv", w, m, path);

@@ -69,17 +69,37 @@ __global__ void __launch_bounds__(TB) dq_cb4(const uint8_t *__restrict__ idx, co
         for (int e = 0; e < 8; e++) o[8 * j + e] = h2f(tab[(w[j] >> (4 * e)) & 15]);
 }
 
-// One thread per 8-weight group.
+// One thread per 8-weight group of an NC-codebook additive code: s * ((C1 + C2) + C3).
+template <int NC>
 __global__ void __launch_bounds__(TB) dq_aq(const uint8_t *__restrict__ codes, const uint16_t *__restrict__ cbk,
                                             const uint16_t *__restrict__ srow, float *__restrict__ out,
                                             int64_t ngroups, int64_t groups_per_row) {
     const int64_t i = (int64_t)blockIdx.x * TB + threadIdx.x;
     if (i >= ngroups) return;
-    const int c1 = codes[2 * i], c2 = codes[2 * i + 1];
     const float s = h2f(srow[i / groups_per_row]);
     float *o = out + i * 8;
 #pragma unroll
-    for (int j = 0; j < 8; j++) o[j] = s * (h2f(cbk[c1 * 8 + j]) + h2f(cbk[2048 + c2 * 8 + j]));
+    for (int j = 0; j < 8; j++) {
+        float v = h2f(cbk[codes[NC * i] * 8 + j]);
+#pragma unroll
+        for (int b = 1; b < NC; b++) v += h2f(cbk[2048 * b + codes[NC * i + b] * 8 + j]);
+        o[j] = s * v;
+    }
+}
+
+// One thread per 16 weights (16 index bytes) of the 8-bit codebook format.
+__global__ void __launch_bounds__(TB) dq_cb8(const uint8_t *__restrict__ idx, const uint16_t *__restrict__ cb,
+                                             float *__restrict__ out, int64_t nchunks, int64_t chunks_per_row) {
+    const int64_t i = (int64_t)blockIdx.x * TB + threadIdx.x;
+    if (i >= nchunks) return;
+    const uint4 q = *(const uint4 *)(idx + i * 16);
+    const uint16_t *tab = cb + (i / chunks_per_row) * 256;
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    float *o = out + i * 16;
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[4 * j + e] = h2f(tab[(w[j] >> (8 * e)) & 255]);
 }
 
 int grid_of(int64_t n) { return (int)((n + TB - 1) / TB); }
@@ -104,9 +124,17 @@ const char *launch_dequant(const qmv_weights *w, float *out, hipStream_t s) {
                            (const uint16_t *)w->codebook, out, n * k / 32);
         return "dequant.cb4";
     case QMV_AQ2X8:
-        hipLaunchKernelGGL(dq_aq, dim3(grid_of(n * k / 8)), dim3(TB), 0, s, (const uint8_t *)w->codes,
+        hipLaunchKernelGGL(dq_aq<2>, dim3(grid_of(n * k / 8)), dim3(TB), 0, s, (const uint8_t *)w->codes,
                            (const uint16_t *)w->codebook, (const uint16_t *)w->scales, out, n * k / 8, k / 8);
         return "dequant.aq2x8";
+    case QMV_AQ3X8:
+        hipLaunchKernelGGL(dq_aq<3>, dim3(grid_of(n * k / 8)), dim3(TB), 0, s, (const uint8_t *)w->codes,
+                           (const uint16_t *)w->codebook, (const uint16_t *)w->scales, out, n * k / 8, k / 8);
+        return "dequant.aq3x8";
+    case QMV_CB8:
+        hipLaunchKernelGGL(dq_cb8, dim3(grid_of(n * k / 16)), dim3(TB), 0, s, (const uint8_t *)w->codes,
+                           (const uint16_t *)w->codebook, out, n * k / 16, k / 16);
+        return "dequant.cb8";
     }
     return nullptr;
 }

@@ -1,31 +1,145 @@
-// gemv_aq.hip -- 2-bit two-codebook additive GEMV (batch 1..8) for gfx950.
+// gemv_aq.hip -- additive-code GEMVs (batch 1..8) for gfx950: the 2-bit code (two
+// codebooks) and the 3-bit code (three codebooks).
 //
-// Format ("Chasing x100", "The kernel is ready": a 2-bit additive-code GEMV checked
-// against a bit-faithful CPU reference): each group of 8 consecutive weights of a row
-// stores two 8-bit codes (c1, c2); the group's weights are C1[c1] + C2[c2] (two
-// per-matrix tables of 256 x 8 fp16 entries), times a per-row fp16 scale s[n].
+// Format ("Chasing x100", "The kernel is ready": 2-bit and 3-bit additive-code GEMVs
+// checked against a bit-faithful CPU reference): each group of 8 consecutive weights of
+// a row stores NC 8-bit codes (c1, .., cNC), one byte each; the group's weights are
+// C1[c1] + .. + CNC[cNC] (NC per-matrix tables of 256 x 8 fp16 entries), times a per-row
+// fp16 scale s[n].
 //
-// Kernel:
-//   * both tables (8 KiB) are copied into LDS once per workgroup;
-//   * K is processed in chunks of 4096 activations; each chunk of x is staged into LDS
-//     as fp32 (64 floats per lane unit + 4 of padding, so ds_read_b128 over
-//     consecutive lanes does not collide) before the chunk's code loads are issued;
-//   * lane l owns 16 code bytes (8 groups, 64 weights) of the chunk: one 128-bit load;
-//   * per group two ds_read_b128 fetch C1[c1] and C2[c2]; v_fma_mix_f32 forms each
-//     weight as fl32(C1 + C2) (fp16 halves times 1.0 plus fp16 half), so an exactly
-//     cancelling pair gives 0 and the rounding is relative to |w|; the weight is then
-//     applied to every batch row with an fp32 FMA (decoded once for all rows);
+// Kernel (k % 64 == 0, the streaming skeleton of gemv_stream.h):
+//   * the NC tables (4 KiB each) are copied into LDS once per workgroup;
+//   * lane l owns unit l of each 4096-weight step: 8 groups, NC * 8 code bytes (one
+//     128-bit load for NC = 2, three 64-bit loads for NC = 3), prefetched a step ahead;
+//   * per group, NC ds_read_b128 fetch the table rows; v_fma_mix_f32 forms each weight
+//     in fp32 as fl32(C1 + C2) (+ C3): exact when the entries are below 1/4 in
+//     magnitude (the sum then fits 24 bits), else rounded relative to the partial sum;
+//     an exactly cancelling pair gives 0.  The weight is applied to every batch row with
+//     an fp32 FMA (decoded once for all rows);
 //   * the 64 lane partials are summed with DPP and scaled by s[n].
+// Rows whose length is not a multiple of 64 take a plain kernel (byte loads, one K chunk
+// staged at a time).
 #include "device_common.h"
+#include "gemv_stream.h"
 #include "qmv_internal.h"
 
 namespace qmv {
 namespace {
 
-constexpr int WG = 512;
-constexpr int WAVES = WG / 64;
-constexpr int KC = 4096;   // activations per chunk: 64 lanes x 64 weights
-constexpr int XU = 68;     // floats per staged 64-activation lane unit
+using stream::WG;
+using stream::WAVES;
+using stream::XU;
+
+// Table rows of codebook b at LDS byte address tab + b * 4096 + 16 * code.
+template <int NC>
+struct AqPolicy {
+    struct Codes {
+        uint32_t w[2 * NC];  // byte NC * g + b = code b of group g
+    };
+    const uint8_t *crow;  // this row's codes
+    uint32_t tab;         // LDS byte address of the tables
+
+    __device__ __forceinline__ void load(Codes &c, int unit) const {
+        const uint8_t *p = crow + (int64_t)unit * (8 * NC);
+        if (NC == 2) {
+            const uint4 v = ld_stream16(p);
+            c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < NC; i++) {
+                const u32x2 v = __builtin_nontemporal_load((const u32x2 *)(p + 8 * i));
+                c.w[2 * i] = v.x;
+                c.w[2 * i + 1] = v.y;
+            }
+        }
+    }
+
+    template <int M>
+    __device__ __forceinline__ void dot(const Codes &c, const float *xu, float (&s)[M]) const {
+#pragma unroll
+        for (int g = 0; g < 8; g++) {
+            uint32_t row[NC];
+#pragma unroll
+            for (int b = 0; b < NC; b++) {
+                const int bi = NC * g + b;
+                row[b] = tab + b * 4096 + (((c.w[bi >> 2] >> (8 * (bi & 3))) & 0xFFu) << 4);
+            }
+            const uint4 a = lds_ld16(row[0]), b = lds_ld16(row[1]);
+            const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+            float wv[8];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                wv[2 * j] = fmaf(lo_h(av[j]), 1.0f, lo_h(bv[j]));
+                wv[2 * j + 1] = fmaf(hi_h(av[j]), 1.0f, hi_h(bv[j]));
+            }
+            if (NC == 3) {
+                const uint4 t = lds_ld16(row[NC - 1]);
+                const uint32_t tv[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    wv[2 * j] = fmaf(lo_h(tv[j]), 1.0f, wv[2 * j]);
+                    wv[2 * j + 1] = fmaf(hi_h(tv[j]), 1.0f, wv[2 * j + 1]);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const float *xg = xu + m * stream::XBUF + 8 * g;
+                const float4 x0 = *(const float4 *)xg, x1 = *(const float4 *)(xg + 4);
+                float t = s[m];
+                t = fmaf(wv[0], x0.x, t);
+                t = fmaf(wv[1], x0.y, t);
+                t = fmaf(wv[2], x0.z, t);
+                t = fmaf(wv[3], x0.w, t);
+                t = fmaf(wv[4], x1.x, t);
+                t = fmaf(wv[5], x1.y, t);
+                t = fmaf(wv[6], x1.z, t);
+                t = fmaf(wv[7], x1.w, t);
+                s[m] = t;
+            }
+        }
+    }
+};
+
+// LDS layout: the activation buffers (xfloats floats), then the NC tables.
+template <int NC, int M, int XT>
+__global__ void __launch_bounds__(WG) aq_stream_kernel(const uint8_t *__restrict__ codes,
+                                                       const uint16_t *__restrict__ cbk,
+                                                       const uint16_t *__restrict__ srow,
+                                                       const void *__restrict__ x, float *__restrict__ y,
+                                                       int n, int k, int xfloats) {
+    extern __shared__ float4 lds4[];
+    float *sx = (float *)lds4;
+    uint4 *tab = (uint4 *)(sx + xfloats);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * WAVES + wave;
+    const int rowc = row < n ? row : n - 1;
+
+    // NC * 256 table rows of 16 bytes; threads past the end rewrite the last row
+    const uint4 *src = (const uint4 *)cbk;
+#pragma unroll
+    for (int i = 0; i < (NC * 256 + WG - 1) / WG; i++) {
+        const int e = threadIdx.x + i * WG;
+        const int ec = e < NC * 256 ? e : NC * 256 - 1;
+        tab[ec] = src[ec];
+    }
+
+    AqPolicy<NC> pol{codes + (int64_t)rowc * (k >> 3) * NC, (uint32_t)(uintptr_t)tab};
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; m++) acc[m] = 0.f;
+    stream::walk_row<AqPolicy<NC>, M, XT>(pol, x, k, sx, acc);
+
+    const float s = h2f(srow[rowc]);
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        const float t = wave_sum(acc[m]);
+        if (lane == 0 && row < n) y[(int64_t)m * n + row] = s * t;
+    }
+}
+
+// ---- rows whose length is not a multiple of 64: one K chunk of 4096 staged at a time,
+// code bytes read one by one.
+constexpr int KC = 4096;
 
 template <int M, int XT>
 __device__ void stage_chunk(const void *x, int k, int k0, int kc, float *sx) {
@@ -36,75 +150,59 @@ __device__ void stage_chunk(const void *x, int k, int k0, int kc, float *sx) {
     }
 }
 
-// The lane's code bytes for `ng` groups at p: one 128-bit load when all 8 groups are
-// present and p is 16-byte aligned (k % 64 == 0), else byte loads (ragged rows / tails).
-QMV_DEV uint4 load_codes(const uint8_t *p, int ng) {
-    if (ng == 8 && ((uintptr_t)p & 15) == 0) return ld_stream16(p);
-    uint32_t v[4] = {0, 0, 0, 0};
-    for (int i = 0; i < 2 * ng; i++) v[i >> 2] |= (uint32_t)p[i] << (8 * (i & 3));
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-template <int M, int XT>
-__global__ void __launch_bounds__(WG) gemv_aq_kernel(const uint8_t *__restrict__ codes,
-                                                     const uint16_t *__restrict__ cbk,
-                                                     const uint16_t *__restrict__ srow,
-                                                     const void *__restrict__ x, float *__restrict__ y,
-                                                     int n, int k) {
+template <int NC, int M, int XT>
+__global__ void __launch_bounds__(WG) aq_ragged_kernel(const uint8_t *__restrict__ codes,
+                                                       const uint16_t *__restrict__ cbk,
+                                                       const uint16_t *__restrict__ srow,
+                                                       const void *__restrict__ x, float *__restrict__ y,
+                                                       int n, int k) {
     extern __shared__ float lds[];
-    uint32_t *tab = (uint32_t *)lds;  // C1 then C2: 2 x 256 entries x 4 dwords
-    float *sx = lds + 2048;
+    uint4 *tab = (uint4 *)lds;  // NC tables of 256 rows
+    float *sx = lds + NC * 1024;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x * WAVES + wave;
     const uint32_t tab_addr = (uint32_t)(uintptr_t)tab;
 
-    for (int i = threadIdx.x; i < 512; i += WG) ((uint4 *)tab)[i] = ((const uint4 *)cbk)[i];
+    for (int i = threadIdx.x; i < NC * 256; i += WG) tab[i] = ((const uint4 *)cbk)[i];
 
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; m++) acc[m] = 0.f;
-    const uint8_t *crow = codes + (int64_t)row * (k >> 2);
+    const uint8_t *crow = codes + (int64_t)row * (k >> 3) * NC;
 
     for (int k0 = 0; k0 < k; k0 += KC) {
         const int kc = min(KC, k - k0);
         if (k0) __syncthreads();  // previous chunk fully consumed
         stage_chunk<M, XT>(x, k, k0, kc, sx);
-        const int e0 = lane * 64;  // first weight of this lane's unit within the chunk
-        const bool mine = row < n && e0 < kc;
-        const int ng = mine ? min(8, (kc - e0) >> 3) : 0;
-        const uint4 cq = mine ? load_codes(crow + ((k0 + e0) >> 2), ng) : make_uint4(0, 0, 0, 0);
         __syncthreads();
-        if (mine) {
-            const uint32_t cw[4] = {cq.x, cq.y, cq.z, cq.w};
+        const int e0 = lane * 64;  // first weight of this lane's unit within the chunk
+        if (row < n && e0 < kc) {
+            const int ng = min(8, (kc - e0) >> 3);
+            const uint8_t *cp = crow + (int64_t)((k0 + e0) >> 3) * NC;
+            for (int g = 0; g < ng; g++) {
+                float wv[8];
+                const uint4 a = lds_ld16(tab_addr + (cp[NC * g] << 4));
+                const uint4 b = lds_ld16(tab_addr + 4096 + (cp[NC * g + 1] << 4));
+                const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int g = 0; g < 8; g++) {
-                if (g < ng) {
-                    const uint32_t word = cw[g >> 1];
-                    const uint32_t c1 = (word >> (16 * (g & 1))) & 0xFF, c2 = (word >> (16 * (g & 1) + 8)) & 0xFF;
-                    const uint4 a = lds_ld16(tab_addr + (c1 << 4));
-                    const uint4 b = lds_ld16(tab_addr + 4096 + (c2 << 4));
-                    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-                    float wv[8];
+                for (int j = 0; j < 4; j++) {
+                    wv[2 * j] = fmaf(lo_h(av[j]), 1.0f, lo_h(bv[j]));
+                    wv[2 * j + 1] = fmaf(hi_h(av[j]), 1.0f, hi_h(bv[j]));
+                }
+                if (NC == 3) {
+                    const uint4 t = lds_ld16(tab_addr + 8192 + (cp[NC * g + NC - 1] << 4));
+                    const uint32_t tv[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
-                        wv[2 * j] = fmaf(lo_h(av[j]), 1.0f, lo_h(bv[j]));
-                        wv[2 * j + 1] = fmaf(hi_h(av[j]), 1.0f, hi_h(bv[j]));
+                        wv[2 * j] = fmaf(lo_h(tv[j]), 1.0f, wv[2 * j]);
+                        wv[2 * j + 1] = fmaf(hi_h(tv[j]), 1.0f, wv[2 * j + 1]);
                     }
+                }
 #pragma unroll
-                    for (int m = 0; m < M; m++) {
-                        const float *xg = sx + (m * 64 + lane) * XU + 8 * g;
-                        const float4 x0 = *(const float4 *)xg, x1 = *(const float4 *)(xg + 4);
-                        float t = acc[m];
-                        t = fmaf(wv[0], x0.x, t);
-                        t = fmaf(wv[1], x0.y, t);
-                        t = fmaf(wv[2], x0.z, t);
-                        t = fmaf(wv[3], x0.w, t);
-                        t = fmaf(wv[4], x1.x, t);
-                        t = fmaf(wv[5], x1.y, t);
-                        t = fmaf(wv[6], x1.z, t);
-                        t = fmaf(wv[7], x1.w, t);
-                        acc[m] = t;
-                    }
+                for (int m = 0; m < M; m++) {
+                    const float *xg = sx + (m * 64 + lane) * XU + 8 * g;
+#pragma unroll
+                    for (int j = 0; j < 8; j++) acc[m] = fmaf(wv[j], xg[j], acc[m]);
                 }
             }
         }
@@ -117,26 +215,35 @@ __global__ void __launch_bounds__(WG) gemv_aq_kernel(const uint8_t *__restrict__
     }
 }
 
-template <int M, int XT>
+size_t stream_lds(int nc, int m, int64_t k) { return stream::x_lds_bytes(m, k) + (size_t)nc * 4096; }
+size_t ragged_lds(int nc, int m) { return (size_t)nc * 4096 + (size_t)m * 64 * XU * 4; }
+
+template <int NC, int M, int XT>
 void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     const int n = (int)w->n, k = (int)w->k;
-    const size_t lds = 2048 * 4 + (size_t)M * 64 * XU * 4;
-    hipLaunchKernelGGL((gemv_aq_kernel<M, XT>), dim3((n + WAVES - 1) / WAVES), dim3(WG), lds, s,
-                       (const uint8_t *)w->codes, (const uint16_t *)w->codebook, (const uint16_t *)w->scales,
-                       x, y, n, k);
+    const dim3 grid((n + WAVES - 1) / WAVES);
+    if (k % 64 == 0) {
+        hipLaunchKernelGGL((aq_stream_kernel<NC, M, XT>), grid, dim3(WG), stream_lds(NC, M, k), s,
+                           (const uint8_t *)w->codes, (const uint16_t *)w->codebook,
+                           (const uint16_t *)w->scales, x, y, n, k, (int)(stream::x_lds_bytes(M, k) / 4));
+    } else {
+        hipLaunchKernelGGL((aq_ragged_kernel<NC, M, XT>), grid, dim3(WG), ragged_lds(NC, M), s,
+                           (const uint8_t *)w->codes, (const uint16_t *)w->codebook,
+                           (const uint16_t *)w->scales, x, y, n, k);
+    }
 }
 
-template <int XT>
+template <int NC, int XT>
 bool dispatch_m(int m, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     switch (m) {
-    case 1: launch<1, XT>(w, x, y, s); return true;
-    case 2: launch<2, XT>(w, x, y, s); return true;
-    case 3: launch<3, XT>(w, x, y, s); return true;
-    case 4: launch<4, XT>(w, x, y, s); return true;
-    case 5: launch<5, XT>(w, x, y, s); return true;
-    case 6: launch<6, XT>(w, x, y, s); return true;
-    case 7: launch<7, XT>(w, x, y, s); return true;
-    case 8: launch<8, XT>(w, x, y, s); return true;
+    case 1: launch<NC, 1, XT>(w, x, y, s); return true;
+    case 2: launch<NC, 2, XT>(w, x, y, s); return true;
+    case 3: launch<NC, 3, XT>(w, x, y, s); return true;
+    case 4: launch<NC, 4, XT>(w, x, y, s); return true;
+    case 5: launch<NC, 5, XT>(w, x, y, s); return true;
+    case 6: launch<NC, 6, XT>(w, x, y, s); return true;
+    case 7: launch<NC, 7, XT>(w, x, y, s); return true;
+    case 8: launch<NC, 8, XT>(w, x, y, s); return true;
     }
     return false;
 }
@@ -145,10 +252,18 @@ bool dispatch_m(int m, const qmv_weights *w, const void *x, float *y, hipStream_
 
 const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, float *y, hipStream_t s) {
     if (w->n > INT32_MAX || w->k > INT32_MAX / 8) return nullptr;
-    const size_t lds = 2048 * 4 + (size_t)m * 64 * XU * 4;
+    const int nc = w->fmt == QMV_AQ3X8 ? 3 : 2;
+    const bool str = w->k % 64 == 0;
+    const size_t lds = str ? stream_lds(nc, m, w->k) : ragged_lds(nc, m);
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
-    const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, w, x, y, s) : dispatch_m<1>(m, w, x, y, s);
-    return ok ? "aq2x8.lds-codebook.fma-mix" : nullptr;
+    bool ok;
+    if (nc == 2)
+        ok = xt == QMV_F32 ? dispatch_m<2, 0>(m, w, x, y, s) : dispatch_m<2, 1>(m, w, x, y, s);
+    else
+        ok = xt == QMV_F32 ? dispatch_m<3, 0>(m, w, x, y, s) : dispatch_m<3, 1>(m, w, x, y, s);
+    if (!ok) return nullptr;
+    if (nc == 2) return str ? "aq2x8.stream.lds-codebook.fma-mix" : "aq2x8.ragged.lds-codebook.fma-mix";
+    return str ? "aq3x8.stream.lds-codebook.fma-mix" : "aq3x8.ragged.lds-codebook.fma-mix";
 }
 
 }  // namespace qmv

@@ -32,6 +32,8 @@ const char *launch_gemv_cb4(const qmv_weights *w, int m, const void *x, int xt, 
                             hipStream_t s);
 const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, float *y,
                            hipStream_t s);
+const char *launch_gemv_cb8(const qmv_weights *w, int m, const void *x, int xt, float *y,
+                            hipStream_t s);
 const char *launch_dequant(const qmv_weights *w, float *out, hipStream_t s);
 const char *launch_quant_act(const float *x, int m, int64_t k, int8_t *xq, float *xs, hipStream_t s);
 const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *xq, const float *xs, float *y,

@@ -9,8 +9,9 @@
  *   - the q6_K prefill GEMM, an int8 contraction of expanded q6_K weights
  *     against per-32 int8 quantized activations ("57 · r54 —
  *     MINFER_MMQ_Q6K_EXP", §2.1 and §2.3);
- *   - the 4-bit 16-entry codebook and 2-bit additive formats ("Chasing x100",
- *     "The kernel is ready" and the quality table).
+ *   - the 4-bit 16-entry and 8-bit 256-entry codebook formats and the 2-bit and
+ *     3-bit additive formats ("Chasing x100", "The kernel is ready" and the
+ *     quality table).
  *
  * Conventions for every call:
  *   - All data pointers are DEVICE pointers unless a comment says otherwise.
@@ -42,8 +43,10 @@ enum {
     QMV_Q6_K = 2,  /* 256 per super-block: ql 128 B, qh 64 B, 16 int8 sc, fp16 d;
                       w = d*sc[e/16]*(q-32), q = low nibble | 2 high bits << 4                  */
     QMV_CB4 = 3,   /* 4-bit index into a 16-entry fp16 codebook per 128 weights along k         */
-    QMV_AQ2X8 = 4  /* per 8 weights two 8-bit codes into two 256x8 fp16 codebooks, summed,
+    QMV_AQ2X8 = 4, /* per 8 weights two 8-bit codes into two 256x8 fp16 codebooks, summed,
                       times an fp16 per-row scale                                               */
+    QMV_CB8 = 5,   /* 8-bit index into a 256-entry fp16 codebook per output row; k % 64 == 0   */
+    QMV_AQ3X8 = 6  /* as AQ2X8 with three codes and three codebooks per 8 weights              */
 };
 
 /* Activation element types. */
@@ -73,6 +76,8 @@ enum {
  *   Q6_K       ql u8[n][k/256][128]     qh u8[n][k/256][64] sc i8[n][k/256][16]  d f16[n][k/256]  NULL
  *   CB4        idx u8[n][k/2]           NULL                NULL                 NULL             cb f16[n][k/128][16]
  *   AQ2X8      codes u8[n][k/8][2]      NULL                s f16[n]             NULL             cbk f16[2][256][8]
+ *   CB8        idx u8[n][k]             NULL                NULL                 NULL             cb f16[n][256]
+ *   AQ3X8      codes u8[n][k/8][3]      NULL                s f16[n]             NULL             cbk f16[3][256][8]
  *
  * Element order inside the packed planes:
  *   Q4_0 : code byte j of a block holds weight j (bits 0-3) and weight j+16 (bits 4-7).
@@ -82,6 +87,8 @@ enum {
  *   CB4  : index byte i holds index 2i (bits 0-3) and index 2i+1 (bits 4-7).
  *   AQ2X8: group g of row n stores c1 then c2; weight 8g+j = s[n]*(C1[c1][j]+C2[c2][j]),
  *          C1 = cbk[0], C2 = cbk[1].
+ *   CB8  : index byte j of row n holds weight j; weight = cb[n][idx].
+ *   AQ3X8: group g stores c1, c2, c3; weight 8g+j = s[n]*(C1[c1][j]+C2[c2][j]+C3[c3][j]).
  * The same matrix stored as raw blocks (18 B per q4_0 block, 210 B per q6_K super-block)
  * has exactly the same bytes; these planes are that array split by field so that every
  * field can be read with aligned 128-bit loads.
@@ -127,9 +134,11 @@ int qmv_validate(const qmv_weights *w, int32_t m, int32_t xt);
 int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *y, void *stream);
 
 /*
- * Dequantize W to dense fp32 out[n][k] (device).  Every q4_0, q6_K and CB4
- * weight is exactly representable in fp32 and is written exactly; AQ2X8 weights
- * are s*(C1+C2) rounded once to fp32.  Used to check the unpack stage alone.
+ * Dequantize W to dense fp32 out[n][k] (device).  Every q4_0, q6_K, CB4 and CB8
+ * weight is exactly representable in fp32 and is written exactly; additive-code
+ * weights are s times the fp32 sum of the codebook entries (exact when the entries
+ * are below 1/4 in magnitude), rounded once more by the product.  Used to check the
+ * unpack stage alone.
  */
 int qmv_dequant(const qmv_weights *w, float *out, void *stream);
 

@@ -4,7 +4,8 @@ import numpy as np
 import synth
 
 PLANES = {synth.FMT_Q4_0: ("qs", "d"), synth.FMT_Q6_K: ("ql", "qh", "sc", "d"),
-          synth.FMT_CB4: ("idx", "cb"), synth.FMT_AQ2X8: ("codes", "cbk", "s")}
+          synth.FMT_CB4: ("idx", "cb"), synth.FMT_AQ2X8: ("codes", "cbk", "s"),
+          synth.FMT_CB8: ("idx", "cb"), synth.FMT_AQ3X8: ("codes", "cbk", "s")}
 
 # Per-element bound on |y_gpu - y_ref|, relative to sum_k |w||x| (the stated float tolerance).
 REL_TOL = 2e-3

@@ -40,6 +40,13 @@ def test_plane_bytes_match_the_format_definitions():
     # 2-bit additive: 2 bytes per 8 weights + 2 B per row + 8 KiB of codebooks
     assert qmv.plane_bytes(qmv.AQ2X8, 14336, 4096, "codes") == 14680064
     assert qmv.weight_bytes(qmv.AQ2X8, 14336, 4096) == 14680064 + 2 * 14336 + 8192
+    # 8-bit codebook: one byte per weight + 512 B of codebook per row
+    assert qmv.weight_bytes(qmv.CB8, 2048, 7168) == 2048 * 7168 + 2048 * 512
+    assert qmv.plane_bytes(qmv.CB8, 3, 64, "codes") == 192
+    # 3-bit additive: 3 bytes per 8 weights + 2 B per row + 12 KiB of codebooks
+    assert qmv.plane_bytes(qmv.AQ3X8, 14336, 4096, "codes") == 14336 * 512 * 3
+    assert qmv.weight_bytes(qmv.AQ3X8, 14336, 4096) == 14336 * 512 * 3 + 2 * 14336 + 12288
+    assert qmv.weight_bytes(qmv.CB8, 4, 96) == -2              # k not a multiple of 64
     assert qmv.plane_bytes(qmv.Q4_0, 4, 32, "codebook") == 0
     assert qmv.weight_bytes(qmv.Q6_K, 4, 100) == -2
     assert qmv.weight_bytes(9, 4, 256) == -3
@@ -52,7 +59,8 @@ def _fake(fmt, n, k, **over):
     return qmv.QWeights(fmt, n, k, planes)
 
 
-@pytest.mark.parametrize("fmt,k", [(qmv.Q4_0, 64), (qmv.Q6_K, 512), (qmv.CB4, 256), (qmv.AQ2X8, 16)])
+@pytest.mark.parametrize("fmt,k", [(qmv.Q4_0, 64), (qmv.Q6_K, 512), (qmv.CB4, 256), (qmv.AQ2X8, 16),
+                                   (qmv.CB8, 128), (qmv.AQ3X8, 24)])
 def test_validate_accepts_well_formed_descriptors(fmt, k):
     assert qmv.validate(_fake(fmt, 8, k), 1, qmv.F32) == 0
     assert qmv.validate(_fake(fmt, 8, k), 8, qmv.BF16) == 0
@@ -70,6 +78,9 @@ def test_validate_error_codes():
     assert qmv.validate(_fake(qmv.Q4_0, 8, 64), 1, 5) == -4
     assert qmv.validate(_fake(qmv.Q4_0, 8, 64, d=(1 << 20) + 8)) == -5
     assert qmv.validate(_fake(qmv.Q6_K, 8, 256, qh=0)) == -1
+    assert qmv.validate(_fake(qmv.CB8, 8, 128, cb=0)) == -1
+    assert qmv.validate(_fake(qmv.AQ3X8, 8, 24, s=0)) == -1
+    assert qmv.validate(_fake(qmv.AQ3X8, 8, 20)) == -2         # k not a multiple of 8
     assert qmv.validate(_fake(qmv.Q4_0, 8, 64), 0) == -6
     assert qmv.validate(_fake(qmv.Q4_0, 8, 64), 9) == -6
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):

@@ -310,12 +310,18 @@ def test_cb4_unit_vector_returns_codebook_entry_exactly(qmv):
 
 # ------------------------------------------------------------- 2-bit additive
 
-AQ_SMALL = [(1, 8), (5, 24), (9, 64), (33, 1000), (64, 4096), (17, 4096 + 8), (40, 14336)]
+AQ_SMALL = [(1, 8), (5, 24), (9, 64), (33, 1000), (64, 4096), (17, 4096 + 8), (40, 14336), (7, 12288),
+            (5, 4160), (3, 8192 + 192)]
+
+
+def aq_path(fmt, k):
+    name = "aq2x8" if fmt == synth.FMT_AQ2X8 else "aq3x8"
+    return f"{name}.stream.lds-codebook.fma-mix" if k % 64 == 0 else f"{name}.ragged.lds-codebook.fma-mix"
 
 
 @pytest.mark.parametrize("n,k", AQ_SMALL)
 def test_aq_small_full_parity(qmv, n, k):
-    run_case(qmv, synth.FMT_AQ2X8, n, k, 1, synth.DT_BF16, seed=n + k, expect_path="aq2x8.lds-codebook.fma-mix")
+    run_case(qmv, synth.FMT_AQ2X8, n, k, 1, synth.DT_BF16, seed=n + k, expect_path=aq_path(synth.FMT_AQ2X8, k))
 
 
 @pytest.mark.parametrize("m", [1, 4])
@@ -352,3 +358,98 @@ def test_aq_single_codebook_vq_case(qmv):
     torch.cuda.synchronize()
     yr, b = oracle.gemv(oracle.Mat(synth.FMT_AQ2X8, n, k, w), x, oracle.BF16)
     assert_parity(y.cpu().numpy(), yr, b, "aq vq")
+
+
+@pytest.mark.parametrize("m,xt", [(5, synth.DT_BF16), (8, synth.DT_F32)])
+def test_aq_batched_multi_step(qmv, m, xt):
+    # more than four batch rows: one activation buffer, two barriers per step; 3 steps
+    run_case(qmv, synth.FMT_AQ2X8, 19, 12288, m, xt, seed=m + 31, expect_path=aq_path(synth.FMT_AQ2X8, 12288))
+
+
+# ------------------------------------------------------------- 3-bit additive
+
+@pytest.mark.parametrize("n,k", AQ_SMALL)
+def test_aq3_small_full_parity(qmv, n, k):
+    run_case(qmv, synth.FMT_AQ3X8, n, k, 1, synth.DT_BF16, seed=n + k + 1, expect_path=aq_path(synth.FMT_AQ3X8, k))
+
+
+@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("n,k", [(14336, 4096), (4096, 14336)])
+def test_aq3_config_shapes_sampled(qmv, m, n, k):
+    run_case(qmv, synth.FMT_AQ3X8, n, k, m, synth.DT_BF16, seed=0, rows=sample_rows(n))
+
+
+@pytest.mark.parametrize("m,xt,k", [(2, synth.DT_F32, 2048), (3, synth.DT_BF16, 8192 + 64), (6, synth.DT_F32, 12288),
+                                    (8, synth.DT_BF16, 4096), (4, synth.DT_F32, 1000)])
+def test_aq3_batched(qmv, m, xt, k):
+    run_case(qmv, synth.FMT_AQ3X8, 37, k, m, xt, seed=m + 13, expect_path=aq_path(synth.FMT_AQ3X8, k))
+
+
+def test_aq3_cancelling_codebooks_give_zero(qmv):
+    # C2 = -C1 and C3 = 0: every weight is exactly 0 when c1 == c2
+    import torch
+    n, k = 24, 8192
+    w = synth.gen_weights(synth.FMT_AQ3X8, n, k, seed=5)
+    w["cbk"][1] = -w["cbk"][0]
+    w["cbk"][2] = 0
+    w["codes"][:, :, 1] = w["codes"][:, :, 0]
+    y = qmv.gemv(qweights(synth.FMT_AQ3X8, n, k, w), x_to_device(synth.gen_x(2, k, synth.DT_BF16, seed=5), synth.DT_BF16))
+    torch.cuda.synchronize()
+    assert np.all(y.cpu().numpy() == 0.0)
+
+
+def test_aq3_with_zero_third_codebook_matches_two_codebook_kernel(qmv):
+    # C3 = 0: the 3-book kernel on (c1, c2, c3) and the 2-book kernel on (c1, c2) compute
+    # the same weights; both are held to the oracle and to each other within the bound
+    import torch
+    n, k = 40, 4096 * 2
+    w3 = synth.gen_weights(synth.FMT_AQ3X8, n, k, seed=9)
+    w3["cbk"][2] = 0
+    w2 = {"codes": np.ascontiguousarray(w3["codes"][:, :, :2]), "cbk": np.ascontiguousarray(w3["cbk"][:2]),
+          "s": w3["s"]}
+    x = synth.gen_x(1, k, synth.DT_F32, seed=9)
+    y3 = qmv.gemv(qweights(synth.FMT_AQ3X8, n, k, w3), x_to_device(x, synth.DT_F32))
+    y2 = qmv.gemv(qweights(synth.FMT_AQ2X8, n, k, w2), x_to_device(x, synth.DT_F32))
+    torch.cuda.synchronize()
+    yr, b = oracle.gemv(oracle.Mat(synth.FMT_AQ3X8, n, k, w3), x, oracle.F32)
+    assert_parity(y3.cpu().numpy(), yr, b, "aq3 c3=0")
+    assert_parity(y2.cpu().numpy(), yr, b, "aq2 same weights")
+
+
+# ------------------------------------------------------------- 8-bit codebook
+
+CB8_SMALL = [(1, 64), (9, 192), (33, 4096), (17, 4160), (5, 12288), (40, 7168), (3, 16384 + 64)]
+
+
+@pytest.mark.parametrize("n,k", CB8_SMALL)
+@pytest.mark.parametrize("xt", [synth.DT_BF16, synth.DT_F32])
+def test_cb8_small_full_parity(qmv, n, k, xt):
+    run_case(qmv, synth.FMT_CB8, n, k, 1, xt, seed=n + k, expect_path="cb8.stream.lds-table.fma-mix")
+
+
+@pytest.mark.parametrize("m,xt,k", [(2, synth.DT_BF16, 2048), (3, synth.DT_F32, 7168), (4, synth.DT_BF16, 12288),
+                                    (5, synth.DT_F32, 4160), (8, synth.DT_BF16, 7168)])
+def test_cb8_batched(qmv, m, xt, k):
+    run_case(qmv, synth.FMT_CB8, 29, k, m, xt, seed=m + 17, expect_path="cb8.stream.lds-table.fma-mix")
+
+
+@pytest.mark.parametrize("n,k", [(2048, 7168), (7168, 2048), (129280, 7168)])
+def test_cb8_shared_expert_and_head_shapes_sampled(qmv, n, k):
+    # the shared expert's gate/up and down, and the output head, at their full sizes
+    run_case(qmv, synth.FMT_CB8, n, k, 1, synth.DT_BF16, seed=0, rows=sample_rows(n))
+
+
+def test_cb8_unit_vector_returns_codebook_entry_exactly(qmv):
+    import torch
+    n, k, m = 45, 8192 + 128, 6
+    w = synth.gen_weights(synth.FMT_CB8, n, k, seed=21)
+    dense = oracle.dequant(oracle.Mat(synth.FMT_CB8, n, k, w)).astype(np.float32)
+    cols = (0, 63, 4095, 4096, 8191, 8319)  # unit and step edges, the ragged last step
+    e = np.zeros((m, k), dtype=np.float32)
+    for r, j in enumerate(cols):
+        e[r, j] = 1.0
+    y = qmv.gemv(qweights(synth.FMT_CB8, n, k, w), x_to_device(e, synth.DT_F32))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    for r, j in enumerate(cols):
+        assert np.array_equal(y[r], dense[:, j]), j

@@ -21,7 +21,8 @@ def qmv():
 
 
 @pytest.mark.parametrize("fmt,n,k", [(synth.FMT_Q4_0, 33, 4096), (synth.FMT_Q6_K, 17, 2048),
-                                     (synth.FMT_CB4, 19, 1024), (synth.FMT_Q6_K, 256, 1024)])
+                                     (synth.FMT_CB4, 19, 1024), (synth.FMT_Q6_K, 256, 1024),
+                                     (synth.FMT_CB8, 21, 640)])
 def test_dequant_bit_exact(qmv, fmt, n, k):
     import torch
     w = synth.gen_weights(fmt, n, k, seed=n)
@@ -30,7 +31,7 @@ def test_dequant_bit_exact(qmv, fmt, n, k):
     assert qmv.last_path().startswith("dequant.")
     ref = oracle.dequant(oracle.Mat(fmt, n, k, w))
     assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
-    if fmt != synth.FMT_CB4:
+    if fmt in (synth.FMT_Q4_0, synth.FMT_Q6_K):
         codes = oracle.codes(oracle.Mat(fmt, n, k, w))
         assert codes.min() >= 0 and codes.max() <= (15 if fmt == synth.FMT_Q4_0 else 63)
 
@@ -47,6 +48,20 @@ def test_dequant_aq_within_two_roundings(qmv):
     mag = s * (np.abs(w["cbk"][0][w["codes"][:, :, 0]].astype(np.float64)) +
                np.abs(w["cbk"][1][w["codes"][:, :, 1]].astype(np.float64))).reshape(n, k)
     assert np.all(np.abs(out - ref) <= 2.0 ** -23 * (mag + np.abs(ref)))
+
+
+def test_dequant_aq3_within_three_roundings(qmv):
+    import torch
+    n, k = 23, 512
+    w = synth.gen_weights(synth.FMT_AQ3X8, n, k, seed=4)
+    out = qmv.dequant(qweights(synth.FMT_AQ3X8, n, k, w)).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    assert qmv.last_path() == "dequant.aq3x8"
+    ref = oracle.dequant(oracle.Mat(synth.FMT_AQ3X8, n, k, w))
+    # s*((C1+C2)+C3): two roundings of the sums, one of the product (each <= 2^-24 relative)
+    s = w["s"].astype(np.float64)[:, None]
+    mag = s * sum(np.abs(w["cbk"][b][w["codes"][:, :, b]].astype(np.float64)) for b in range(3)).reshape(n, k)
+    assert np.all(np.abs(out - ref) <= 3 * 2.0 ** -24 * (mag + np.abs(ref)))
 
 
 def _quant_gpu(qmv, x):

@@ -343,10 +343,10 @@ def test_cb8_closed_forms():
     sx = float(np.sum(x[0].astype(np.float64)))
     for r in range(n):
         assert abs(y[0, r] - float(cb[r, v[r]]) * sx) <= 1e-15 * float(np.sum(np.abs(x)))
-    w = synth.gen_weights(synth.FMT_CB8, 5, 48, seed=2)
-    m = oracle.Mat(oracle.CB8, 5, 48, w)
-    for j in (0, 13, 47):
-        e = np.zeros((1, 48), dtype=np.float32)
+    w = synth.gen_weights(synth.FMT_CB8, 5, 64, seed=2)
+    m = oracle.Mat(oracle.CB8, 5, 64, w)
+    for j in (0, 13, 63):
+        e = np.zeros((1, 64), dtype=np.float32)
         e[0, j] = 1.0
         assert np.array_equal(oracle.gemv(m, e)[0][0], w["cb"].astype(np.float64)[np.arange(5), w["idx"][:, j]])
 
