@@ -11,7 +11,8 @@ Prints ONE JSON line: value = algorithmic bytes (packed weights + scales + x + y
 per step / time per step, in GB/s.  `roofline` covers the dominant kernel, timed
 with HIP events on the stream it runs on; `cpu_baseline` times the CPU oracle on
 a bounded sample of the same workload.  `secondary` carries the other workloads
-(q6_K GEMV, codebook MoE, additive GEMV, q6_K prefill GEMM) when they run.
+(q6_K GEMV, 4-bit codebook MoE, 2-bit and 3-bit additive GEMVs, 8-bit codebook GEMV,
+q6_K prefill GEMM) when they run.
 """
 from __future__ import annotations
 
@@ -45,7 +46,7 @@ def parse():
     ap.add_argument("--only-primary", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--secondary", default="q6_K_gemv,cb4_moe,aq2x8,q6_K_gemm",
+    ap.add_argument("--secondary", default="q6_K_gemv,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm",
                     help="comma-separated secondary workloads to run")
     return ap.parse_args()
 
@@ -182,11 +183,18 @@ def gemv_workload(qmv, fmt, shapes, batch, xt, steps, label):
 
     g = graph_of(step, steps)
     ms = time_graph(g, steps)
-    qmv.gemv(mats[0][0], xs[0], ys[0])
+    per_shape = []
+    for s, (n, k) in enumerate(shapes):
+        R = max(steps, 40)
+        avg = time_graph(graph_of(lambda i, s=s: qmv.gemv(mats[s][i % copies], xs[s], ys[s]), R), R)
+        qmv.gemv(mats[s][0], xs[s], ys[s])
+        per_shape.append({"shape": f"{n}x{k}", "bytes": algo[s], "avg_launch_ms": round(avg, 5),
+                          "GBps": round(algo[s] / avg / 1e6, 1), "path": qmv.last_path()})
     gbs = sum(algo) / ms / 1e6
     return {"workload": label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "ms_per_step": round(ms, 5), "bytes_per_step": sum(algo), "pool_copies": copies,
-            "path": qmv.last_path(), "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"}}
+            "path": qmv.last_path(), "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+            "shapes": per_shape}
 
 
 def moe_workload(qmv, tokens, label):
@@ -227,12 +235,14 @@ def moe_workload(qmv, tokens, label):
 
 
 def gemm_workload(qmv, steps, label):
-    """q6_K prefill GEMM, M = 512 tokens, W 11008x4096 and 4096x11008: TOPS = 2 M N K / time,
-    for the int8 contraction alone (activations already quantized) and end to end."""
+    """q6_K prefill GEMM, M = 512 tokens, W 11008x4096 and 4096x11008: TOPS = 2 M N K / time
+    for the int8 contraction alone (activations already quantized) and end to end.  The
+    weights are registered with their pre-expanded planes (the default-on registration the
+    method describes), and the in-kernel expansion of the same calls is timed beside it."""
     import torch
     M = 512
     out = {"workload": label, "unit": "TOPS", "shapes": []}
-    tot_ops, tot_ms, tot_ms_e2e = 0, 0.0, 0.0
+    tot_ops, tot_ms, tot_ms_e2e, tot_ms_raw = 0, 0.0, 0.0, 0.0
     for i, (n, k) in enumerate([(11008, 4096), (4096, 11008)]):
         _, pool = make_pool(qmv, synth.FMT_Q6_K, n, k, seed=i, copies=4)
         x = torch.from_numpy(synth.gen_x(M, k, seed=i)).cuda()
@@ -240,18 +250,28 @@ def gemm_workload(qmv, steps, label):
         y = torch.empty((M, n), dtype=torch.float32, device="cuda")
         ws = torch.empty(qmv.workspace_bytes(pool[0], M), dtype=torch.uint8, device="cuda")
         R = max(8, steps // 4)
+        ms_raw = time_graph(graph_of(lambda j: qmv.gemm_q8(pool[j % 4], xq, xs, y), R), R)
+        path_raw = qmv.last_path()
+        for W in pool:
+            qmv.register_plane(W)
         ms = time_graph(graph_of(lambda j: qmv.gemm_q8(pool[j % 4], xq, xs, y), R), R)
         path = qmv.last_path()
         ms2 = time_graph(graph_of(lambda j: qmv.gemm(pool[j % 4], x, y, ws), R), R)
+        for W in pool:
+            qmv.unregister_plane(W)
         ops = 2 * M * n * k
         tot_ops += ops
         tot_ms += ms
         tot_ms_e2e += ms2
+        tot_ms_raw += ms_raw
         out["shapes"].append({"shape": f"{n}x{k}", "M": M, "ms": round(ms, 5), "TOPS": round(ops / ms / 1e9, 1),
-                              "ms_with_quantizer": round(ms2, 5), "path": path})
+                              "ms_with_quantizer": round(ms2, 5), "path": path,
+                              "ms_in_kernel_expand": round(ms_raw, 5),
+                              "TOPS_in_kernel_expand": round(ops / ms_raw / 1e9, 1), "path_in_kernel_expand": path_raw})
     tops = tot_ops / tot_ms / 1e9
     out.update({"value": round(tops, 1), "frac_of_peak": round(tops / INT8_PEAK_TOPS, 4),
                 "TOPS_with_quantizer": round(tot_ops / tot_ms_e2e / 1e9, 1),
+                "TOPS_in_kernel_expand": round(tot_ops / tot_ms_raw / 1e9, 1),
                 "roofline": {"bound": "mfma", "peak": INT8_PEAK_TOPS, "unit": "TOPS"}})
     return out
 
@@ -349,6 +369,15 @@ def main():
             sec[f"aq2x8_gemv_b{b}"] = gemv_workload(qmv, synth.FMT_AQ2X8, [(14336, 4096), (4096, 14336)], b,
                                                     synth.DT_BF16, 50,
                                                     f"2-bit additive GEMV batch {b}, 14336x4096 + 4096x14336, bf16 x")
+        for b in ((1, 4) if "aq3x8" in want else ()):
+            sec[f"aq3x8_gemv_b{b}"] = gemv_workload(qmv, synth.FMT_AQ3X8, [(14336, 4096), (4096, 14336)], b,
+                                                    synth.DT_BF16, 50,
+                                                    f"3-bit additive GEMV batch {b}, 14336x4096 + 4096x14336, bf16 x")
+        if "cb8" in want:
+            sec["cb8_gemv"] = gemv_workload(qmv, synth.FMT_CB8, [(2048, 7168), (2048, 7168), (7168, 2048),
+                                                                 (129280, 7168)], 1, synth.DT_BF16, 20,
+                                            "8-bit codebook GEMV batch 1, shared expert gate/up 2048x7168 + "
+                                            "down 7168x2048 and output head 129280x7168, bf16 x")
         if "q6_K_gemm" in want:
             sec["q6_K_gemm"] = gemm_workload(qmv, a.steps, "q6_K prefill GEMM, M=512, 11008x4096 + 4096x11008")
         out["secondary"] = sec

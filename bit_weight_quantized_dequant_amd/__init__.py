@@ -13,7 +13,8 @@ import os
 __all__ = [
     "Q4_0", "Q6_K", "CB4", "AQ2X8", "CB8", "AQ3X8", "F32", "BF16", "QmvError", "QWeights", "lib", "plane_bytes",
     "weight_bytes", "validate", "gemv", "dequant", "quant_act", "workspace_bytes", "gemm",
-    "gemm_q8", "partials", "moe_ffn", "last_path", "strerror", "PLANES",
+    "gemm_q8", "partials", "plane_bytes_of", "register_plane", "unregister_plane", "moe_ffn", "last_path",
+    "strerror", "PLANES",
 ]
 
 Q4_0, Q6_K, CB4, AQ2X8, CB8, AQ3X8 = 1, 2, 3, 4, 5, 6
@@ -79,6 +80,12 @@ def lib():
         L.qmm_gemm_q8.argtypes = [P, I32, P, P, P, P]
         L.qmm_partials.restype = C.c_int
         L.qmm_partials.argtypes = [P, I32, P, P, P]
+        L.qmm_plane_bytes.restype = I64
+        L.qmm_plane_bytes.argtypes = [P]
+        L.qmm_register_plane.restype = C.c_int
+        L.qmm_register_plane.argtypes = [P, P, I64, P]
+        L.qmm_unregister_plane.restype = C.c_int
+        L.qmm_unregister_plane.argtypes = [P]
         L.qmv_moe_ffn.restype = C.c_int
         L.qmv_moe_ffn.argtypes = [P, P, P, I32, P, I32, P, I32, P, P, P]
         L.qmv_last_path.restype = C.c_char_p
@@ -228,6 +235,30 @@ def partials(w: QWeights, xq, out=None, stream=None):
         out = torch.empty((m, w.n, w.k // 32), dtype=torch.int32, device=xq.device)
     _check(lib().qmm_partials(w.ref, m, _ptr(xq), _ptr(out), _stream(stream)), "qmm_partials")
     return out
+
+
+def plane_bytes_of(w: QWeights) -> int:
+    return lib().qmm_plane_bytes(w.ref)
+
+
+def register_plane(w: QWeights, plane=None, stream=None):
+    """Fill a pre-expanded plane for the q6_K GEMM (allocated here unless given) and record
+    it for w.  Returns the plane tensor, which must be kept alive while it is registered."""
+    import torch
+    need = plane_bytes_of(w)
+    if need < 0:
+        raise QmvError(need, "qmm_plane_bytes")
+    if plane is None:
+        plane = torch.empty(need, dtype=torch.uint8, device="cuda")
+    _check(lib().qmm_register_plane(w.ref, _ptr(plane), plane.numel() * plane.element_size(), _stream(stream)),
+           "qmm_register_plane")
+    w._plane = plane
+    return plane
+
+
+def unregister_plane(w: QWeights):
+    _check(lib().qmm_unregister_plane(w.ref), "qmm_unregister_plane")
+    w._plane = None
 
 
 def moe_ffn(gate: QWeights, up: QWeights, down: QWeights, n_experts: int, ids, x, h=None, y=None,

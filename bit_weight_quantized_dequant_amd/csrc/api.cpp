@@ -7,6 +7,8 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <string>
+#include <unordered_map>
 
 #include "qmv_internal.h"
 
@@ -35,6 +37,50 @@ int block_of(int32_t fmt) {
     case QMV_AQ3X8: return 8;
     }
     return 0;
+}
+// Registered pre-expanded q6_K planes, keyed by the codes pointer of the weights they
+// were built from; the entry also holds the geometry and the other planes, so that a
+// descriptor reusing the pointer with another layout does not pick up a stale plane.
+struct PlaneEntry {
+    const void *codes_hi, *scales, *super;
+    int64_t n, k;
+    const int8_t *plane;
+};
+std::mutex g_plane_mu;
+std::unordered_map<const void *, PlaneEntry> g_planes;
+
+bool exp_opted_out() {
+    const char *e = std::getenv("QMV_Q6K_EXP");
+    return e && std::strcmp(e, "0") == 0;
+}
+
+// The plane to use for w and the suffix its label carries.
+const int8_t *plane_of(const qmv_weights *w, const char **suffix) {
+    std::lock_guard<std::mutex> lock(g_plane_mu);
+    auto it = g_planes.find(w->codes);
+    if (it != g_planes.end()) {
+        const PlaneEntry &e = it->second;
+        if (e.n == w->n && e.k == w->k && e.codes_hi == w->codes_hi && e.scales == w->scales &&
+            e.super == w->super) {
+            *suffix = ".plane";
+            return e.plane;
+        }
+        *suffix = "(fallback!)";  // recorded for this pointer, but not for this layout
+        return nullptr;
+    }
+    *suffix = exp_opted_out() ? "(exp=off)" : "";
+    return nullptr;
+}
+
+// Runs a GEMM launcher with the plane lookup and records the decorated label.
+template <class F>
+int gemm_with_plane(const char *call, const qmv_weights *w, int m, F &&launch) {
+    const char *suffix = "";
+    const int8_t *plane = plane_of(w, &suffix);
+    const char *path = launch(plane);
+    if (!path) return QMV_ERR_LIMIT;
+    const std::string label = std::string(path) + suffix;
+    return finish_launch(call, w, m, label.c_str());
 }
 }  // namespace
 
@@ -213,9 +259,9 @@ int qmm_gemm_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *
     if (rc) return rc;
     if (!xq || !xs || !y) return QMV_ERR_NULL;
     if (!aligned16(xq) || !aligned16(xs) || !aligned16(y)) return QMV_ERR_ALIGN;
-    const char *path = launch_gemm_q6k(w, m, xq, xs, y, nullptr, (hipStream_t)stream);
-    if (!path) return QMV_ERR_LIMIT;
-    return finish_launch("qmm_gemm_q8", w, m, path);
+    return gemm_with_plane("qmm_gemm_q8", w, m, [&](const int8_t *plane) {
+        return launch_gemm_q6k(w, m, plane, xq, xs, y, nullptr, (hipStream_t)stream);
+    });
 }
 
 int qmm_partials(const qmv_weights *w, int32_t m, const int8_t *xq, int32_t *i32, void *stream) {
@@ -223,9 +269,9 @@ int qmm_partials(const qmv_weights *w, int32_t m, const int8_t *xq, int32_t *i32
     if (rc) return rc;
     if (!xq || !i32) return QMV_ERR_NULL;
     if (!aligned16(xq) || !aligned16(i32)) return QMV_ERR_ALIGN;
-    const char *path = launch_gemm_q6k(w, m, xq, nullptr, nullptr, i32, (hipStream_t)stream);
-    if (!path) return QMV_ERR_LIMIT;
-    return finish_launch("qmm_partials", w, m, path);
+    return gemm_with_plane("qmm_partials", w, m, [&](const int8_t *plane) {
+        return launch_gemm_q6k(w, m, plane, xq, nullptr, nullptr, i32, (hipStream_t)stream);
+    });
 }
 
 int qmm_gemm(const qmv_weights *w, int32_t m, const float *x, float *y, void *ws, int64_t ws_bytes,
@@ -242,9 +288,42 @@ int qmm_gemm(const qmv_weights *w, int32_t m, const float *x, float *y, void *ws
     if (!p1) return QMV_ERR_LIMIT;
     rc = finish_launch("qmm_quant_act", w, m, p1);
     if (rc) return rc;
-    const char *p2 = launch_gemm_q6k(w, m, xq, xs, y, nullptr, (hipStream_t)stream);
-    if (!p2) return QMV_ERR_LIMIT;
-    return finish_launch("qmm_gemm", w, m, p2);
+    return gemm_with_plane("qmm_gemm", w, m, [&](const int8_t *plane) {
+        return launch_gemm_q6k(w, m, plane, xq, xs, y, nullptr, (hipStream_t)stream);
+    });
+}
+
+int64_t qmm_plane_bytes(const qmv_weights *w) {
+    int rc = qmv_validate(w, 1, QMV_F32);
+    if (rc) return rc;
+    if (w->fmt != QMV_Q6_K) return QMV_ERR_FORMAT;
+    return 2 * w->n * w->k;
+}
+
+int qmm_register_plane(const qmv_weights *w, void *plane, int64_t plane_bytes, void *stream) {
+    const int64_t need = qmm_plane_bytes(w);
+    if (need < 0) return (int)need;
+    if (!plane) return QMV_ERR_NULL;
+    if (plane_bytes < need) return QMV_ERR_WORKSPACE;
+    if ((uintptr_t)plane & 255u) return QMV_ERR_ALIGN;
+    if (exp_opted_out()) {  // explicit opt-out: nothing built, nothing recorded
+        std::snprintf(g_last_path, sizeof g_last_path, "plane.q6k(exp=off)");
+        return QMV_OK;
+    }
+    const char *path = launch_expand_q6k(w, (int8_t *)plane, (hipStream_t)stream);
+    if (!path) return QMV_ERR_LIMIT;
+    const int rc = finish_launch("qmm_register_plane", w, 1, path);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lock(g_plane_mu);
+    g_planes[w->codes] = PlaneEntry{w->codes_hi, w->scales, w->super, w->n, w->k, (const int8_t *)plane};
+    return QMV_OK;
+}
+
+int qmm_unregister_plane(const qmv_weights *w) {
+    if (!w) return QMV_ERR_NULL;
+    std::lock_guard<std::mutex> lock(g_plane_mu);
+    g_planes.erase(w->codes);
+    return QMV_OK;
 }
 
 int qmv_moe_ffn(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,

@@ -36,6 +36,7 @@
 // C[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32].  A debug entry point writes the exact
 // I32 partials from this same code path, which pins the layout against the oracle.
 #include <cstring>
+#include <type_traits>
 
 #include "device_common.h"
 #include "qmv_internal.h"
@@ -82,19 +83,28 @@ QMV_DEV void expand4(uint32_t q, uint32_t sc2, uint32_t c2, uint32_t &hb, uint32
 template <int NW> struct RawA;
 template <> struct RawA<16> { uint4 ql, qh; };
 template <> struct RawA<8> { uint2 ql, qh; };
+// The same thread's share of a step from the pre-expanded planes: its h and l bytes.
+template <int NW> struct RawE;
+template <> struct RawE<16> { uint4 h, l; };
+template <> struct RawE<8> { uint2 h, l; };
 
 // Step st = 4 s + j covers weights [64 j, 64 j + 64) of super-block s: half h = j >> 1,
 // runs t = 2 (j & 1) + {0, 1}, each run 32 consecutive l.  Weight (h, t, l) has its low
 // nibble in ql[64 h + 32 (t & 1) + l] (bits 4 (t >> 1)..) and its high bits in
-// qh[32 h + l] (bits 2 t..); ql/qh bytes of a half serve both of its steps.
-template <int WN, bool PARTIALS, int PD>
+// qh[32 h + l] (bits 2 t..); ql/qh bytes of a half serve both of its steps.  Tile byte
+// 32 tt + l of the step is weight 64 st + 32 tt + l of the row: natural k order, which
+// is also the order of the pre-expanded planes (EXP: the thread copies its h and l bytes
+// instead of expanding codes).
+template <int WN, bool PARTIALS, int PD, bool EXP>
 __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh,
                                                          const int8_t *__restrict__ scp, const uint16_t *__restrict__ dp,
+                                                         const int8_t *__restrict__ ph, const int8_t *__restrict__ pl,
                                                          const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                          float *__restrict__ y, int32_t *__restrict__ part,
                                                          int M, int N, int K) {
     using G = Geo<WN>;
     constexpr int BN = G::BN, TPW = G::TPW, NWT = G::W;
+    using RA = std::conditional_t<EXP, RawE<NWT>, RawA<NWT>>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ float sD[2][BN];
 
@@ -112,6 +122,8 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
     const uint8_t *qhr = qh + (int64_t)erow * (K >> 2) + l0;
     const int8_t *scr = scp + (int64_t)erow * (K >> 4) + 2 * tt + (l0 >> 4);
     const uint16_t *dr = dp + (int64_t)erow * (K >> 8);
+    const int8_t *phr = ph + (int64_t)erow * K + 32 * tt + l0;  // EXP: this thread's h, l bytes
+    const int8_t *plr = pl + (int64_t)erow * K + 32 * tt + l0;
     // activation staging role: token bt, bytes [32 bo, 32 bo + 32) of the step
     const int bt = tid >> 1, bo = tid & 1;
     const int8_t *xr = xq + (int64_t)min(m0 + bt, M - 1) * K + 32 * bo;
@@ -128,7 +140,7 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
     // raw inputs of one step, held in registers from the prefetch to the expansion; with a
     // prefetch distance of 2 there are two sets, used by even and odd steps
     struct Raw {
-        RawA<NWT> ra;
+        RA ra;
         int scb;
         uint32_t dbits;
         uint4 rb0, rb1;
@@ -143,16 +155,26 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
         auto &rb1 = r.rb1;
         auto &xsv = r.xsv;
         const int s = st >> 2, j = st & 3, h = j >> 1;
-        if ((j & 1) == 0) {  // a new half: its ql/qh bytes
+        if constexpr (EXP) {
             if constexpr (NWT == 16) {
-                ra.ql = ld_stream16(qlr + 128 * s + 64 * h);
-                ra.qh = ld_stream16(qhr + 64 * s + 32 * h);
+                ra.h = ld_stream16(phr + st * KS);
+                ra.l = ld_stream16(plr + st * KS);
             } else {
-                ra.ql = *(const uint2 *)(qlr + 128 * s + 64 * h);
-                ra.qh = *(const uint2 *)(qhr + 64 * s + 32 * h);
+                ra.h = *(const uint2 *)(phr + st * KS);
+                ra.l = *(const uint2 *)(plr + st * KS);
             }
+        } else {
+            if ((j & 1) == 0) {  // a new half: its ql/qh bytes
+                if constexpr (NWT == 16) {
+                    ra.ql = ld_stream16(qlr + 128 * s + 64 * h);
+                    ra.qh = ld_stream16(qhr + 64 * s + 32 * h);
+                } else {
+                    ra.ql = *(const uint2 *)(qlr + 128 * s + 64 * h);
+                    ra.qh = *(const uint2 *)(qhr + 64 * s + 32 * h);
+                }
+            }
+            scb = scr[16 * s + 8 * h + 4 * (j & 1)];
         }
-        scb = scr[16 * s + 8 * h + 4 * (j & 1)];
         if (j == 0) dbits = dr[s];
         rb0 = *(const uint4 *)(xr + st * KS);
         rb1 = *(const uint4 *)(xr + st * KS + 16);
@@ -163,42 +185,54 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
         }
     };
 
+    // Stage step st into LDS buffer buf: the weight tile (expanded from the codes, or copied
+    // from the planes), the super-block's d once per super-block, the activation bytes.
     auto store = [&](int st, int buf, const Raw &r) {
-        const auto &ra = r.ra;
-        const int scb = r.scb;
+        const RA ra = r.ra;
         const uint32_t dbits = r.dbits;
         const uint4 rb0 = r.rb0, rb1 = r.rb1;
-        const int j = st & 3;
-        const int sh = 2 * (2 * (j & 1) + tt);  // qh bit offset of run t
-        const uint32_t sc16 = (uint32_t)scb & 0xFFFFu;
-        const uint32_t sc2 = sc16 | (sc16 << 16);
-        const uint32_t c16 = (uint32_t)(-32 * scb) & 0xFFFFu;
-        const uint32_t c2 = c16 | (c16 << 16);
-        constexpr int ND = NWT / 4;
-        uint32_t qlw[ND], qhw[ND], hv[ND], lv[ND];
-        if constexpr (NWT == 16) {
-            qlw[0] = ra.ql.x; qlw[1] = ra.ql.y; qlw[2] = ra.ql.z; qlw[3] = ra.ql.w;
-            qhw[0] = ra.qh.x; qhw[1] = ra.qh.y; qhw[2] = ra.qh.z; qhw[3] = ra.qh.w;
-        } else {
-            qlw[0] = ra.ql.x; qlw[1] = ra.ql.y;
-            qhw[0] = ra.qh.x; qhw[1] = ra.qh.y;
-        }
-#pragma unroll
-        for (int i = 0; i < ND; i++) {
-            const uint32_t nib = ((j & 1) ? qlw[i] >> 4 : qlw[i]) & 0x0F0F0F0Fu;
-            const uint32_t q = nib | (((qhw[i] >> sh) & 0x03030303u) << 4);
-            expand4(q, sc2, c2, hv[i], lv[i]);
-        }
         uint8_t *dh = sH(buf) + er * RS + 32 * tt + l0;
         uint8_t *dl = sL(buf) + er * RS + 32 * tt + l0;
-        if constexpr (NWT == 16) {
-            *(uint4 *)dh = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-            *(uint4 *)dl = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+        if constexpr (EXP) {
+            if constexpr (NWT == 16) {
+                *(uint4 *)dh = make_uint4(ra.h.x, ra.h.y, ra.h.z, ra.h.w);
+                *(uint4 *)dl = make_uint4(ra.l.x, ra.l.y, ra.l.z, ra.l.w);
+            } else {
+                *(uint2 *)dh = make_uint2(ra.h.x, ra.h.y);
+                *(uint2 *)dl = make_uint2(ra.l.x, ra.l.y);
+            }
         } else {
-            *(uint2 *)dh = make_uint2(hv[0], hv[1]);
-            *(uint2 *)dl = make_uint2(lv[0], lv[1]);
+            const int scb = r.scb;
+            const int j = st & 3;
+            const int sh = 2 * (2 * (j & 1) + tt);  // qh bit offset of run t
+            const uint32_t sc16 = (uint32_t)scb & 0xFFFFu;
+            const uint32_t sc2 = sc16 | (sc16 << 16);
+            const uint32_t c16 = (uint32_t)(-32 * scb) & 0xFFFFu;
+            const uint32_t c2 = c16 | (c16 << 16);
+            constexpr int ND = NWT / 4;
+            uint32_t qlw[ND], qhw[ND], hv[ND], lv[ND];
+            if constexpr (NWT == 16) {
+                qlw[0] = ra.ql.x; qlw[1] = ra.ql.y; qlw[2] = ra.ql.z; qlw[3] = ra.ql.w;
+                qhw[0] = ra.qh.x; qhw[1] = ra.qh.y; qhw[2] = ra.qh.z; qhw[3] = ra.qh.w;
+            } else {
+                qlw[0] = ra.ql.x; qlw[1] = ra.ql.y;
+                qhw[0] = ra.qh.x; qhw[1] = ra.qh.y;
+            }
+#pragma unroll
+            for (int i = 0; i < ND; i++) {
+                const uint32_t nib = ((j & 1) ? qlw[i] >> 4 : qlw[i]) & 0x0F0F0F0Fu;
+                const uint32_t q = nib | (((qhw[i] >> sh) & 0x03030303u) << 4);
+                expand4(q, sc2, c2, hv[i], lv[i]);
+            }
+            if constexpr (NWT == 16) {
+                *(uint4 *)dh = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+                *(uint4 *)dl = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+            } else {
+                *(uint2 *)dh = make_uint2(hv[0], hv[1]);
+                *(uint2 *)dl = make_uint2(lv[0], lv[1]);
+            }
         }
-        if (j == 0 && ep == 0) sD[(st >> 2) & 1][er] = h2f((uint16_t)dbits);
+        if ((st & 3) == 0 && ep == 0) sD[(st >> 2) & 1][er] = h2f((uint16_t)dbits);
         uint8_t *db = sB(buf) + bt * RS + 32 * bo;
         *(uint4 *)db = rb0;
         *(uint4 *)(db + 16) = rb1;
@@ -225,7 +259,7 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
             if (st + 1 < nsteps) fetch(st + 1, cur);
         } else {
             if (st + 2 < nsteps) {
-                if ((st & 1) == 1) cur.ra = nxt.ra;  // st + 2 odd: same half as st + 1
+                if (!EXP && (st & 1) == 1) cur.ra = nxt.ra;  // st + 2 odd: same half as st + 1
                 fetch(st + 2, cur);
             }
         }
@@ -280,7 +314,7 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
     fetch(0, R0);
     if (PD == 2 && nsteps > 1) {
         fetch(1, R1);
-        R1.ra = R0.ra;  // step 1 is the second step of half 0
+        if (!EXP) R1.ra = R0.ra;  // step 1 is the second step of half 0
     }
     store(0, 0, R0);
     __syncthreads();
@@ -312,29 +346,27 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
     }
 }
 
-template <int WN, bool PARTIALS, int PD>
-void launch_tiles(const qmv_weights *w, int m, const int8_t *xq, const float *xs, float *y, int32_t *partials,
-                  hipStream_t s) {
+template <int WN, bool PARTIALS, int PD, bool EXP>
+void launch_tiles(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs, float *y,
+                  int32_t *partials, hipStream_t s) {
     using G = Geo<WN>;
     const int64_t n = w->n, k = w->k;
     const dim3 grid((unsigned)((n + G::BN - 1) / G::BN), (unsigned)((m + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm_q6k_kernel<WN, PARTIALS, PD>), grid, dim3(TB), G::LDS, s, (const uint8_t *)w->codes,
-                       (const uint8_t *)w->codes_hi, (const int8_t *)w->scales, (const uint16_t *)w->super, xq, xs,
-                       y, partials, m, (int)n, (int)k);
+    hipLaunchKernelGGL((gemm_q6k_kernel<WN, PARTIALS, PD, EXP>), grid, dim3(TB), G::LDS, s, (const uint8_t *)w->codes,
+                       (const uint8_t *)w->codes_hi, (const int8_t *)w->scales, (const uint16_t *)w->super, plane,
+                       plane ? plane + n * k : nullptr, xq, xs, y, partials, m, (int)n, (int)k);
 }
 
-}  // namespace
-
-const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *xq, const float *xs, float *y,
-                            int32_t *partials, hipStream_t s) {
-    const int64_t n = w->n, k = w->k;
-    if (n > INT32_MAX || k > INT32_MAX || (int64_t)m * k > INT32_MAX) return nullptr;
+template <bool EXP>
+const char *launch_gemm(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs,
+                        float *y, int32_t *partials, hipStream_t s) {
+    const int64_t n = w->n;
     // 64-row tiles when they give at least two workgroups per CU, else 32-row tiles
     const int64_t tiles64 = ((n + 63) / 64) * ((m + BM - 1) / BM);
     const bool wide = tiles64 >= 2 * (int64_t)device_info().num_cus;
     if (partials) {
-        if (wide) launch_tiles<2, true, 1>(w, m, xq, xs, y, partials, s);
-        else launch_tiles<1, true, 1>(w, m, xq, xs, y, partials, s);
+        if (wide) launch_tiles<2, true, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
+        else launch_tiles<1, true, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
         return "gemm.q6k.mfma-i8-32x32x32.hl-split.partials";
     }
     // 64-row tiles keep the loads of the next step in flight (their register budget allows
@@ -342,13 +374,58 @@ const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *xq, const
     const char *fp = forced_path();  // test-only override of the prefetch distance
     const int pd = strcmp(fp, "gemm.pd1") == 0 ? 1 : strcmp(fp, "gemm.pd2") == 0 ? 2 : (wide ? 1 : 2);
     if (wide) {
-        if (pd == 1) launch_tiles<2, false, 1>(w, m, xq, xs, y, partials, s);
-        else launch_tiles<2, false, 2>(w, m, xq, xs, y, partials, s);
+        if (pd == 1) launch_tiles<2, false, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
+        else launch_tiles<2, false, 2, EXP>(w, m, plane, xq, xs, y, partials, s);
     } else {
-        if (pd == 1) launch_tiles<1, false, 1>(w, m, xq, xs, y, partials, s);
-        else launch_tiles<1, false, 2>(w, m, xq, xs, y, partials, s);
+        if (pd == 1) launch_tiles<1, false, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
+        else launch_tiles<1, false, 2, EXP>(w, m, plane, xq, xs, y, partials, s);
     }
     return "gemm.q6k.mfma-i8-32x32x32.hl-split";
+}
+
+// Pre-expansion of a q6_K matrix into the planes the EXP kernels copy: for every weight,
+// w' = sc * (q - 32) = 64 h + l with h = w' >> 6 (arithmetic) and l = w' & 63, stored
+// as int8 H[n][k] then L[n][k].  One thread per 64-weight unit (half h, offset 16 odd)
+// of a super-block, as in the dequantizer.
+__global__ void __launch_bounds__(256) expand_q6k_planes(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh,
+                                                         const int8_t *__restrict__ sc, int8_t *__restrict__ H,
+                                                         int8_t *__restrict__ L, int64_t nunits) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nunits) return;
+    const int64_t sb = i >> 2;
+    const int h = (int)((i >> 1) & 1), odd = (int)(i & 1);
+    const uint8_t *a = ql + sb * 128 + 64 * h + 16 * odd;
+    const uint8_t *hb = qh + sb * 64 + 32 * h + 16 * odd;
+    const int64_t e0 = sb * 256 + 128 * h + 16 * odd;
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+        const int s = sc[sb * 16 + 8 * h + 2 * t + odd];
+        for (int j = 0; j < 16; j++) {
+            const int q = ((a[j + 32 * (t & 1)] >> (4 * (t >> 1))) & 15) | (((hb[j] >> (2 * t)) & 3) << 4);
+            const int wv = s * (q - 32);
+            H[e0 + 32 * t + j] = (int8_t)(wv >> 6);
+            L[e0 + 32 * t + j] = (int8_t)(wv & 63);
+        }
+    }
+}
+
+}  // namespace
+
+const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs,
+                            float *y, int32_t *partials, hipStream_t s) {
+    const int64_t n = w->n, k = w->k;
+    if (n > INT32_MAX || k > INT32_MAX || (int64_t)m * k > INT32_MAX) return nullptr;
+    return plane ? launch_gemm<true>(w, m, plane, xq, xs, y, partials, s)
+                 : launch_gemm<false>(w, m, nullptr, xq, xs, y, partials, s);
+}
+
+const char *launch_expand_q6k(const qmv_weights *w, int8_t *plane, hipStream_t s) {
+    const int64_t nunits = w->n * w->k / 64;
+    if (nunits > (int64_t)INT32_MAX * 256) return nullptr;
+    hipLaunchKernelGGL(expand_q6k_planes, dim3((unsigned)((nunits + 255) / 256)), dim3(256), 0, s,
+                       (const uint8_t *)w->codes, (const uint8_t *)w->codes_hi, (const int8_t *)w->scales, plane,
+                       plane + w->n * w->k, nunits);
+    return "plane.q6k.expand";
 }
 
 }  // namespace qmv

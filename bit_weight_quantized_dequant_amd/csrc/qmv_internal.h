@@ -36,8 +36,11 @@ const char *launch_gemv_cb8(const qmv_weights *w, int m, const void *x, int xt, 
                             hipStream_t s);
 const char *launch_dequant(const qmv_weights *w, float *out, hipStream_t s);
 const char *launch_quant_act(const float *x, int m, int64_t k, int8_t *xq, float *xs, hipStream_t s);
-const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *xq, const float *xs, float *y,
-                            int32_t *partials, hipStream_t s);
+// plane: the registered pre-expanded H/L planes of w (int8 [n][k] each, H then L), or
+// nullptr for the in-kernel expansion of the codes.
+const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs,
+                            float *y, int32_t *partials, hipStream_t s);
+const char *launch_expand_q6k(const qmv_weights *w, int8_t *plane, hipStream_t s);
 const char *launch_moe_cb4(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,
                            int n_experts, const int32_t *ids, int n_ids, const void *x, int xt,
                            float *h, float *y, hipStream_t s);

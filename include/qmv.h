@@ -177,6 +177,36 @@ int qmm_gemm_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *
 int qmm_partials(const qmv_weights *w, int32_t m, const int8_t *xq, int32_t *i32, void *stream);
 
 /*
+ * Pre-expanded q6_K planes for the GEMM ("57 · r54 — MINFER_MMQ_Q6K_EXP": a dense
+ * int8 plane expanded once at registration so that the GEMM's weight staging is a plain
+ * copy, §2.1; the expansion is an integer transform, so results are byte-identical with
+ * and without it, §2.3; default on with an explicit "0" opt-out and a label that tells
+ * the cases apart, §2.4 and §3.1).
+ *
+ * The planes: for every weight, w' = sc * (q - 32) = 64 H + L with H in [-64, 64] and L in
+ * [0, 63]; H int8 [n][k], then L int8 [n][k] (k order), 2 bytes per weight.
+ *
+ * qmm_plane_bytes: 2 * n * k for a valid QMV_Q6_K descriptor, else a QMV_ERR_* code.
+ * qmm_register_plane: fills `plane` (device memory owned by the caller, at least
+ *   qmm_plane_bytes(w) bytes, 256-byte aligned) from w's codes on `stream`, and records it
+ *   for w, keyed by w->codes together with n, k and w's other plane pointers.  qmm_gemm,
+ *   qmm_gemm_q8 and qmm_partials on w then copy their weight tiles from it.  The plane must
+ *   stay allocated and unchanged, and w's codes unchanged, until qmm_unregister_plane(w);
+ *   work on other streams must be ordered after the fill by the caller.  With
+ *   QMV_Q6K_EXP=0 in the environment nothing is written or recorded and QMV_OK is returned.
+ *   Errors: QMV_ERR_NULL, QMV_ERR_FORMAT (not q6_K), QMV_ERR_SHAPE, QMV_ERR_WORKSPACE
+ *   (plane_bytes too small), QMV_ERR_ALIGN, QMV_ERR_HIP.  Thread-safe.
+ * qmm_unregister_plane: forgets the plane recorded for w->codes (QMV_OK either way).
+ * GEMM labels (qmv_last_path): "...hl-split.plane" when the plane is used; "...hl-split"
+ *   when none is recorded; "...hl-split(exp=off)" when none is recorded and QMV_Q6K_EXP=0;
+ *   "...hl-split(fallback!)" when one is recorded for w->codes with another geometry or
+ *   other planes (it is not used; the codes are expanded in the kernel).
+ */
+int64_t qmm_plane_bytes(const qmv_weights *w);
+int qmm_register_plane(const qmv_weights *w, void *plane, int64_t plane_bytes, void *stream);
+int qmm_unregister_plane(const qmv_weights *w);
+
+/*
  * Mixture-of-experts FFN over routed experts (batch 1 decode):
  *   for each listed expert e = ids[j]:  h[j] = SiLU(G_e x) * (U_e x),  y[j] = D_e h[j]
  * with SiLU(z) = z / (1 + e^-z).  No routing weights are applied; the caller

@@ -120,3 +120,113 @@ def test_gemm_all_codes_32_give_zero(qmv):
     y = qmv.gemm(qweights(synth.FMT_Q6_K, n, k, w), torch.from_numpy(synth.gen_x(m, k, seed=4)).cuda())
     torch.cuda.synchronize()
     assert np.all(y.cpu().numpy() == 0.0)
+
+
+# ------------------------------------------------------- pre-expanded planes
+
+def test_plane_holds_the_exact_hi_lo_split(qmv):
+    # 64 H + L == sc * (q - 32) for every weight, H in [-64, 64], L in [0, 63]; q from the
+    # oracle's integer decode, sc with both signs and both extremes
+    import torch
+    n, k = 37, 1024
+    w = synth.gen_weights(synth.FMT_Q6_K, n, k, seed=3)
+    w["sc"][::3] = -w["sc"][::3]
+    w["sc"][1, 0, :] = -128
+    w["sc"][2, 0, :] = 127
+    W = qweights(synth.FMT_Q6_K, n, k, w)
+    plane = qmv.register_plane(W)
+    torch.cuda.synchronize()
+    assert qmv.last_path() == "plane.q6k.expand"
+    p = plane.cpu().numpy().view(np.int8).astype(np.int64)
+    H, L = p[: n * k].reshape(n, k), p[n * k: 2 * n * k].reshape(n, k)
+    q = oracle.codes(oracle.Mat(oracle.Q6_K, n, k, w)).astype(np.int64)
+    sc = np.repeat(w["sc"].reshape(n, k // 16).astype(np.int64), 16, axis=1)
+    assert np.array_equal(64 * H + L, sc * (q - 32))
+    assert L.min() >= 0 and L.max() <= 63 and H.min() >= -64 and H.max() <= 64
+    qmv.unregister_plane(W)
+
+
+@pytest.mark.parametrize("n,k,m", [(64, 512, 128), (70, 768, 45), (257, 2048, 130), (4096, 1024, 512), (3, 256, 1),
+                                   (8192, 256, 512)])
+@pytest.mark.parametrize("force", ["", "gemm.pd1", "gemm.pd2"])
+def test_gemm_with_plane_is_byte_identical(qmv, monkeypatch, n, k, m, force):
+    # outputs and int32 partials with the plane equal those of the in-kernel expansion bit
+    # for bit (the expansion is an integer transform), for both tile shapes and both
+    # prefetch distances; the partials also equal the oracle's
+    import torch
+    monkeypatch.setenv("QMV_FORCE_PATH", force)
+    w, x, W, xd = _setup(qmv, n, k, m, seed=n + 7 * m)
+    xq, xs = qmv.quant_act(xd)
+    y0 = qmv.gemm_q8(W, xq, xs)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split"
+    p0 = qmv.partials(W, xq)
+    qmv.register_plane(W)
+    y1 = qmv.gemm_q8(W, xq, xs)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+    p1 = qmv.partials(W, xq)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.partials.plane"
+    y2 = qmv.gemm(W, xd)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+    qmv.unregister_plane(W)
+    y3 = qmv.gemm_q8(W, xq, xs)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split"
+    torch.cuda.synchronize()
+    y0, y1, y2, y3 = (t.cpu().numpy().view(np.int32) for t in (y0, y1, y2, y3))
+    assert np.array_equal(y0, y1) and np.array_equal(y0, y2) and np.array_equal(y0, y3)
+    assert np.array_equal(p0.cpu().numpy(), p1.cpu().numpy())
+    if n * m <= 64 * 130:
+        rq, _ = oracle.quant_act(x)
+        mm, nn = np.meshgrid(np.arange(m), np.arange(n), indexing="ij")
+        _, i32 = oracle.q6k_partials(oracle.Mat(oracle.Q6_K, n, k, w), rq, mm.ravel(), nn.ravel())
+        assert np.array_equal(p1.cpu().numpy().reshape(m * n, k // 32).astype(np.int64), i32)
+
+
+def test_plane_labels_opt_out_and_fallback(qmv, monkeypatch):
+    import torch
+    n, k, m = 96, 512, 70
+    w, x, W, xd = _setup(qmv, n, k, m, seed=5)
+    xq, xs = qmv.quant_act(xd)
+    ref = qmv.gemm_q8(W, xq, xs)
+    # opted out: registration builds nothing, the GEMM names the reason
+    monkeypatch.setenv("QMV_Q6K_EXP", "0")
+    qmv.register_plane(W)
+    assert qmv.last_path() == "plane.q6k(exp=off)"
+    y_off = qmv.gemm_q8(W, xq, xs)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split(exp=off)"
+    monkeypatch.delenv("QMV_Q6K_EXP")
+    # registered for 96 rows; a descriptor over the same codes with 95 rows must not use it
+    qmv.register_plane(W)
+    W95 = qmv.QWeights(synth.FMT_Q6_K, n - 1, k, W.planes)
+    y95 = qmv.gemm_q8(W95, xq, xs)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split(fallback!)"
+    y_plane = qmv.gemm_q8(W, xq, xs)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+    qmv.unregister_plane(W)
+    torch.cuda.synchronize()
+    ref = ref.cpu().numpy()
+    assert np.array_equal(y_off.cpu().numpy().view(np.int32), ref.view(np.int32))
+    assert np.array_equal(y_plane.cpu().numpy().view(np.int32), ref.view(np.int32))
+    assert np.array_equal(y95.cpu().numpy().view(np.int32), ref[:, : n - 1].copy().view(np.int32))
+
+
+@pytest.mark.parametrize("n,k", [(11008, 4096), (4096, 11008)])
+def test_gemm_prefill_shapes_with_plane(qmv, n, k):
+    # the workload shapes: byte-identical with and without the plane, and within the bound
+    # of the oracle on sampled pairs
+    import torch
+    m = 512
+    w, x, W, xd = _setup(qmv, n, k, m, seed=0)
+    y0 = qmv.gemm(W, xd)
+    qmv.register_plane(W)
+    y1 = qmv.gemm(W, xd)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+    qmv.unregister_plane(W)
+    torch.cuda.synchronize()
+    y0, y1 = y0.cpu().numpy(), y1.cpu().numpy()
+    assert np.array_equal(y0.view(np.int32), y1.view(np.int32))
+    xq, xs = oracle.quant_act(x)
+    rng = np.random.default_rng(2)
+    mm = np.concatenate([[0, m - 1], rng.integers(0, m, 62)])
+    nn = np.concatenate([[n - 1, 0], rng.integers(0, n, 62)])
+    yr, b = oracle.q6k_gemm_pairs(oracle.Mat(oracle.Q6_K, n, k, w), xq, xs, mm, nn, nthreads=8)
+    assert_parity(y1[mm, nn][None, :], yr[None, :], b[None, :], f"gemm plane {n}x{k} sampled")
