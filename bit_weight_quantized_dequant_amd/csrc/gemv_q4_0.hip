@@ -38,9 +38,19 @@ constexpr size_t lds_bytes(int wg, int m, int bpl) {
     return (size_t)xchunks_per_thread(wg, m, bpl) * wg / 8 * XS * sizeof(float);
 }
 
+// and_or with a volatile asm: kept in program order relative to the scheduling barriers,
+// so the unpack of a later block is not hoisted next to this one (its halves would all be
+// live at once).
+QMV_DEV uint32_t and_or_ordered(uint32_t a, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask), "v"(bits));
+    return r;
+}
+
 // sum_{i<32} (q_i - 8) * x_i for one block (codes in 4 dwords, activations in xb[0..31]).
 // Each (q - 8) is an exact binary16 half; v_fma_mix_f32 multiplies it by the fp32
 // activation inside a fused multiply-add, so the only roundings are those of the sums.
+template <bool ORDERED = false>
 QMV_DEV float dot_q4_mix(uint4 q, const float *xb) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     const qmv_h2 off_lo = {(_Float16)-1032.f, (_Float16)-1032.f};  // (1024 + q) - 1032 = q - 8
@@ -49,10 +59,11 @@ QMV_DEV float dot_q4_mix(uint4 q, const float *xb) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const uint32_t w8 = w[i] >> 8;
-        const qmv_h2 t0 = as_h2(and_or(w[i], 0x000F000Fu, 0x64006400u)) + off_lo;  // bytes 0, 2 low
-        const qmv_h2 t1 = as_h2(and_or(w[i], 0x00F000F0u, 0x5C005C00u)) + off_hi;  // bytes 0, 2 high
-        const qmv_h2 t2 = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) + off_lo;    // bytes 1, 3 low
-        const qmv_h2 t3 = as_h2(and_or(w8, 0x00F000F0u, 0x5C005C00u)) + off_hi;    // bytes 1, 3 high
+        auto ao = [](uint32_t a, uint32_t mk, uint32_t b) { return ORDERED ? and_or_ordered(a, mk, b) : and_or(a, mk, b); };
+        const qmv_h2 t0 = as_h2(ao(w[i], 0x000F000Fu, 0x64006400u)) + off_lo;  // bytes 0, 2 low
+        const qmv_h2 t1 = as_h2(ao(w[i], 0x00F000F0u, 0x5C005C00u)) + off_hi;  // bytes 0, 2 high
+        const qmv_h2 t2 = as_h2(ao(w8, 0x000F000Fu, 0x64006400u)) + off_lo;    // bytes 1, 3 low
+        const qmv_h2 t3 = as_h2(ao(w8, 0x00F000F0u, 0x5C005C00u)) + off_hi;    // bytes 1, 3 high
         a0 = fmaf((float)t0.x, xb[4 * i + 0], a0);
         a0 = fmaf((float)t0.y, xb[4 * i + 2], a0);
         b0 = fmaf((float)t2.x, xb[4 * i + 1], b0);
@@ -95,8 +106,8 @@ QMV_DEV float dot_q4_cvt(uint4 q, const float *xb) {
 //   * Vector loads complete in issue order, so the LDS writes wait for x only, and block u
 //     becomes usable as soon as loads 0..u have landed.
 //   * The 64 lane partials of a row are summed across the wavefront with DPP.
-template <int WG, int M, int BPL, int XT, bool MIX>
-__global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict__ qs,
+template <int WG, int M, int BPL, int XT, bool MIX, int R>
+__global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_kernel(const uint8_t *__restrict__ qs,
                                                        const uint16_t *__restrict__ dsc,
                                                        const void *__restrict__ x,
                                                        float *__restrict__ y, int n, int k) {
@@ -106,8 +117,7 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
     const int nblk = k >> 5;
     const int total = M * (k >> 2);  // 16-byte activation chunks, m-major; 8 per block
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row = blockIdx.x * WAVES + wave;
-    const int rowc = row < n ? row : n - 1;
+    const int row0 = (blockIdx.x * WAVES + wave) * R;  // this wave's rows: row0 .. row0 + R - 1
 
     float4 xv[XPT];
 #pragma unroll
@@ -116,16 +126,20 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
         xv[j] = ld_act4<XT>(x, (int64_t)(c < total ? c : total - 1) * 4);
     }
 
-    uint4 q[BPL];
-    uint16_t dd[BPL];
-    const uint4 *qr = (const uint4 *)(qs + (int64_t)rowc * (k >> 1));
-    const uint16_t *dr = dsc + (int64_t)rowc * nblk;
+    // block-major load order (block u of every row, then block u + 1), so that block u
+    // can be computed as soon as its loads have landed
+    uint4 q[BPL][R];
+    uint16_t dd[BPL][R];
 #pragma unroll
     for (int u = 0; u < BPL; u++) {
         int b = lane + 64 * u;
         b = b < nblk ? b : nblk - 1;
-        q[u] = ld_stream16(qr + b);
-        dd[u] = dr[b];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int rowc = row0 + r < n ? row0 + r : n - 1;
+            q[u][r] = ld_stream16((const uint4 *)(qs + (int64_t)rowc * (k >> 1)) + b);
+            dd[u][r] = dsc[(int64_t)rowc * nblk + b];
+        }
     }
     __builtin_amdgcn_sched_barrier(0);  // every load is issued before the LDS writes wait on x
 
@@ -135,29 +149,39 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_kernel(const uint8_t *__restrict
     for (int j = 0; j < XPT; j++) dst[j * (WG / 8) * XS4] = xv[j];
     __syncthreads();
 
-    float acc[M];
+    // each block's 32 activations are read from LDS once per batch row and used for all R rows
+    float acc[R][M];
 #pragma unroll
-    for (int m = 0; m < M; m++) acc[m] = 0.f;
+    for (int r = 0; r < R; r++)
+#pragma unroll
+        for (int m = 0; m < M; m++) acc[r][m] = 0.f;
 #pragma unroll
     for (int u = 0; u < BPL; u++) {
         const int b = lane + 64 * u;
         const int bc = b < nblk ? b : nblk - 1;
-        const float d = h2f(dd[u]);
 #pragma unroll
         for (int m = 0; m < M; m++) {
             float xb[32];
 #pragma unroll
             for (int i = 0; i < 8; i++) *(float4 *)(xb + 4 * i) = sx4[(m * nblk + bc) * XS4 + i];
-            const float s = MIX ? dot_q4_mix(q[u], xb) : dot_q4_cvt(q[u], xb);
-            const float v = fmaf(d, s, acc[m]);
-            acc[m] = b < nblk ? v : acc[m];
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const float s = MIX ? dot_q4_mix<(R > 1)>(q[u][r], xb) : dot_q4_cvt(q[u][r], xb);
+                const float v = fmaf(h2f(dd[u][r]), s, acc[r][m]);
+                acc[r][m] = b < nblk ? v : acc[r][m];
+            }
         }
+        // keep the next block's activation reads below this block's dots: hoisted, every
+        // block's 32 activations would be live at once
+        if (R > 1) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int m = 0; m < M; m++) {
-        const float t = wave_sum(acc[m]);
-        if (lane == 0 && row < n) y[(int64_t)m * n + row] = t;
-    }
+    for (int r = 0; r < R; r++)
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float t = wave_sum(acc[r][m]);
+            if (lane == 0 && row0 + r < n) y[(int64_t)m * n + row0 + r] = t;
+        }
 }
 
 // Batches whose activations do not fit one workgroup's LDS (m * k > 16384) and rows longer
@@ -243,47 +267,48 @@ bool launch_chunked(int m, const qmv_weights *w, const void *x, float *y, hipStr
 }
 
 // 256-thread workgroups for short rows (more workgroups, x staged by fewer waves each),
-// 512 for long ones.
-template <int M, int BPL, int XT, bool MIX>
-void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
-    const int n = (int)w->n, k = (int)w->k;
-    if (BPL <= 2) {
-        hipLaunchKernelGGL((gemv_q4_0_kernel<256, M, BPL, XT, MIX>), dim3((n + 3) / 4), dim3(256),
-                           lds_bytes(256, M, BPL), s, (const uint8_t *)w->codes,
-                           (const uint16_t *)w->scales, x, y, n, k);
+// 512 for long ones; R rows per wave.
+template <int M, int BPL, int XT, bool MIX, int R>
+bool launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
+    if constexpr (R > 1 && M * BPL > 4) {
+        return false;  // not instantiated: the launcher takes one row per wave there
     } else {
-        hipLaunchKernelGGL((gemv_q4_0_kernel<512, M, BPL, XT, MIX>), dim3((n + 7) / 8), dim3(512),
-                           lds_bytes(512, M, BPL), s, (const uint8_t *)w->codes,
-                           (const uint16_t *)w->scales, x, y, n, k);
+        const int n = (int)w->n, k = (int)w->k;
+        constexpr int WG = BPL <= 2 ? 256 : 512;
+        constexpr int ROWS = WG / 64 * R;
+        hipLaunchKernelGGL((gemv_q4_0_kernel<WG, M, BPL, XT, MIX, R>), dim3((n + ROWS - 1) / ROWS), dim3(WG),
+                           lds_bytes(WG, M, BPL), s, (const uint8_t *)w->codes, (const uint16_t *)w->scales, x,
+                           y, n, k);
+        return true;
     }
 }
 
-template <int M, int XT, bool MIX>
+template <int M, int XT, bool MIX, int R>
 bool dispatch_bpl(int bpl, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     switch (bpl) {
-    case 1: launch<M, 1, XT, MIX>(w, x, y, s); return true;
-    case 2: launch<M, 2, XT, MIX>(w, x, y, s); return true;
-    case 3: launch<M, 3, XT, MIX>(w, x, y, s); return true;
-    case 4: launch<M, 4, XT, MIX>(w, x, y, s); return true;
-    case 5: launch<M, 5, XT, MIX>(w, x, y, s); return true;
-    case 6: launch<M, 6, XT, MIX>(w, x, y, s); return true;
-    case 7: launch<M, 7, XT, MIX>(w, x, y, s); return true;
-    case 8: launch<M, 8, XT, MIX>(w, x, y, s); return true;
+    case 1: return launch<M, 1, XT, MIX, R>(w, x, y, s);
+    case 2: return launch<M, 2, XT, MIX, R>(w, x, y, s);
+    case 3: return launch<M, 3, XT, MIX, R>(w, x, y, s);
+    case 4: return launch<M, 4, XT, MIX, R>(w, x, y, s);
+    case 5: return launch<M, 5, XT, MIX, R>(w, x, y, s);
+    case 6: return launch<M, 6, XT, MIX, R>(w, x, y, s);
+    case 7: return launch<M, 7, XT, MIX, R>(w, x, y, s);
+    case 8: return launch<M, 8, XT, MIX, R>(w, x, y, s);
     }
     return false;
 }
 
-template <int XT, bool MIX>
+template <int XT, bool MIX, int R>
 bool dispatch_m(int m, int bpl, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     switch (m) {
-    case 1: return dispatch_bpl<1, XT, MIX>(bpl, w, x, y, s);
-    case 2: return dispatch_bpl<2, XT, MIX>(bpl, w, x, y, s);
-    case 3: return dispatch_bpl<3, XT, MIX>(bpl, w, x, y, s);
-    case 4: return dispatch_bpl<4, XT, MIX>(bpl, w, x, y, s);
-    case 5: return dispatch_bpl<5, XT, MIX>(bpl, w, x, y, s);
-    case 6: return dispatch_bpl<6, XT, MIX>(bpl, w, x, y, s);
-    case 7: return dispatch_bpl<7, XT, MIX>(bpl, w, x, y, s);
-    case 8: return dispatch_bpl<8, XT, MIX>(bpl, w, x, y, s);
+    case 1: return dispatch_bpl<1, XT, MIX, R>(bpl, w, x, y, s);
+    case 2: return dispatch_bpl<2, XT, MIX, R>(bpl, w, x, y, s);
+    case 3: return dispatch_bpl<3, XT, MIX, R>(bpl, w, x, y, s);
+    case 4: return dispatch_bpl<4, XT, MIX, R>(bpl, w, x, y, s);
+    case 5: return dispatch_bpl<5, XT, MIX, R>(bpl, w, x, y, s);
+    case 6: return dispatch_bpl<6, XT, MIX, R>(bpl, w, x, y, s);
+    case 7: return dispatch_bpl<7, XT, MIX, R>(bpl, w, x, y, s);
+    case 8: return dispatch_bpl<8, XT, MIX, R>(bpl, w, x, y, s);
     }
     return false;
 }
@@ -300,18 +325,23 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
         const bool ok = xt == QMV_F32 ? launch_chunked<0>(m, w, x, y, s) : launch_chunked<1>(m, w, x, y, s);
         return ok ? "q4_0.lds-x-chunked.fma-mix" : nullptr;
     }
+    // two rows per wave (each staged activation block read once for both) while both rows'
+    // blocks fit in registers with the batch (m * bpl <= 4); one row per wave otherwise, on
+    // request (test override) and for the reference variant
+    const char *fp = forced_path();
+    const bool cvt = strcmp(fp, "q4_0.cvt") == 0 && m == 1 && xt == QMV_F32;
+    const bool r1 = cvt || strcmp(fp, "q4_0.r1") == 0 || m * bpl > 4;
     const size_t lds = bpl <= 2 ? lds_bytes(256, m, bpl) : lds_bytes(512, m, bpl);
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
-    const bool cvt = strcmp(forced_path(), "q4_0.cvt") == 0 && m == 1 && xt == QMV_F32;
     bool ok;
     if (cvt)
-        ok = dispatch_bpl<1, 0, false>(bpl, w, x, y, s);
-    else if (xt == QMV_F32)
-        ok = dispatch_m<0, true>(m, bpl, w, x, y, s);
+        ok = dispatch_bpl<1, 0, false, 1>(bpl, w, x, y, s);
+    else if (r1)
+        ok = xt == QMV_F32 ? dispatch_m<0, true, 1>(m, bpl, w, x, y, s) : dispatch_m<1, true, 1>(m, bpl, w, x, y, s);
     else
-        ok = dispatch_m<1, true>(m, bpl, w, x, y, s);
+        ok = xt == QMV_F32 ? dispatch_m<0, true, 2>(m, bpl, w, x, y, s) : dispatch_m<1, true, 2>(m, bpl, w, x, y, s);
     if (!ok) return nullptr;
-    return cvt ? "q4_0.lds-x.cvt-ubyte" : "q4_0.lds-x.fma-mix";
+    return cvt ? "q4_0.lds-x.cvt-ubyte" : r1 ? "q4_0.lds-x.fma-mix" : "q4_0.lds-x.fma-mix.2row";
 }
 
 }  // namespace qmv

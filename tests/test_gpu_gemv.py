@@ -54,19 +54,31 @@ def sample_rows(n, count=96, seed=0):
 Q4_SMALL = [(1, 32), (7, 64), (64, 2048 + 160), (130, 4096), (33, 11008), (300, 2048 * 8)]
 
 
+def q4_path(m, k):
+    # two rows per wave while m * (blocks per lane) <= 4, else one
+    bpl = -(-(k // 32) // 64)
+    return "q4_0.lds-x.fma-mix.2row" if m * bpl <= 4 else "q4_0.lds-x.fma-mix"
+
+
 @pytest.mark.parametrize("n,k", Q4_SMALL)
-@pytest.mark.parametrize("path", ["default", "q4_0.cvt"])
+@pytest.mark.parametrize("path", ["default", "q4_0.r1", "q4_0.cvt"])
 def test_q4_0_small_full_parity(qmv, monkeypatch, n, k, path):
     if path != "default":
         monkeypatch.setenv("QMV_FORCE_PATH", path)
-    expect = "q4_0.lds-x.cvt-ubyte" if path == "q4_0.cvt" else "q4_0.lds-x.fma-mix"
+    expect = {"default": q4_path(1, k), "q4_0.r1": "q4_0.lds-x.fma-mix", "q4_0.cvt": "q4_0.lds-x.cvt-ubyte"}[path]
     run_case(qmv, synth.FMT_Q4_0, n, k, 1, synth.DT_F32, seed=n + k, expect_path=expect)
 
 
 @pytest.mark.parametrize("m", [2, 3, 4, 8])
 @pytest.mark.parametrize("xt", [synth.DT_F32, synth.DT_BF16])
 def test_q4_0_batched(qmv, m, xt):
-    run_case(qmv, synth.FMT_Q4_0, 96, 2048, m, xt, seed=m)
+    run_case(qmv, synth.FMT_Q4_0, 97, 2048, m, xt, seed=m, expect_path=q4_path(m, 2048))
+
+
+@pytest.mark.parametrize("n,k,m", [(5, 4096, 2), (9, 4096 + 64, 1), (33, 8192, 1), (2, 2048 * 3, 1)])
+def test_q4_0_two_rows_per_wave_tails(qmv, n, k, m):
+    # odd row counts (the last wave's second row is past the end), ragged block tails
+    run_case(qmv, synth.FMT_Q4_0, n, k, m, synth.DT_F32, seed=n * k + m, expect_path=q4_path(m, k))
 
 
 @pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096), (4096, 11008)])
