@@ -76,6 +76,47 @@ QMV_DEV float dot_q4_mix(uint4 q, const float *xb) {
     return (a0 + b0) + (a1 + b1) * 0.25f;
 }
 
+// The centred sums of two rows' blocks against the same 32 activations, interleaved per
+// dword (each activation used by both rows as soon as it is read).
+QMV_DEV void dot_q4_mix2(uint4 qa, uint4 qb, const float *xb, float &sa, float &sb) {
+    const uint32_t wa[4] = {qa.x, qa.y, qa.z, qa.w}, wb[4] = {qb.x, qb.y, qb.z, qb.w};
+    const qmv_h2 off_lo = {(_Float16)-1032.f, (_Float16)-1032.f};
+    const qmv_h2 off_hi = {(_Float16)-288.f, (_Float16)-288.f};
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f, e0 = 0.f, e1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t va8 = wa[i] >> 8, vb8 = wb[i] >> 8;
+        const qmv_h2 t0 = as_h2(and_or_ordered(wa[i], 0x000F000Fu, 0x64006400u)) + off_lo;
+        const qmv_h2 t1 = as_h2(and_or_ordered(wa[i], 0x00F000F0u, 0x5C005C00u)) + off_hi;
+        const qmv_h2 t2 = as_h2(and_or_ordered(va8, 0x000F000Fu, 0x64006400u)) + off_lo;
+        const qmv_h2 t3 = as_h2(and_or_ordered(va8, 0x00F000F0u, 0x5C005C00u)) + off_hi;
+        const qmv_h2 u0 = as_h2(and_or_ordered(wb[i], 0x000F000Fu, 0x64006400u)) + off_lo;
+        const qmv_h2 u1 = as_h2(and_or_ordered(wb[i], 0x00F000F0u, 0x5C005C00u)) + off_hi;
+        const qmv_h2 u2 = as_h2(and_or_ordered(vb8, 0x000F000Fu, 0x64006400u)) + off_lo;
+        const qmv_h2 u3 = as_h2(and_or_ordered(vb8, 0x00F000F0u, 0x5C005C00u)) + off_hi;
+        const float x0 = xb[4 * i], x1 = xb[4 * i + 1], x2 = xb[4 * i + 2], x3 = xb[4 * i + 3];
+        const float y0 = xb[16 + 4 * i], y1 = xb[16 + 4 * i + 1], y2 = xb[16 + 4 * i + 2], y3 = xb[16 + 4 * i + 3];
+        a0 = fmaf((float)t0.x, x0, a0);
+        a0 = fmaf((float)t0.y, x2, a0);
+        b0 = fmaf((float)t2.x, x1, b0);
+        b0 = fmaf((float)t2.y, x3, b0);
+        a1 = fmaf((float)t1.x, y0, a1);
+        a1 = fmaf((float)t1.y, y2, a1);
+        b1 = fmaf((float)t3.x, y1, b1);
+        b1 = fmaf((float)t3.y, y3, b1);
+        c0 = fmaf((float)u0.x, x0, c0);
+        c0 = fmaf((float)u0.y, x2, c0);
+        e0 = fmaf((float)u2.x, x1, e0);
+        e0 = fmaf((float)u2.y, x3, e0);
+        c1 = fmaf((float)u1.x, y0, c1);
+        c1 = fmaf((float)u1.y, y2, c1);
+        e1 = fmaf((float)u3.x, y1, e1);
+        e1 = fmaf((float)u3.y, y3, e1);
+    }
+    sa = (a0 + b0) + (a1 + b1) * 0.25f;
+    sb = (c0 + e0) + (c1 + e1) * 0.25f;
+}
+
 // Same centred sum with byte-to-float conversions (v_cvt_f32_ubyte*), a reference variant.
 QMV_DEV float dot_q4_cvt(uint4 q, const float *xb) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -116,7 +157,9 @@ __global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_kernel(const uint8_t *
     constexpr int XPT = xchunks_per_thread(WG, M, BPL);
     const int nblk = k >> 5;
     const int total = M * (k >> 2);  // 16-byte activation chunks, m-major; 8 per block
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is uniform: made scalar, the row bases live in SGPRs and each load takes
+    // a 32-bit lane offset instead of a 64-bit address per lane
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row0 = (blockIdx.x * WAVES + wave) * R;  // this wave's rows: row0 .. row0 + R - 1
 
     float4 xv[XPT];
@@ -130,15 +173,22 @@ __global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_kernel(const uint8_t *
     // can be computed as soon as its loads have landed
     uint4 q[BPL][R];
     uint16_t dd[BPL][R];
+    const uint4 *qrow[R];
+    const uint16_t *drow[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int rowc = row0 + r < n ? row0 + r : n - 1;
+        qrow[r] = (const uint4 *)(qs + (int64_t)rowc * (k >> 1));
+        drow[r] = dsc + (int64_t)rowc * nblk;
+    }
 #pragma unroll
     for (int u = 0; u < BPL; u++) {
         int b = lane + 64 * u;
         b = b < nblk ? b : nblk - 1;
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            const int rowc = row0 + r < n ? row0 + r : n - 1;
-            q[u][r] = ld_stream16((const uint4 *)(qs + (int64_t)rowc * (k >> 1)) + b);
-            dd[u][r] = dsc[(int64_t)rowc * nblk + b];
+            q[u][r] = ld_stream16(qrow[r] + b);
+            dd[u][r] = drow[r][b];
         }
     }
     __builtin_amdgcn_sched_barrier(0);  // every load is issued before the LDS writes wait on x
@@ -164,10 +214,16 @@ __global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_kernel(const uint8_t *
             float xb[32];
 #pragma unroll
             for (int i = 0; i < 8; i++) *(float4 *)(xb + 4 * i) = sx4[(m * nblk + bc) * XS4 + i];
+            float sr[R];
+            if constexpr (R == 2 && MIX) {
+                dot_q4_mix2(q[u][0], q[u][1], xb, sr[0], sr[1]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; r++) sr[r] = MIX ? dot_q4_mix(q[u][r], xb) : dot_q4_cvt(q[u][r], xb);
+            }
 #pragma unroll
             for (int r = 0; r < R; r++) {
-                const float s = MIX ? dot_q4_mix<(R > 1)>(q[u][r], xb) : dot_q4_cvt(q[u][r], xb);
-                const float v = fmaf(h2f(dd[u][r]), s, acc[r][m]);
+                const float v = fmaf(h2f(dd[u][r]), sr[r], acc[r][m]);
                 acc[r][m] = b < nblk ? v : acc[r][m];
             }
         }
