@@ -255,13 +255,14 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
         float xsc[TPW][2];
 #pragma unroll
         for (int t = 0; t < TPW; t++) { xsc[t][0] = cur.xsv[t].x; xsc[t][1] = cur.xsv[t].y; }
+        // The prefetch is unconditional (past the end it re-reads the last step, unused): a
+        // branch around it would make the compiler wait for these loads at the join, i.e.
+        // before this step's MFMAs, costing a memory round trip per step.
         if (PD == 1) {
-            if (st + 1 < nsteps) fetch(st + 1, cur);
+            fetch(st + 1 < nsteps ? st + 1 : nsteps - 1, cur);
         } else {
-            if (st + 2 < nsteps) {
-                if (!EXP && (st & 1) == 1) cur.ra = nxt.ra;  // st + 2 odd: same half as st + 1
-                fetch(st + 2, cur);
-            }
+            if (!EXP && (st & 1) == 1) cur.ra = nxt.ra;  // st + 2 odd: same half as st + 1
+            fetch(st + 2 < nsteps ? st + 2 : nsteps - 2 + (st & 1), cur);
         }
 
 #pragma unroll
