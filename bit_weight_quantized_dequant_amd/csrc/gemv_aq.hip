@@ -30,6 +30,25 @@ using stream::WG;
 using stream::WAVES;
 using stream::XU;
 
+// fl32(h + g) for halves h of a and g of b (HI selects the high halves), and fl32(h + f) for a
+// half h of a and an fp32 f: one v_fma_mix_f32 each (h * 1.0 + g, a single rounding).
+// Written as fmaf((float)h, 1.0f, (float)g) the compiler folds the multiply and emits two
+// conversions and an add instead.
+template <int HI>
+QMV_DEV float sum_hh(uint32_t a, uint32_t b) {
+    float r;
+    if (HI) asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+    else asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+template <int HI>
+QMV_DEV float sum_hf(uint32_t a, float f) {
+    float r;
+    if (HI) asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(a), "v"(f));
+    else asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(a), "v"(f));
+    return r;
+}
+
 // Table rows of codebook b at LDS byte address tab + b * 4096 + 16 * code.
 template <int NC>
 struct AqPolicy {
@@ -69,16 +88,16 @@ struct AqPolicy {
             float wv[8];
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                wv[2 * j] = fmaf(lo_h(av[j]), 1.0f, lo_h(bv[j]));
-                wv[2 * j + 1] = fmaf(hi_h(av[j]), 1.0f, hi_h(bv[j]));
+                wv[2 * j] = sum_hh<0>(av[j], bv[j]);
+                wv[2 * j + 1] = sum_hh<1>(av[j], bv[j]);
             }
             if (NC == 3) {
                 const uint4 t = lds_ld16(row[NC - 1]);
                 const uint32_t tv[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    wv[2 * j] = fmaf(lo_h(tv[j]), 1.0f, wv[2 * j]);
-                    wv[2 * j + 1] = fmaf(hi_h(tv[j]), 1.0f, wv[2 * j + 1]);
+                    wv[2 * j] = sum_hf<0>(tv[j], wv[2 * j]);
+                    wv[2 * j + 1] = sum_hf<1>(tv[j], wv[2 * j + 1]);
                 }
             }
 #pragma unroll
@@ -186,16 +205,16 @@ __global__ void __launch_bounds__(WG) aq_ragged_kernel(const uint8_t *__restrict
                 const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    wv[2 * j] = fmaf(lo_h(av[j]), 1.0f, lo_h(bv[j]));
-                    wv[2 * j + 1] = fmaf(hi_h(av[j]), 1.0f, hi_h(bv[j]));
+                    wv[2 * j] = sum_hh<0>(av[j], bv[j]);
+                    wv[2 * j + 1] = sum_hh<1>(av[j], bv[j]);
                 }
                 if (NC == 3) {
                     const uint4 t = lds_ld16(tab_addr + 8192 + (cp[NC * g + NC - 1] << 4));
                     const uint32_t tv[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
-                        wv[2 * j] = fmaf(lo_h(tv[j]), 1.0f, wv[2 * j]);
-                        wv[2 * j + 1] = fmaf(hi_h(tv[j]), 1.0f, wv[2 * j + 1]);
+                        wv[2 * j] = sum_hf<0>(tv[j], wv[2 * j]);
+                        wv[2 * j + 1] = sum_hf<1>(tv[j], wv[2 * j + 1]);
                     }
                 }
 #pragma unroll
