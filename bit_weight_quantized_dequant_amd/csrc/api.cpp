@@ -333,8 +333,8 @@ int qmv_moe_ffn(const qmv_weights *gate, const qmv_weights *up, const qmv_weight
     if ((rc = qmv_validate(gate, 1, xt)) || (rc = qmv_validate(up, 1, xt)) ||
         (rc = qmv_validate(down, 1, QMV_F32)))
         return rc;
-    if (gate->fmt != up->fmt || gate->n != up->n || gate->k != up->k || down->k != gate->n ||
-        down->n != gate->k)
+    if (gate->fmt != QMV_CB4 || up->fmt != QMV_CB4 || down->fmt != QMV_CB4) return QMV_ERR_FORMAT;
+    if (gate->n != up->n || gate->k != up->k || down->k != gate->n || down->n != gate->k)
         return QMV_ERR_SHAPE;
     if (n_experts < 1) return QMV_ERR_SHAPE;
     if (n_ids < 1 || n_ids > 64) return QMV_ERR_BATCH;

@@ -212,8 +212,9 @@ int qmm_unregister_plane(const qmv_weights *w);
  * with SiLU(z) = z / (1 + e^-z).  No routing weights are applied; the caller
  * combines y[j].
  *   gate, up : descriptors of expert 0 (n = d_ff, k = d_model); down: of expert 0
- *              (n = d_model, k = d_ff).  Expert e's planes follow expert 0's
- *              contiguously: plane(e) = plane(0) + e * qmv_plane_bytes(...).
+ *              (n = d_model, k = d_ff); all three QMV_CB4 (QMV_ERR_FORMAT otherwise).
+ *              Expert e's planes follow expert 0's contiguously:
+ *              plane(e) = plane(0) + e * qmv_plane_bytes(...).
  *   n_experts: experts stored; ids: device int32 [n_ids]; ids outside
  *              [0, n_experts) produce NaN rows (their loads are redirected to
  *              expert 0, which stays in bounds; none of those bytes is used).

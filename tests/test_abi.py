@@ -99,6 +99,11 @@ def test_calls_reject_bad_arguments_before_any_gpu_work():
     assert L.qmm_gemm(q6.ref, 4, 1 << 20, 1 << 20, 1 << 20, need - 1, None) == -7
     assert L.qmm_quant_act(1 << 20, 2, 48, 1 << 20, 1 << 20, None) == -2
     assert L.qmv_moe_ffn(None, None, None, 1, None, 1, None, 0, None, None, None) == -1
+    g, u, d = _fake(qmv.CB4, 256, 512), _fake(qmv.CB4, 256, 512), _fake(qmv.CB4, 512, 256)
+    ga = _fake(qmv.AQ2X8, 256, 512)
+    args = (1, 1 << 20, 1, 1 << 20, 0, 1 << 20, 1 << 20, None)
+    assert L.qmv_moe_ffn(ga.ref, u.ref, d.ref, *args) == -3        # CB4 experts only
+    assert L.qmv_moe_ffn(g.ref, u.ref, _fake(qmv.CB4, 512, 128).ref, *args) == -2  # down k != d_ff
 
 
 def test_plane_calls_check_arguments_before_any_gpu_work(monkeypatch):
