@@ -110,7 +110,18 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave % WN, wm = wave / WN;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    // Workgroups are dealt to the eight XCDs round-robin in dispatch order (x fastest).
+    // Remap so that XCD x takes one contiguous run of row tiles with all their column
+    // tiles: the column tiles that share a weight tile then share one L2.
+    int n0, m0;
+    {
+        const int nrt = gridDim.x, nct = gridDim.y, ntiles = nrt * nct;
+        const int b = blockIdx.x + nrt * blockIdx.y;
+        const int xcd = b & 7, q = b >> 3, base = ntiles >> 3, rem = ntiles & 7;
+        const int t = xcd * base + min(xcd, rem) + q;
+        n0 = (t / nct) * BN;
+        m0 = (t % nct) * BM;
+    }
     const int nsteps = K / KS, nblk = K >> 5;
     const int li = lane & 31, lg = lane >> 5;
 
