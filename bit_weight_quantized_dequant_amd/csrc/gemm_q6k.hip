@@ -375,16 +375,18 @@ const char *launch_gemm(const qmv_weights *w, int m, const int8_t *plane, const 
     const int64_t n = w->n;
     // 64-row tiles when they give at least two workgroups per CU, else 32-row tiles
     const int64_t tiles64 = ((n + 63) / 64) * ((m + BM - 1) / BM);
-    const bool wide = tiles64 >= 2 * (int64_t)device_info().num_cus;
+    const char *fp = forced_path();  // test-only overrides of the tile width and prefetch distance
+    const bool wide = strcmp(fp, "gemm.w64") == 0 ? true : strcmp(fp, "gemm.w32") == 0 ? false
+                                                      : tiles64 >= 2 * (int64_t)device_info().num_cus;
     if (partials) {
         if (wide) launch_tiles<2, true, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
         else launch_tiles<1, true, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
         return "gemm.q6k.mfma-i8-32x32x32.hl-split.partials";
     }
-    // 64-row tiles keep the loads of the next step in flight (their register budget allows
-    // three workgroups per CU); 32-row tiles have registers for two steps ahead
-    const char *fp = forced_path();  // test-only override of the prefetch distance
-    const int pd = strcmp(fp, "gemm.pd1") == 0 ? 1 : strcmp(fp, "gemm.pd2") == 0 ? 2 : (wide ? 1 : 2);
+    // 64-row tiles that expand codes keep the loads of the next step in flight (their
+    // register budget allows three workgroups per CU); 32-row tiles, and 64-row tiles that
+    // copy registered planes (fewer registers per step), fetch two steps ahead
+    const int pd = strcmp(fp, "gemm.pd1") == 0 ? 1 : strcmp(fp, "gemm.pd2") == 0 ? 2 : (wide && !EXP ? 1 : 2);
     if (wide) {
         if (pd == 1) launch_tiles<2, false, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
         else launch_tiles<2, false, 2, EXP>(w, m, plane, xq, xs, y, partials, s);

@@ -148,11 +148,11 @@ def test_plane_holds_the_exact_hi_lo_split(qmv):
 
 @pytest.mark.parametrize("n,k,m", [(64, 512, 128), (70, 768, 45), (257, 2048, 130), (4096, 1024, 512), (3, 256, 1),
                                    (8192, 256, 512)])
-@pytest.mark.parametrize("force", ["", "gemm.pd1", "gemm.pd2"])
+@pytest.mark.parametrize("force", ["", "gemm.pd1", "gemm.pd2", "gemm.w64", "gemm.w32"])
 def test_gemm_with_plane_is_byte_identical(qmv, monkeypatch, n, k, m, force):
     # outputs and int32 partials with the plane equal those of the in-kernel expansion bit
-    # for bit (the expansion is an integer transform), for both tile shapes and both
-    # prefetch distances; the partials also equal the oracle's
+    # for bit (the expansion is an integer transform), for both tile widths (forced either
+    # way on every shape) and both prefetch distances; the partials also equal the oracle's
     import torch
     monkeypatch.setenv("QMV_FORCE_PATH", force)
     w, x, W, xd = _setup(qmv, n, k, m, seed=n + 7 * m)
