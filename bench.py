@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--only-primary", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--secondary", default="q6_K_gemv,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm",
+    ap.add_argument("--secondary", default="q6_K_gemv,q4_0_batch,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm",
                     help="comma-separated secondary workloads to run")
     return ap.parse_args()
 
@@ -365,6 +365,10 @@ def main():
         if "q6_K_gemv" in want:
             sec["q6_K_gemv"] = gemv_workload(qmv, synth.FMT_Q6_K, [(256, 1024)], 1, synth.DT_F32, 200,
                                              "q6_K GEMV batch 1, 256x1024, fp32 x")
+        for b in ((2, 4, 8) if "q4_0_batch" in want else ()):
+            sec[f"q4_0_gemv_b{b}"] = gemv_workload(qmv, synth.FMT_Q4_0, [(4096, 4096), (11008, 4096), (4096, 11008)],
+                                                   b, synth.DT_F32, 50,
+                                                   f"q4_0 GEMV batch {b}, Llama-7B decode shapes, fp32 x")
         if "cb4_moe" in want:
             sec["cb4_moe"] = moe_workload(qmv, 64, "4-bit codebook MoE FFN, batch 1, 256 experts top-8, "
                                                    "gate/up 2048x7168 + down 7168x2048, bf16 x")

@@ -376,7 +376,13 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
     const int64_t n = w->n, k = w->k, nblk = k / 32;
     const int bpl = (int)((nblk + 63) / 64);
     if (n > INT32_MAX || k > INT32_MAX / 8) return nullptr;
-    if (bpl > 8 || (int64_t)m * k > 16384) {  // activations staged in K chunks
+    const char *fp = forced_path();
+    const bool force_r1 = strcmp(fp, "q4_0.r1") == 0;
+    // K-chunked kernel: when the activations do not fit one workgroup's LDS, and for batches
+    // beyond the two-row one-shot kernel (m * bpl > 4): there the one-row one-shot kernel,
+    // holding every block of m rows' dots in registers, loses 10-40 % to it (measured), and
+    // more where it spills.  The one-row kernel stays reachable for m > 1 as a test override.
+    if (bpl > 8 || (int64_t)m * k > 16384 || strcmp(fp, "q4_0.chunked") == 0 || (m > 1 && m * bpl > 4 && !force_r1)) {
         if ((int64_t)m * 64 * XS * (int64_t)sizeof(float) > device_info().lds_per_block) return nullptr;
         const bool ok = xt == QMV_F32 ? launch_chunked<0>(m, w, x, y, s) : launch_chunked<1>(m, w, x, y, s);
         return ok ? "q4_0.lds-x-chunked.fma-mix" : nullptr;
@@ -384,9 +390,8 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
     // two rows per wave (each staged activation block read once for both) while both rows'
     // blocks fit in registers with the batch (m * bpl <= 4); one row per wave otherwise, on
     // request (test override) and for the reference variant
-    const char *fp = forced_path();
     const bool cvt = strcmp(fp, "q4_0.cvt") == 0 && m == 1 && xt == QMV_F32;
-    const bool r1 = cvt || strcmp(fp, "q4_0.r1") == 0 || m * bpl > 4;
+    const bool r1 = cvt || force_r1 || m * bpl > 4;
     const size_t lds = bpl <= 2 ? lds_bytes(256, m, bpl) : lds_bytes(512, m, bpl);
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
     bool ok;

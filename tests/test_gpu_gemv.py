@@ -55,17 +55,21 @@ Q4_SMALL = [(1, 32), (7, 64), (64, 2048 + 160), (130, 4096), (33, 11008), (300, 
 
 
 def q4_path(m, k):
-    # two rows per wave while m * (blocks per lane) <= 4, else one
+    # the K-chunked kernel when x does not fit one workgroup's LDS or the batch is beyond the
+    # two-row kernel; else two rows per wave while m * (blocks per lane) <= 4, one for m = 1
     bpl = -(-(k // 32) // 64)
+    if bpl > 8 or m * k > 16384 or (m > 1 and m * bpl > 4):
+        return "q4_0.lds-x-chunked.fma-mix"
     return "q4_0.lds-x.fma-mix.2row" if m * bpl <= 4 else "q4_0.lds-x.fma-mix"
 
 
 @pytest.mark.parametrize("n,k", Q4_SMALL)
-@pytest.mark.parametrize("path", ["default", "q4_0.r1", "q4_0.cvt"])
+@pytest.mark.parametrize("path", ["default", "q4_0.r1", "q4_0.cvt", "q4_0.chunked"])
 def test_q4_0_small_full_parity(qmv, monkeypatch, n, k, path):
     if path != "default":
         monkeypatch.setenv("QMV_FORCE_PATH", path)
-    expect = {"default": q4_path(1, k), "q4_0.r1": "q4_0.lds-x.fma-mix", "q4_0.cvt": "q4_0.lds-x.cvt-ubyte"}[path]
+    expect = {"default": q4_path(1, k), "q4_0.r1": "q4_0.lds-x.fma-mix", "q4_0.cvt": "q4_0.lds-x.cvt-ubyte",
+              "q4_0.chunked": "q4_0.lds-x-chunked.fma-mix"}[path]
     run_case(qmv, synth.FMT_Q4_0, n, k, 1, synth.DT_F32, seed=n + k, expect_path=expect)
 
 
@@ -73,6 +77,13 @@ def test_q4_0_small_full_parity(qmv, monkeypatch, n, k, path):
 @pytest.mark.parametrize("xt", [synth.DT_F32, synth.DT_BF16])
 def test_q4_0_batched(qmv, m, xt):
     run_case(qmv, synth.FMT_Q4_0, 97, 2048, m, xt, seed=m, expect_path=q4_path(m, 2048))
+
+
+@pytest.mark.parametrize("n,k,m", [(97, 2048, 8), (65, 4096, 3), (33, 3072, 5), (17, 8192, 2)])
+def test_q4_0_batched_one_row_kernel_on_request(qmv, monkeypatch, n, k, m):
+    # the batches the default routes to the K-chunked kernel, through the one-row kernel
+    monkeypatch.setenv("QMV_FORCE_PATH", "q4_0.r1")
+    run_case(qmv, synth.FMT_Q4_0, n, k, m, synth.DT_F32, seed=n + m, expect_path="q4_0.lds-x.fma-mix")
 
 
 @pytest.mark.parametrize("n,k,m", [(5, 4096, 2), (9, 4096 + 64, 1), (33, 8192, 1), (2, 2048 * 3, 1)])
@@ -122,8 +133,7 @@ def test_q4_0_deterministic_and_permutation_equivariant(qmv):
 def test_q4_0_k_chunked_batches(qmv, n, k, m, xt):
     # activations beyond one workgroup's LDS (m * k > 16384, or k > 16384) go through the
     # K-chunked kernel; the ragged last chunk and row tails are included
-    path = "q4_0.lds-x-chunked.fma-mix" if (m * k > 16384 or k > 16384) else "q4_0.lds-x.fma-mix"
-    run_case(qmv, synth.FMT_Q4_0, n, k, m, xt, seed=n + k + m, expect_path=path)
+    run_case(qmv, synth.FMT_Q4_0, n, k, m, xt, seed=n + k + m, expect_path=q4_path(m, k))
 
 
 def test_q4_0_chunked_unit_vector_returns_column_exactly(qmv):
