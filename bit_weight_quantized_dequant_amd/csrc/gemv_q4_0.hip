@@ -240,23 +240,23 @@ __global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_kernel(const uint8_t *
         }
 }
 
-// Batches whose activations do not fit one workgroup's LDS (m * k > 16384) and rows longer
-// than 16384: K is walked in chunks of 2048 (64 blocks, one per lane).  The wave's block of
-// chunk c + 1 is requested before the dots of chunk c, and each chunk's activations are
-// staged per workgroup of 4 rows, with the same branch-free loads (clamped indices) as the
-// one-shot kernel.
+// Batches (m >= 2) and rows longer than 16384: K is walked in chunks of 2048 (64 blocks, one
+// per lane).  The wave's block of chunk c + 1 is requested before the dots of chunk c, and
+// each chunk's activations (m x 2048) are staged once per workgroup, with the same
+// branch-free loads (clamped indices) as the one-shot kernel; each looked-up block serves
+// all m batch rows.
 constexpr int KC = 2048;
 
-template <int M, int XT>
-__global__ void __launch_bounds__(256) gemv_q4_0_chunked_kernel(const uint8_t *__restrict__ qs,
-                                                                const uint16_t *__restrict__ dsc,
-                                                                const void *__restrict__ x,
-                                                                float *__restrict__ y, int n, int k) {
+template <int WG, int M, int XT>
+__global__ void __launch_bounds__(WG) gemv_q4_0_chunked_kernel(const uint8_t *__restrict__ qs,
+                                                               const uint16_t *__restrict__ dsc,
+                                                               const void *__restrict__ x,
+                                                               float *__restrict__ y, int n, int k) {
     extern __shared__ float4 sx4[];
-    constexpr int WG = 256, XPT = M * (KC / 4) / WG;
+    constexpr int WAVES = WG / 64, NX = M * (KC / 4), XPT = (NX + WG - 1) / WG;  // NX: chunk's x pieces
     const int nblk = k >> 5, nch = (nblk + 63) >> 6;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row = blockIdx.x * 4 + wave;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row = blockIdx.x * WAVES + wave;
     const int rowc = row < n ? row : n - 1;
     const uint4 *qr = (const uint4 *)(qs + (int64_t)rowc * (k >> 1));
     const uint16_t *dr = dsc + (int64_t)rowc * nblk;
@@ -272,7 +272,8 @@ __global__ void __launch_bounds__(256) gemv_q4_0_chunked_kernel(const uint8_t *_
         float4 xv[XPT];
 #pragma unroll
         for (int j = 0; j < XPT; j++) {
-            const int cc = threadIdx.x + j * WG, m = cc >> 9, e = cc & 511;
+            const int cc = threadIdx.x + j * WG, e = cc & 511;
+            const int m = (cc >> 9) < M ? cc >> 9 : M - 1;  // pieces past the batch re-read row M - 1
             xv[j] = ld_act4<XT>(x, (int64_t)m * k + k0 + 4 * (e < kq ? e : kq - 1));
         }
         int bn = (c + 1) * 64 + lane;  // next chunk's block (clamped on the last chunk)
@@ -284,7 +285,7 @@ __global__ void __launch_bounds__(256) gemv_q4_0_chunked_kernel(const uint8_t *_
 #pragma unroll
         for (int j = 0; j < XPT; j++) {
             const int cc = threadIdx.x + j * WG, m = cc >> 9, e = cc & 511;
-            sx4[(m * 64 + (e >> 3)) * XS4 + (e & 7)] = xv[j];
+            if (XPT * WG == NX || cc < NX) sx4[(m * 64 + (e >> 3)) * XS4 + (e & 7)] = xv[j];
         }
         __syncthreads();
         const int b = c * 64 + lane;
@@ -307,14 +308,17 @@ __global__ void __launch_bounds__(256) gemv_q4_0_chunked_kernel(const uint8_t *_
     }
 }
 
+// 512-thread workgroups: each chunk's activations are staged once for eight rows (with four
+// rows per workgroup the batch-8 staging traffic outweighed the weights).
 template <int XT>
 bool launch_chunked(int m, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
+    constexpr int WG = 512;
     const int n = (int)w->n, k = (int)w->k;
-    const dim3 grid((n + 3) / 4);
+    const dim3 grid((n + WG / 64 - 1) / (WG / 64));
     const size_t lds = (size_t)m * 64 * XS * sizeof(float);
 #define QMV_Q4C(MM)                                                                                          \
     case MM:                                                                                                 \
-        hipLaunchKernelGGL((gemv_q4_0_chunked_kernel<MM, XT>), grid, dim3(256), lds, s,                      \
+        hipLaunchKernelGGL((gemv_q4_0_chunked_kernel<WG, MM, XT>), grid, dim3(WG), lds, s,                   \
                            (const uint8_t *)w->codes, (const uint16_t *)w->scales, x, y, n, k);             \
         return true;
     switch (m) { QMV_Q4C(1) QMV_Q4C(2) QMV_Q4C(3) QMV_Q4C(4) QMV_Q4C(5) QMV_Q4C(6) QMV_Q4C(7) QMV_Q4C(8) }
@@ -354,21 +358,6 @@ bool dispatch_bpl(int bpl, const qmv_weights *w, const void *x, float *y, hipStr
     return false;
 }
 
-template <int XT, bool MIX, int R>
-bool dispatch_m(int m, int bpl, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
-    switch (m) {
-    case 1: return dispatch_bpl<1, XT, MIX, R>(bpl, w, x, y, s);
-    case 2: return dispatch_bpl<2, XT, MIX, R>(bpl, w, x, y, s);
-    case 3: return dispatch_bpl<3, XT, MIX, R>(bpl, w, x, y, s);
-    case 4: return dispatch_bpl<4, XT, MIX, R>(bpl, w, x, y, s);
-    case 5: return dispatch_bpl<5, XT, MIX, R>(bpl, w, x, y, s);
-    case 6: return dispatch_bpl<6, XT, MIX, R>(bpl, w, x, y, s);
-    case 7: return dispatch_bpl<7, XT, MIX, R>(bpl, w, x, y, s);
-    case 8: return dispatch_bpl<8, XT, MIX, R>(bpl, w, x, y, s);
-    }
-    return false;
-}
-
 }  // namespace
 
 const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt, float *y,
@@ -377,30 +366,27 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
     const int bpl = (int)((nblk + 63) / 64);
     if (n > INT32_MAX || k > INT32_MAX / 8) return nullptr;
     const char *fp = forced_path();
-    const bool force_r1 = strcmp(fp, "q4_0.r1") == 0;
-    // K-chunked kernel: when the activations do not fit one workgroup's LDS, and for batches
-    // beyond the two-row one-shot kernel (m * bpl > 4): there the one-row one-shot kernel,
-    // holding every block of m rows' dots in registers, loses 10-40 % to it (measured), and
-    // more where it spills.  The one-row kernel stays reachable for m > 1 as a test override.
-    if (bpl > 8 || (int64_t)m * k > 16384 || strcmp(fp, "q4_0.chunked") == 0 || (m > 1 && m * bpl > 4 && !force_r1)) {
+    // Batches, and rows longer than 16384, go through the K-chunked kernel: for m >= 2 it beats
+    // the one-shot kernels, which hold m rows' dots for every block of a lane in registers.
+    if (bpl > 8 || m > 1 || strcmp(fp, "q4_0.chunked") == 0) {
         if ((int64_t)m * 64 * XS * (int64_t)sizeof(float) > device_info().lds_per_block) return nullptr;
         const bool ok = xt == QMV_F32 ? launch_chunked<0>(m, w, x, y, s) : launch_chunked<1>(m, w, x, y, s);
         return ok ? "q4_0.lds-x-chunked.fma-mix" : nullptr;
     }
-    // two rows per wave (each staged activation block read once for both) while both rows'
-    // blocks fit in registers with the batch (m * bpl <= 4); one row per wave otherwise, on
-    // request (test override) and for the reference variant
-    const bool cvt = strcmp(fp, "q4_0.cvt") == 0 && m == 1 && xt == QMV_F32;
-    const bool r1 = cvt || force_r1 || m * bpl > 4;
-    const size_t lds = bpl <= 2 ? lds_bytes(256, m, bpl) : lds_bytes(512, m, bpl);
+    // batch 1: two rows per wave (each staged activation block read once for both) while both
+    // rows' blocks fit in registers (bpl <= 4); one row per wave otherwise, on request (test
+    // override) and for the reference variant
+    const bool cvt = strcmp(fp, "q4_0.cvt") == 0 && xt == QMV_F32;
+    const bool r1 = cvt || strcmp(fp, "q4_0.r1") == 0 || bpl > 4;
+    const size_t lds = bpl <= 2 ? lds_bytes(256, 1, bpl) : lds_bytes(512, 1, bpl);
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
     bool ok;
     if (cvt)
         ok = dispatch_bpl<1, 0, false, 1>(bpl, w, x, y, s);
     else if (r1)
-        ok = xt == QMV_F32 ? dispatch_m<0, true, 1>(m, bpl, w, x, y, s) : dispatch_m<1, true, 1>(m, bpl, w, x, y, s);
+        ok = xt == QMV_F32 ? dispatch_bpl<1, 0, true, 1>(bpl, w, x, y, s) : dispatch_bpl<1, 1, true, 1>(bpl, w, x, y, s);
     else
-        ok = xt == QMV_F32 ? dispatch_m<0, true, 2>(m, bpl, w, x, y, s) : dispatch_m<1, true, 2>(m, bpl, w, x, y, s);
+        ok = xt == QMV_F32 ? dispatch_bpl<1, 0, true, 2>(bpl, w, x, y, s) : dispatch_bpl<1, 1, true, 2>(bpl, w, x, y, s);
     if (!ok) return nullptr;
     return cvt ? "q4_0.lds-x.cvt-ubyte" : r1 ? "q4_0.lds-x.fma-mix" : "q4_0.lds-x.fma-mix.2row";
 }

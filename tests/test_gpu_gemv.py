@@ -55,12 +55,12 @@ Q4_SMALL = [(1, 32), (7, 64), (64, 2048 + 160), (130, 4096), (33, 11008), (300, 
 
 
 def q4_path(m, k):
-    # the K-chunked kernel when x does not fit one workgroup's LDS or the batch is beyond the
-    # two-row kernel; else two rows per wave while m * (blocks per lane) <= 4, one for m = 1
+    # batches and rows longer than 16384 go through the K-chunked kernel; batch 1 through the
+    # one-shot kernel, two rows per wave while the blocks per lane are at most 4
     bpl = -(-(k // 32) // 64)
-    if bpl > 8 or m * k > 16384 or (m > 1 and m * bpl > 4):
+    if bpl > 8 or m > 1:
         return "q4_0.lds-x-chunked.fma-mix"
-    return "q4_0.lds-x.fma-mix.2row" if m * bpl <= 4 else "q4_0.lds-x.fma-mix"
+    return "q4_0.lds-x.fma-mix.2row" if bpl <= 4 else "q4_0.lds-x.fma-mix"
 
 
 @pytest.mark.parametrize("n,k", Q4_SMALL)
@@ -77,13 +77,6 @@ def test_q4_0_small_full_parity(qmv, monkeypatch, n, k, path):
 @pytest.mark.parametrize("xt", [synth.DT_F32, synth.DT_BF16])
 def test_q4_0_batched(qmv, m, xt):
     run_case(qmv, synth.FMT_Q4_0, 97, 2048, m, xt, seed=m, expect_path=q4_path(m, 2048))
-
-
-@pytest.mark.parametrize("n,k,m", [(97, 2048, 8), (65, 4096, 3), (33, 3072, 5), (17, 8192, 2)])
-def test_q4_0_batched_one_row_kernel_on_request(qmv, monkeypatch, n, k, m):
-    # the batches the default routes to the K-chunked kernel, through the one-row kernel
-    monkeypatch.setenv("QMV_FORCE_PATH", "q4_0.r1")
-    run_case(qmv, synth.FMT_Q4_0, n, k, m, synth.DT_F32, seed=n + m, expect_path="q4_0.lds-x.fma-mix")
 
 
 @pytest.mark.parametrize("n,k,m", [(5, 4096, 2), (9, 4096 + 64, 1), (33, 8192, 1), (2, 2048 * 3, 1)])
