@@ -16,9 +16,12 @@
 //     magnitude (the sum then fits 24 bits), else rounded relative to the partial sum;
 //     an exactly cancelling pair gives 0.  The weight is applied to every batch row with
 //     an fp32 FMA (decoded once for all rows);
-//   * the 64 lane partials are summed with DPP and scaled by s[n].
+//   * the 64 lane partials are summed with DPP and scaled by s[n];
+//   * batches run two rows per wave: each activation read from LDS serves both rows.
 // Rows whose length is not a multiple of 64 take a plain kernel (byte loads, one K chunk
 // staged at a time).
+#include <cstring>
+
 #include "device_common.h"
 #include "gemv_stream.h"
 #include "qmv_internal.h"
@@ -49,78 +52,89 @@ QMV_DEV float sum_hf(uint32_t a, float f) {
     return r;
 }
 
-// Table rows of codebook b at LDS byte address tab + b * 4096 + 16 * code.
-template <int NC>
+// Table rows of codebook b at LDS byte address tab + b * 4096 + 16 * code.  R rows per wave:
+// lane l owns unit l of each of the R rows, and each activation read serves all of them.
+template <int NC, int RR>
 struct AqPolicy {
+    static constexpr int R = RR;  // rows per wave
     struct Codes {
-        uint32_t w[2 * NC];  // byte NC * g + b = code b of group g
+        uint32_t w[R][2 * NC];  // row r: byte NC * g + b = code b of group g
     };
-    const uint8_t *crow;  // this row's codes
-    uint32_t tab;         // LDS byte address of the tables
+    const uint8_t *crow[R];  // the rows' codes
+    uint32_t tab;            // LDS byte address of the tables
 
     __device__ __forceinline__ void load(Codes &c, int unit) const {
-        const uint8_t *p = crow + (int64_t)unit * (8 * NC);
-        if (NC == 2) {
-            const uint4 v = ld_stream16(p);
-            c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
-        } else {
 #pragma unroll
-            for (int i = 0; i < NC; i++) {
-                const u32x2 v = __builtin_nontemporal_load((const u32x2 *)(p + 8 * i));
-                c.w[2 * i] = v.x;
-                c.w[2 * i + 1] = v.y;
+        for (int r = 0; r < R; r++) {
+            const uint8_t *p = crow[r] + (int64_t)unit * (8 * NC);
+            if (NC == 2) {
+                const uint4 v = ld_stream16(p);
+                c.w[r][0] = v.x; c.w[r][1] = v.y; c.w[r][2] = v.z; c.w[r][3] = v.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < NC; i++) {
+                    const u32x2 v = __builtin_nontemporal_load((const u32x2 *)(p + 8 * i));
+                    c.w[r][2 * i] = v.x;
+                    c.w[r][2 * i + 1] = v.y;
+                }
             }
         }
     }
 
     template <int M>
-    __device__ __forceinline__ void dot(const Codes &c, const float *xu, float (&s)[M]) const {
+    __device__ __forceinline__ void dot(const Codes &c, const float *xu, float (&s)[R * M]) const {
 #pragma unroll
         for (int g = 0; g < 8; g++) {
-            uint32_t row[NC];
+            float wv[R][8];
 #pragma unroll
-            for (int b = 0; b < NC; b++) {
-                const int bi = NC * g + b;
-                row[b] = tab + b * 4096 + (((c.w[bi >> 2] >> (8 * (bi & 3))) & 0xFFu) << 4);
-            }
-            const uint4 a = lds_ld16(row[0]), b = lds_ld16(row[1]);
-            const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-            float wv[8];
+            for (int r = 0; r < R; r++) {
+                uint32_t row[NC];
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                wv[2 * j] = sum_hh<0>(av[j], bv[j]);
-                wv[2 * j + 1] = sum_hh<1>(av[j], bv[j]);
-            }
-            if (NC == 3) {
-                const uint4 t = lds_ld16(row[NC - 1]);
-                const uint32_t tv[4] = {t.x, t.y, t.z, t.w};
+                for (int b = 0; b < NC; b++) {
+                    const int bi = NC * g + b;
+                    row[b] = tab + b * 4096 + (((c.w[r][bi >> 2] >> (8 * (bi & 3))) & 0xFFu) << 4);
+                }
+                const uint4 a = lds_ld16(row[0]), b = lds_ld16(row[1]);
+                const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    wv[2 * j] = sum_hf<0>(tv[j], wv[2 * j]);
-                    wv[2 * j + 1] = sum_hf<1>(tv[j], wv[2 * j + 1]);
+                    wv[r][2 * j] = sum_hh<0>(av[j], bv[j]);
+                    wv[r][2 * j + 1] = sum_hh<1>(av[j], bv[j]);
+                }
+                if (NC == 3) {
+                    const uint4 t = lds_ld16(row[NC - 1]);
+                    const uint32_t tv[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        wv[r][2 * j] = sum_hf<0>(tv[j], wv[r][2 * j]);
+                        wv[r][2 * j + 1] = sum_hf<1>(tv[j], wv[r][2 * j + 1]);
+                    }
                 }
             }
 #pragma unroll
             for (int m = 0; m < M; m++) {
                 const float *xg = xu + m * stream::XBUF + 8 * g;
                 const float4 x0 = *(const float4 *)xg, x1 = *(const float4 *)(xg + 4);
-                float t = s[m];
-                t = fmaf(wv[0], x0.x, t);
-                t = fmaf(wv[1], x0.y, t);
-                t = fmaf(wv[2], x0.z, t);
-                t = fmaf(wv[3], x0.w, t);
-                t = fmaf(wv[4], x1.x, t);
-                t = fmaf(wv[5], x1.y, t);
-                t = fmaf(wv[6], x1.z, t);
-                t = fmaf(wv[7], x1.w, t);
-                s[m] = t;
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    float t = s[r * M + m];
+                    t = fmaf(wv[r][0], x0.x, t);
+                    t = fmaf(wv[r][1], x0.y, t);
+                    t = fmaf(wv[r][2], x0.z, t);
+                    t = fmaf(wv[r][3], x0.w, t);
+                    t = fmaf(wv[r][4], x1.x, t);
+                    t = fmaf(wv[r][5], x1.y, t);
+                    t = fmaf(wv[r][6], x1.z, t);
+                    t = fmaf(wv[r][7], x1.w, t);
+                    s[r * M + m] = t;
+                }
             }
         }
     }
 };
 
 // LDS layout: the activation buffers (xfloats floats), then the NC tables.
-template <int NC, int M, int XT>
+template <int NC, int M, int R, int XT>
 __global__ void __launch_bounds__(WG) aq_stream_kernel(const uint8_t *__restrict__ codes,
                                                        const uint16_t *__restrict__ cbk,
                                                        const uint16_t *__restrict__ srow,
@@ -129,9 +143,8 @@ __global__ void __launch_bounds__(WG) aq_stream_kernel(const uint8_t *__restrict
     extern __shared__ float4 lds4[];
     float *sx = (float *)lds4;
     uint4 *tab = (uint4 *)(sx + xfloats);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row = blockIdx.x * WAVES + wave;
-    const int rowc = row < n ? row : n - 1;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = (blockIdx.x * WAVES + wave) * R;  // this wave's rows: row0 .. row0 + R - 1
 
     // NC * 256 table rows of 16 bytes; threads past the end rewrite the last row
     const uint4 *src = (const uint4 *)cbk;
@@ -142,17 +155,27 @@ __global__ void __launch_bounds__(WG) aq_stream_kernel(const uint8_t *__restrict
         tab[ec] = src[ec];
     }
 
-    AqPolicy<NC> pol{codes + (int64_t)rowc * (k >> 3) * NC, (uint32_t)(uintptr_t)tab};
-    float acc[M];
+    AqPolicy<NC, R> pol;
+    pol.tab = (uint32_t)(uintptr_t)tab;
 #pragma unroll
-    for (int m = 0; m < M; m++) acc[m] = 0.f;
-    stream::walk_row<AqPolicy<NC>, M, XT>(pol, x, k, sx, acc);
+    for (int r = 0; r < R; r++) {
+        const int rowc = row0 + r < n ? row0 + r : n - 1;
+        pol.crow[r] = codes + (int64_t)rowc * (k >> 3) * NC;
+    }
+    float acc[R * M];
+#pragma unroll
+    for (int m = 0; m < R * M; m++) acc[m] = 0.f;
+    stream::walk_row<AqPolicy<NC, R>, M, XT>(pol, x, k, sx, acc);
 
-    const float s = h2f(srow[rowc]);
 #pragma unroll
-    for (int m = 0; m < M; m++) {
-        const float t = wave_sum(acc[m]);
-        if (lane == 0 && row < n) y[(int64_t)m * n + row] = s * t;
+    for (int r = 0; r < R; r++) {
+        const int row = row0 + r;
+        const float s = h2f(srow[row < n ? row : n - 1]);
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float t = wave_sum(acc[r * M + m]);
+            if (lane == 0 && row < n) y[(int64_t)m * n + row] = s * t;
+        }
     }
 }
 
@@ -237,14 +260,31 @@ __global__ void __launch_bounds__(WG) aq_ragged_kernel(const uint8_t *__restrict
 size_t stream_lds(int nc, int m, int64_t k) { return stream::x_lds_bytes(m, k) + (size_t)nc * 4096; }
 size_t ragged_lds(int nc, int m) { return (size_t)nc * 4096 + (size_t)m * 64 * XU * 4; }
 
+template <int NC, int M, int R, int XT>
+void launch_stream(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
+    const int n = (int)w->n, k = (int)w->k;
+    hipLaunchKernelGGL((aq_stream_kernel<NC, M, R, XT>), dim3((n + WAVES * R - 1) / (WAVES * R)), dim3(WG),
+                       stream_lds(NC, M, k), s, (const uint8_t *)w->codes, (const uint16_t *)w->codebook,
+                       (const uint16_t *)w->scales, x, y, n, k, (int)(stream::x_lds_bytes(M, k) / 4));
+}
+
+// Rows per wave of the streaming kernel: two for batches (each activation read from LDS
+// serves both rows, which the batch's LDS traffic needs), one for batch 1; test overrides
+// "aq.r1" / "aq.r2" force either.
+int stream_rows(int m) {
+    const char *fp = forced_path();
+    if (strcmp(fp, "aq.r1") == 0) return 1;
+    if (strcmp(fp, "aq.r2") == 0) return 2;
+    return m > 1 ? 2 : 1;
+}
+
 template <int NC, int M, int XT>
 void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     const int n = (int)w->n, k = (int)w->k;
     const dim3 grid((n + WAVES - 1) / WAVES);
     if (k % 64 == 0) {
-        hipLaunchKernelGGL((aq_stream_kernel<NC, M, XT>), grid, dim3(WG), stream_lds(NC, M, k), s,
-                           (const uint8_t *)w->codes, (const uint16_t *)w->codebook,
-                           (const uint16_t *)w->scales, x, y, n, k, (int)(stream::x_lds_bytes(M, k) / 4));
+        if (stream_rows(M) == 2) launch_stream<NC, M, 2, XT>(w, x, y, s);
+        else launch_stream<NC, M, 1, XT>(w, x, y, s);
     } else {
         hipLaunchKernelGGL((aq_ragged_kernel<NC, M, XT>), grid, dim3(WG), ragged_lds(NC, M), s,
                            (const uint8_t *)w->codes, (const uint16_t *)w->codebook,
@@ -281,8 +321,10 @@ const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, f
     else
         ok = xt == QMV_F32 ? dispatch_m<3, 0>(m, w, x, y, s) : dispatch_m<3, 1>(m, w, x, y, s);
     if (!ok) return nullptr;
-    if (nc == 2) return str ? "aq2x8.stream.lds-codebook.fma-mix" : "aq2x8.ragged.lds-codebook.fma-mix";
-    return str ? "aq3x8.stream.lds-codebook.fma-mix" : "aq3x8.ragged.lds-codebook.fma-mix";
+    if (!str) return nc == 2 ? "aq2x8.ragged.lds-codebook.fma-mix" : "aq3x8.ragged.lds-codebook.fma-mix";
+    if (stream_rows(m) == 2)
+        return nc == 2 ? "aq2x8.stream.lds-codebook.fma-mix.2row" : "aq3x8.stream.lds-codebook.fma-mix.2row";
+    return nc == 2 ? "aq2x8.stream.lds-codebook.fma-mix" : "aq3x8.stream.lds-codebook.fma-mix";
 }
 
 }  // namespace qmv

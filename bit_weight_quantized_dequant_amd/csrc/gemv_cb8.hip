@@ -42,6 +42,7 @@ QMV_DEV float lds_h(uint32_t a) {
 }
 
 struct Cb8Policy {
+    static constexpr int R = 1;  // rows per wave
     struct Codes {
         uint4 q[4];  // index bytes 0..63 of the unit
     };

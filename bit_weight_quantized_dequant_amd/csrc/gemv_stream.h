@@ -18,11 +18,12 @@
 // four batch rows two activation buffers do not fit in LDS; the single-buffer variant
 // writes after a second barrier instead.
 //
-// A policy P provides:
-//   typename P::Codes                                  the lane's code bytes of one unit
+// A policy P provides (R = P::R rows per wave, 1 or more):
+//   typename P::Codes                                  the lane's code bytes of one unit (R rows)
 //   void load(Codes &c, int unit) const                issue the loads (unit clamped)
-//   template <int M> void dot(const Codes &c, const float *xu, float (&s)[M]) const
-//       s[m] += sum over the unit's 64 weights of w * x[m], x[m] at xu + m * 64 * XU
+//   template <int M> void dot(const Codes &c, const float *xu, float (&s)[R * M]) const
+//       s[r * M + m] += sum over unit's 64 weights of row r of w * x[m], x[m] at
+//       xu + m * 64 * XU (each activation read once for the R rows)
 #pragma once
 
 #include <type_traits>
@@ -68,11 +69,12 @@ QMV_DEV void store_x(const float4 (&xv)[2 * M], float *buf) {
     }
 }
 
-// Walk one row: acc[m] += sum over its k weights of w * x[m].  `sx` holds nbuf(M)
+// Walk the wave's row(s): acc[r * M + m] += sum over row r's k weights of w * x[m].  `sx` holds nbuf(M)
 // activation buffers when k > KC, one otherwise; every thread of the workgroup calls
 // this with the same k (the barriers are workgroup-wide).
 template <class P, int M, int XT>
-QMV_DEV void walk_row(const P &pol, const void *x, int k, float *sx, float (&acc)[M]) {
+QMV_DEV void walk_row(const P &pol, const void *x, int k, float *sx, float (&acc)[P::R * M]) {
+    constexpr int RM = P::R * M;
     constexpr bool TWO = nbuf(M) == 2;
     const int lane = threadIdx.x & 63;
     const int nunits = k >> 6, nst = (nunits + 63) >> 6;
@@ -98,15 +100,15 @@ QMV_DEV void walk_row(const P &pol, const void *x, int k, float *sx, float (&acc
         const float *buf = sx + (TWO ? (c & 1) * M * XBUF : 0);
         const int u = c * 64 + lane;
         const int uc = u < nunits ? lane : nunits - 1 - c * 64;
-        float s[M];
+        float s[RM];
 #pragma unroll
-        for (int m = 0; m < M; m++) s[m] = 0.f;
+        for (int m = 0; m < RM; m++) s[m] = 0.f;
         pol.template dot<M>(use, buf + uc * XU, s);
         // keep the dot here rather than sunk into a branch over the valid lanes
 #pragma unroll
-        for (int m = 0; m < M; m++) asm volatile("" : "+v"(s[m]));
+        for (int m = 0; m < RM; m++) asm volatile("" : "+v"(s[m]));
 #pragma unroll
-        for (int m = 0; m < M; m++) acc[m] = u < nunits ? acc[m] + s[m] : acc[m];
+        for (int m = 0; m < RM; m++) acc[m] = u < nunits ? acc[m] + s[m] : acc[m];
         if (MORE) {
             if (!TWO) __syncthreads();  // every wave is done with the only buffer
             store_x<M>(xv, sx + (TWO ? ((c + 1) & 1) * M * XBUF : 0));

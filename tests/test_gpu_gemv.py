@@ -329,9 +329,12 @@ AQ_SMALL = [(1, 8), (5, 24), (9, 64), (33, 1000), (64, 4096), (17, 4096 + 8), (4
             (5, 4160), (3, 8192 + 192)]
 
 
-def aq_path(fmt, k):
+def aq_path(fmt, k, m=1):
+    # the streaming kernel (two rows per wave for batches) when k % 64 == 0, else the ragged one
     name = "aq2x8" if fmt == synth.FMT_AQ2X8 else "aq3x8"
-    return f"{name}.stream.lds-codebook.fma-mix" if k % 64 == 0 else f"{name}.ragged.lds-codebook.fma-mix"
+    if k % 64:
+        return f"{name}.ragged.lds-codebook.fma-mix"
+    return f"{name}.stream.lds-codebook.fma-mix" + (".2row" if m > 1 else "")
 
 
 @pytest.mark.parametrize("n,k", AQ_SMALL)
@@ -378,10 +381,23 @@ def test_aq_single_codebook_vq_case(qmv):
 @pytest.mark.parametrize("m,xt", [(5, synth.DT_BF16), (8, synth.DT_F32)])
 def test_aq_batched_multi_step(qmv, m, xt):
     # more than four batch rows: one activation buffer, two barriers per step; 3 steps
-    run_case(qmv, synth.FMT_AQ2X8, 19, 12288, m, xt, seed=m + 31, expect_path=aq_path(synth.FMT_AQ2X8, 12288))
+    run_case(qmv, synth.FMT_AQ2X8, 19, 12288, m, xt, seed=m + 31, expect_path=aq_path(synth.FMT_AQ2X8, 12288, m))
 
 
 # ------------------------------------------------------------- 3-bit additive
+
+@pytest.mark.parametrize("fmt", [synth.FMT_AQ2X8, synth.FMT_AQ3X8])
+@pytest.mark.parametrize("force,m,n", [("aq.r2", 1, 37), ("aq.r1", 4, 37), ("", 3, 17), ("aq.r2", 2, 1)])
+def test_aq_rows_per_wave(qmv, monkeypatch, fmt, force, m, n):
+    # one or two rows per wave either way round; odd row counts leave the last wave's second
+    # row past the end
+    if force:
+        monkeypatch.setenv("QMV_FORCE_PATH", force)
+    k = 4096 + 64
+    name = "aq2x8" if fmt == synth.FMT_AQ2X8 else "aq3x8"
+    two = force == "aq.r2" or (not force and m > 1)
+    run_case(qmv, fmt, n, k, m, synth.DT_F32, seed=n + m, expect_path=f"{name}.stream.lds-codebook.fma-mix" + (".2row" if two else ""))
+
 
 @pytest.mark.parametrize("n,k", AQ_SMALL)
 def test_aq3_small_full_parity(qmv, n, k):
@@ -397,7 +413,7 @@ def test_aq3_config_shapes_sampled(qmv, m, n, k):
 @pytest.mark.parametrize("m,xt,k", [(2, synth.DT_F32, 2048), (3, synth.DT_BF16, 8192 + 64), (6, synth.DT_F32, 12288),
                                     (8, synth.DT_BF16, 4096), (4, synth.DT_F32, 1000)])
 def test_aq3_batched(qmv, m, xt, k):
-    run_case(qmv, synth.FMT_AQ3X8, 37, k, m, xt, seed=m + 13, expect_path=aq_path(synth.FMT_AQ3X8, k))
+    run_case(qmv, synth.FMT_AQ3X8, 37, k, m, xt, seed=m + 13, expect_path=aq_path(synth.FMT_AQ3X8, k, m))
 
 
 def test_aq3_cancelling_codebooks_give_zero(qmv):
