@@ -269,13 +269,13 @@ void launch_stream(const qmv_weights *w, const void *x, float *y, hipStream_t s)
 }
 
 // Rows per wave of the streaming kernel: two for batches (each activation read from LDS
-// serves both rows, which the batch's LDS traffic needs), one for batch 1; test overrides
-// "aq.r1" / "aq.r2" force either.
-int stream_rows(int m) {
+// serves both rows, which the batch's LDS traffic needs) when there are rows for at least one
+// such workgroup per CU, else one; test overrides "aq.r1" / "aq.r2" force either.
+int stream_rows(int m, int64_t n) {
     const char *fp = forced_path();
     if (strcmp(fp, "aq.r1") == 0) return 1;
     if (strcmp(fp, "aq.r2") == 0) return 2;
-    return m > 1 ? 2 : 1;
+    return m > 1 && n >= 2 * WAVES * (int64_t)device_info().num_cus ? 2 : 1;
 }
 
 template <int NC, int M, int XT>
@@ -283,7 +283,7 @@ void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     const int n = (int)w->n, k = (int)w->k;
     const dim3 grid((n + WAVES - 1) / WAVES);
     if (k % 64 == 0) {
-        if (stream_rows(M) == 2) launch_stream<NC, M, 2, XT>(w, x, y, s);
+        if (stream_rows(M, n) == 2) launch_stream<NC, M, 2, XT>(w, x, y, s);
         else launch_stream<NC, M, 1, XT>(w, x, y, s);
     } else {
         hipLaunchKernelGGL((aq_ragged_kernel<NC, M, XT>), grid, dim3(WG), ragged_lds(NC, M), s,
@@ -322,7 +322,7 @@ const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, f
         ok = xt == QMV_F32 ? dispatch_m<3, 0>(m, w, x, y, s) : dispatch_m<3, 1>(m, w, x, y, s);
     if (!ok) return nullptr;
     if (!str) return nc == 2 ? "aq2x8.ragged.lds-codebook.fma-mix" : "aq3x8.ragged.lds-codebook.fma-mix";
-    if (stream_rows(m) == 2)
+    if (stream_rows(m, w->n) == 2)
         return nc == 2 ? "aq2x8.stream.lds-codebook.fma-mix.2row" : "aq3x8.stream.lds-codebook.fma-mix.2row";
     return nc == 2 ? "aq2x8.stream.lds-codebook.fma-mix" : "aq3x8.stream.lds-codebook.fma-mix";
 }
