@@ -19,6 +19,8 @@
 // stage of the expert FFN (a wave computes row r of G_e and of U_e and writes
 // SiLU(g) * u), and the down stage (y_e = D_e h_e), with the expert id read on the
 // device and its planes found at e * plane_bytes from expert 0's.
+#include <cstring>
+
 #include "device_common.h"
 #include "qmv_internal.h"
 
@@ -29,7 +31,7 @@ constexpr int WG = 512;
 constexpr int WAVES = WG / 64;
 constexpr int XS = 36;
 
-enum { JOB_GEMV = 0, JOB_GATEUP = 1, JOB_DOWN = 2 };
+enum { JOB_GEMV = 0, JOB_GATEUP = 1, JOB_DOWN = 2, JOB_DOWN2 = 3 };  // DOWN2: two rows per wave
 
 struct Cb4Args {
     const uint8_t *idx0, *idx1;  // index planes (expert 0): first matrix, second (gate/up: up)
@@ -151,12 +153,14 @@ template <int JOB, int M, int CPL, int XT>
 __global__ void __launch_bounds__(WG) cb4_kernel(Cb4Args a) {
     extern __shared__ float4 lds4[];
     constexpr int XPT = xpt_of(M, CPL);
-    constexpr int XT_ = JOB == JOB_DOWN ? 0 : XT;
+    constexpr bool DOWN = JOB == JOB_DOWN || JOB == JOB_DOWN2;
+    constexpr int XT_ = DOWN ? 0 : XT;
     const int k = a.k, ngroups = k >> 7, nchunk = k >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row = blockIdx.x * WAVES + wave;
+    const int row = (blockIdx.x * WAVES + wave) * (JOB == JOB_DOWN2 ? 2 : 1);
     const int rowc = row < a.n ? row : a.n - 1;
-    constexpr int NT = JOB == JOB_GATEUP ? 2 : 1;  // tables (rows) per wave
+    const int rowc1 = row + 1 < a.n ? row + 1 : a.n - 1;  // DOWN2: the wave's second row
+    constexpr int NT = JOB == JOB_GATEUP || JOB == JOB_DOWN2 ? 2 : 1;  // tables (rows) per wave
     float *sx = (float *)lds4;
     uint16_t *tabs = (uint16_t *)(sx + x_floats(M, CPL));
     uint16_t *tab0 = tabs + wave * NT * ngroups * 16;
@@ -164,7 +168,7 @@ __global__ void __launch_bounds__(WG) cb4_kernel(Cb4Args a) {
 
     int32_t id = 0;
     if (JOB != JOB_GEMV) id = a.ids[blockIdx.y];
-    const void *x = JOB == JOB_DOWN ? (const void *)((const float *)a.x + (int64_t)blockIdx.y * k) : a.x;
+    const void *x = DOWN ? (const void *)((const float *)a.x + (int64_t)blockIdx.y * k) : a.x;
     const int total = M * (k >> 2);
     float4 xv[XPT];
 #pragma unroll
@@ -178,15 +182,17 @@ __global__ void __launch_bounds__(WG) cb4_kernel(Cb4Args a) {
     RowData<CPL> r0, r1;
     load_tables<CPL>(r0, a.cb0 + e * a.cb_stride + (int64_t)rowc * ngroups * 16, nchunk, lane);
     if (JOB == JOB_GATEUP) load_tables<CPL>(r1, a.cb1 + e * a.cb_stride + (int64_t)rowc * ngroups * 16, nchunk, lane);
+    if (JOB == JOB_DOWN2) load_tables<CPL>(r1, a.cb0 + e * a.cb_stride + (int64_t)rowc1 * ngroups * 16, nchunk, lane);
     load_codes<CPL>(r0, a.idx0 + e * a.idx_stride + (int64_t)rowc * (k >> 1), nchunk, lane);
     if (JOB == JOB_GATEUP) load_codes<CPL>(r1, a.idx1 + e * a.idx_stride + (int64_t)rowc * (k >> 1), nchunk, lane);
+    if (JOB == JOB_DOWN2) load_codes<CPL>(r1, a.idx0 + e * a.idx_stride + (int64_t)rowc1 * (k >> 1), nchunk, lane);
     __builtin_amdgcn_sched_barrier(0);  // every load is issued before the LDS writes wait
 
     float4 *dst = lds4 + (threadIdx.x >> 3) * (XS / 4) + (threadIdx.x & 7);
 #pragma unroll
     for (int j = 0; j < XPT; j++) dst[j * (WG / 8) * (XS / 4)] = xv[j];
     store_tables<CPL>(r0, tab0, nchunk, lane);
-    if (JOB == JOB_GATEUP) store_tables<CPL>(r1, tab1, nchunk, lane);
+    if (NT == 2) store_tables<CPL>(r1, tab1, nchunk, lane);
     __syncthreads();
 
     if (JOB == JOB_GEMV) {
@@ -202,6 +208,11 @@ __global__ void __launch_bounds__(WG) cb4_kernel(Cb4Args a) {
         const float g = wave_sum(row_dot<CPL>(r0, tab0, sx, nchunk, lane));
         const float u = wave_sum(row_dot<CPL>(r1, tab1, sx, nchunk, lane));
         if (lane == 0 && row < a.n) out[row] = ok_expert ? g / (1.f + expf(-g)) * u : __builtin_nanf("");
+    } else if (JOB == JOB_DOWN2) {
+        const float t0 = wave_sum(row_dot<CPL>(r0, tab0, sx, nchunk, lane));
+        const float t1 = wave_sum(row_dot<CPL>(r1, tab1, sx, nchunk, lane));
+        if (lane == 0 && row < a.n) out[row] = ok_expert ? t0 : __builtin_nanf("");
+        if (lane == 0 && row + 1 < a.n) out[row + 1] = ok_expert ? t1 : __builtin_nanf("");
     } else {
         const float t = wave_sum(row_dot<CPL>(r0, tab0, sx, nchunk, lane));
         if (lane == 0 && row < a.n) out[row] = ok_expert ? t : __builtin_nanf("");
@@ -210,9 +221,11 @@ __global__ void __launch_bounds__(WG) cb4_kernel(Cb4Args a) {
 
 template <int JOB, int M, int CPL, int XT>
 void launch(const Cb4Args &a, int slots, hipStream_t s) {
-    constexpr int NT = JOB == JOB_GATEUP ? 2 : 1;
+    constexpr int NT = JOB == JOB_GATEUP || JOB == JOB_DOWN2 ? 2 : 1;
+    constexpr int RPW = JOB == JOB_DOWN2 ? 2 : 1;  // matrix rows per wave
     const size_t lds = (size_t)x_floats(M, CPL) * 4 + (size_t)WAVES * NT * (a.k >> 7) * 32;
-    hipLaunchKernelGGL((cb4_kernel<JOB, M, CPL, XT>), dim3((a.n + WAVES - 1) / WAVES, slots), dim3(WG), lds, s, a);
+    const int waves = (a.n + RPW - 1) / RPW;
+    hipLaunchKernelGGL((cb4_kernel<JOB, M, CPL, XT>), dim3((waves + WAVES - 1) / WAVES, slots), dim3(WG), lds, s, a);
 }
 
 template <int JOB, int M, int XT>
@@ -412,7 +425,7 @@ const char *launch_moe_cb4(const qmv_weights *gate, const qmv_weights *up, const
     const int cpl1 = (int)((dm / 32 + 63) / 64), cpl2 = (int)((dff / 32 + 63) / 64);
     if (cpl1 > 8 || cpl2 > 8 || dm > 16384 || dff > 16384) return nullptr;
     if ((int64_t)lds_need(1, dm, 2) > device_info().lds_per_block ||
-        (int64_t)lds_need(1, dff, 1) > device_info().lds_per_block)
+        (int64_t)lds_need(1, dff, 2) > device_info().lds_per_block)
         return nullptr;
     const int64_t idx_gu = dff * dm / 2, cb_gu = dff * (dm / 128) * 16;
     Cb4Args a1{(const uint8_t *)gate->codes, (const uint8_t *)up->codes, (const uint16_t *)gate->codebook,
@@ -423,8 +436,10 @@ const char *launch_moe_cb4(const qmv_weights *gate, const qmv_weights *up, const
     const int64_t idx_d = dm * dff / 2, cb_d = dm * (dff / 128) * 16;
     Cb4Args a2{(const uint8_t *)down->codes, nullptr, (const uint16_t *)down->codebook, nullptr, idx_d, cb_d,
                h, y, ids, (int)dm, (int)dff, n_experts};
-    if (!dispatch_cpl<JOB_DOWN, 1, 0>(cpl2, a2, n_ids, s)) return nullptr;
-    return "moe.cb4.gateup-silu+down";
+    const bool two = strcmp(forced_path(), "moe.down1") != 0;  // test override: one row per wave
+    if (!(two ? dispatch_cpl<JOB_DOWN2, 1, 0>(cpl2, a2, n_ids, s) : dispatch_cpl<JOB_DOWN, 1, 0>(cpl2, a2, n_ids, s)))
+        return nullptr;
+    return two ? "moe.cb4.gateup-silu+down2" : "moe.cb4.gateup-silu+down";
 }
 
 }  // namespace qmv

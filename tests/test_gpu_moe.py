@@ -45,7 +45,7 @@ def h_bound(g, u, bg, bu):
     return 1.1 * eg * (np.abs(u) + eu) + np.abs(sg) * eu + 1e-6 * np.abs(sg * u) + 1e-30
 
 
-def run_moe(qmv, n_experts, dm, dff, ids, seed, rows_h=None, rows_y=None):
+def run_moe(qmv, n_experts, dm, dff, ids, seed, rows_h=None, rows_y=None, expect="moe.cb4.gateup-silu+down2"):
     import torch
     routed = sorted({int(i) for i in ids if 0 <= i < n_experts})
     gp, gh = stacked_planes(n_experts, routed, dff, dm, 0, seed)
@@ -59,7 +59,7 @@ def run_moe(qmv, n_experts, dm, dff, ids, seed, rows_h=None, rows_y=None):
     print(f"moe E={n_experts} dm={dm} dff={dff} ids={list(ids)}", flush=True)
     h, y = qmv.moe_ffn(G, U, D, n_experts, ids_t, x_to_device(x[0], synth.DT_BF16))
     torch.cuda.synchronize()
-    assert qmv.last_path() == "moe.cb4.gateup-silu+down"
+    assert qmv.last_path() == expect
     h, y = h.cpu().numpy(), y.cpu().numpy()
     for j, e in enumerate(ids):
         if not 0 <= e < n_experts:
@@ -78,12 +78,19 @@ def run_moe(qmv, n_experts, dm, dff, ids, seed, rows_h=None, rows_y=None):
         assert_parity(yj[None, :], yr, by, f"down expert {e}")
 
 
-def test_moe_small_with_invalid_id(qmv):
-    run_moe(qmv, n_experts=6, dm=512, dff=256, ids=[3, 0, 5, -1, 6], seed=1)
+@pytest.mark.parametrize("force", ["", "moe.down1"])
+def test_moe_small_with_invalid_id(qmv, monkeypatch, force):
+    # the down stage with two rows per wave (default) and one (override)
+    monkeypatch.setenv("QMV_FORCE_PATH", force)
+    run_moe(qmv, n_experts=6, dm=512, dff=256, ids=[3, 0, 5, -1, 6], seed=1,
+            expect="moe.cb4.gateup-silu+down" + ("" if force else "2"))
 
 
-def test_moe_ragged_sizes(qmv):
-    run_moe(qmv, n_experts=3, dm=1152, dff=640, ids=[2, 1], seed=2)
+@pytest.mark.parametrize("force", ["", "moe.down1"])
+def test_moe_ragged_sizes(qmv, monkeypatch, force):
+    monkeypatch.setenv("QMV_FORCE_PATH", force)
+    run_moe(qmv, n_experts=3, dm=1152, dff=640, ids=[2, 1], seed=2,
+            expect="moe.cb4.gateup-silu+down" + ("" if force else "2"))
 
 
 def test_moe_deepseek_like_layer_top8_of_256(qmv):
