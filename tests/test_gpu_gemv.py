@@ -90,6 +90,14 @@ def test_q4_0_full_size_sampled(qmv, n, k):
     run_case(qmv, synth.FMT_Q4_0, n, k, 1, synth.DT_F32, seed=0, rows=sample_rows(n))
 
 
+@pytest.mark.parametrize("m", [2, 4, 8])
+@pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096), (4096, 11008)])
+def test_q4_0_full_size_batched_sampled(qmv, n, k, m):
+    # the batch workloads the benchmark times (K-chunked kernel), at their full sizes
+    run_case(qmv, synth.FMT_Q4_0, n, k, m, synth.DT_F32, seed=m, rows=sample_rows(n),
+             expect_path="q4_0.lds-x-chunked.fma-mix")
+
+
 def test_q4_0_unit_vector_returns_column_exactly(qmv):
     import torch
     n, k = 200, 4096
