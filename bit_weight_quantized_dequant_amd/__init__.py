@@ -141,7 +141,15 @@ class QWeights:
         self.planes = dict(planes)
         fields = {f: 0 for f in ("codes", "codes_hi", "scales", "super", "codebook")}
         for name, field in PLANES[fmt].items():
-            fields[field] = _ptr(self.planes.get(name))
+            t = self.planes.get(name)
+            if t is not None and not isinstance(t, int):
+                if not t.is_cuda or not t.is_contiguous():
+                    raise ValueError(f"plane {name}: must be a contiguous device tensor")
+                need = plane_bytes(fmt, n, k, field)
+                if need > 0 and t.numel() * t.element_size() < need:
+                    raise ValueError(f"plane {name}: {t.numel() * t.element_size()} bytes, "
+                                     f"the format needs {need}")
+            fields[field] = _ptr(t)
         self._s = _W(fmt, n, k, *(fields[f] for f in ("codes", "codes_hi", "scales", "super", "codebook")))
 
     @property
@@ -155,6 +163,22 @@ class QWeights:
 def _check(rc: int, call: str):
     if rc != 0:
         raise QmvError(rc, call)
+
+
+def _need(t, dtypes, shape, name: str):
+    """Check a tensor argument before its address is handed to the library: the C ABI sees
+    only a pointer, so a wrong dtype, shape or layout would be read or written as if it were
+    right.  Raw integer addresses are passed through unchecked."""
+    if isinstance(t, int):
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def validate(w: QWeights, m: int = 1, xt: int = F32) -> int:
@@ -176,8 +200,10 @@ def gemv(w: QWeights, x, y=None, stream=None):
     squeeze = x.dim() == 1
     x2 = x.reshape(1, -1) if squeeze else x
     m = x2.shape[0]
+    _need(x2, (torch.float32, torch.bfloat16), (m, w.k), "x")
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
+    _need(y, (torch.float32,), (m, w.n), "y")
     _check(lib().qmv_gemv(w.ref, m, _ptr(x2), _xt_of(x2), _ptr(y), _stream(stream)), "qmv_gemv")
     return y[0] if squeeze else y
 
@@ -186,6 +212,7 @@ def dequant(w: QWeights, out=None, stream=None):
     import torch
     if out is None:
         out = torch.empty((w.n, w.k), dtype=torch.float32, device="cuda")
+    _need(out, (torch.float32,), (w.n, w.k), "out")
     _check(lib().qmv_dequant(w.ref, _ptr(out), _stream(stream)), "qmv_dequant")
     return out
 
@@ -193,10 +220,13 @@ def dequant(w: QWeights, out=None, stream=None):
 def quant_act(x, xq=None, xs=None, stream=None):
     import torch
     m, k = x.shape
+    _need(x, (torch.float32,), (m, k), "x")
     if xq is None:
         xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
     if xs is None:
         xs = torch.empty((m, k // 32), dtype=torch.float32, device=x.device)
+    _need(xq, (torch.int8,), (m, k), "xq")
+    _need(xs, (torch.float32,), (m, k // 32), "xs")
     _check(lib().qmm_quant_act(_ptr(x), m, k, _ptr(xq), _ptr(xs), _stream(stream)), "qmm_quant_act")
     return xq, xs
 
@@ -208,13 +238,16 @@ def workspace_bytes(w: QWeights, m: int) -> int:
 def gemm(w: QWeights, x, y=None, ws=None, stream=None):
     import torch
     m = x.shape[0]
+    _need(x, (torch.float32,), (m, w.k), "x")
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
+    _need(y, (torch.float32,), (m, w.n), "y")
     need = workspace_bytes(w, m)
     if need < 0:
         raise QmvError(need, "qmm_workspace_bytes")
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _need(ws, (torch.uint8,), None, "ws")
     _check(lib().qmm_gemm(w.ref, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)), "qmm_gemm")
     return y
 
@@ -222,8 +255,11 @@ def gemm(w: QWeights, x, y=None, ws=None, stream=None):
 def gemm_q8(w: QWeights, xq, xs, y=None, stream=None):
     import torch
     m = xq.shape[0]
+    _need(xq, (torch.int8,), (m, w.k), "xq")
+    _need(xs, (torch.float32,), (m, w.k // 32), "xs")
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.float32, device=xq.device)
+    _need(y, (torch.float32,), (m, w.n), "y")
     _check(lib().qmm_gemm_q8(w.ref, m, _ptr(xq), _ptr(xs), _ptr(y), _stream(stream)), "qmm_gemm_q8")
     return y
 
@@ -231,8 +267,10 @@ def gemm_q8(w: QWeights, xq, xs, y=None, stream=None):
 def partials(w: QWeights, xq, out=None, stream=None):
     import torch
     m = xq.shape[0]
+    _need(xq, (torch.int8,), (m, w.k), "xq")
     if out is None:
         out = torch.empty((m, w.n, w.k // 32), dtype=torch.int32, device=xq.device)
+    _need(out, (torch.int32,), (m, w.n, w.k // 32), "out")
     _check(lib().qmm_partials(w.ref, m, _ptr(xq), _ptr(out), _stream(stream)), "qmm_partials")
     return out
 
@@ -250,6 +288,7 @@ def register_plane(w: QWeights, plane=None, stream=None):
         raise QmvError(need, "qmm_plane_bytes")
     if plane is None:
         plane = torch.empty(need, dtype=torch.uint8, device="cuda")
+    _need(plane, (plane.dtype,), None, "plane")
     _check(lib().qmm_register_plane(w.ref, _ptr(plane), plane.numel() * plane.element_size(), _stream(stream)),
            "qmm_register_plane")
     w._plane = plane
@@ -266,10 +305,14 @@ def moe_ffn(gate: QWeights, up: QWeights, down: QWeights, n_experts: int, ids, x
     """Routed-expert FFN for one token: returns (h [n_ids][d_ff], y [n_ids][d_model])."""
     import torch
     n_ids = ids.numel()
+    _need(ids, (torch.int32,), (n_ids,), "ids")
+    _need(x, (torch.float32, torch.bfloat16), (gate.k,), "x")
     if h is None:
         h = torch.empty((n_ids, gate.n), dtype=torch.float32, device=x.device)
     if y is None:
         y = torch.empty((n_ids, down.n), dtype=torch.float32, device=x.device)
+    _need(h, (torch.float32,), (n_ids, gate.n), "h")
+    _need(y, (torch.float32,), (n_ids, down.n), "y")
     _check(lib().qmv_moe_ffn(gate.ref, up.ref, down.ref, n_experts, _ptr(ids), n_ids, _ptr(x),
                              _xt_of(x), _ptr(h), _ptr(y), _stream(stream)), "qmv_moe_ffn")
     return h, y

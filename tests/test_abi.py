@@ -124,3 +124,28 @@ def test_plane_calls_check_arguments_before_any_gpu_work(monkeypatch):
     assert qmv.last_path() == "plane.q6k(exp=off)"
     assert L.qmm_unregister_plane(q6.ref) == 0
     assert L.qmm_unregister_plane(None) == -1
+
+
+def test_binding_rejects_bad_tensor_arguments():
+    # the C ABI sees only addresses, so the binding checks dtype, device, layout and shape
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.float64)
+    with pytest.raises(TypeError):
+        qmv._need(x, (torch.float32,), (4, 64), "x")
+    with pytest.raises(ValueError, match="device"):
+        qmv._need(x.float(), (torch.float32,), (4, 64), "x")
+    qmv._need(1 << 20, (torch.float32,), (4, 64), "x")      # raw addresses pass unchecked
+    with pytest.raises(ValueError, match="device"):
+        qmv.QWeights(qmv.Q4_0, 8, 64, {"qs": torch.zeros(256, dtype=torch.uint8),
+                                        "d": 1 << 20})
+
+
+@pytest.mark.parametrize("fmt,n,k", [(qmv.Q4_0, 5, 96), (qmv.Q6_K, 3, 512), (qmv.CB4, 4, 256),
+                                     (qmv.AQ2X8, 3, 64), (qmv.CB8, 2, 128), (qmv.AQ3X8, 3, 48)])
+def test_synthetic_planes_have_the_library_sizes(fmt, n, k):
+    # the binding refuses planes shorter than the library's size for them; the generator's
+    # planes are exactly that size
+    import synth
+    w = synth.gen_weights(fmt, n, k, seed=1)
+    for name, field in qmv.PLANES[fmt].items():
+        assert w[name].nbytes == qmv.plane_bytes(fmt, n, k, field), name

@@ -494,3 +494,25 @@ def test_cb8_unit_vector_returns_codebook_entry_exactly(qmv):
     y = y.cpu().numpy()
     for r, j in enumerate(cols):
         assert np.array_equal(y[r], dense[:, j]), j
+
+
+def test_binding_rejects_bad_tensors(qmv):
+    # wrong layout, shape or dtype never reaches the library as a bare address
+    import torch
+    n, k = 8, 64
+    w = synth.gen_weights(synth.FMT_Q4_0, n, k, seed=3)
+    W = qweights(synth.FMT_Q4_0, n, k, w)
+    x = torch.zeros(k, 2, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="contiguous"):
+        qmv.gemv(W, x.t())
+    with pytest.raises(ValueError, match="shape"):
+        qmv.gemv(W, torch.zeros(1, k + 32, device="cuda"))
+    with pytest.raises(ValueError, match="shape"):
+        qmv.gemv(W, torch.zeros(2, k, device="cuda"), y=torch.empty(2, n - 1, device="cuda"))
+    with pytest.raises(TypeError):
+        qmv.gemv(W, torch.zeros(1, k, dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError, match="bytes"):
+        qmv.QWeights(synth.FMT_Q4_0, n, k, {"qs": W.planes["qs"][:-1], "d": W.planes["d"]})
+    y = qmv.gemv(W, torch.zeros(2, k, device="cuda"))
+    torch.cuda.synchronize()
+    assert y.shape == (2, n) and not y.abs().sum().item()
