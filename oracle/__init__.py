@@ -67,6 +67,7 @@ def lib():
         L.qo_quant_act.argtypes = [P, I64, I64, P, P]
         L.qo_q6k_partials.argtypes = [P, P, P, P, I64, P, P]
         L.qo_q6k_gemm_pairs.argtypes = [P, P, P, P, P, I64, P, P, I32]
+        L.qo_q4_0_gemv_q8_pairs.argtypes = [P, P, P, P, P, I64, P, P, I32]
         L.qo_pack_q4_0.argtypes = [P, I64, I64, P]
         L.qo_pack_q6k.argtypes = [P, I64, I64, P, P]
         L.qo_pack_cb4.argtypes = [P, I64, I64, P]
@@ -186,6 +187,29 @@ def q6k_gemm(m: Mat, x: np.ndarray, nthreads: int = 1):
     mm, nn = np.meshgrid(np.arange(M), np.arange(m.n), indexing="ij")
     y, b = q6k_gemm_pairs(m, xq, xs, mm.ravel(), nn.ravel(), nthreads)
     return y.reshape(M, m.n), b.reshape(M, m.n), xq, xs
+
+
+def q4_0_gemv_q8_pairs(m: Mat, xq: np.ndarray, xs: np.ndarray, mm, nn, nthreads: int = 1):
+    """(y, bound) float64 [pair] of the q4_0 GEMV over int8 activations (xq, xs from
+    quant_act) for (mm[i], nn[i]) pairs: per block d * xs * exact sum of (q - 8) * xq."""
+    mm = np.ascontiguousarray(mm, dtype=np.int64)
+    nn = np.ascontiguousarray(nn, dtype=np.int64)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    xs = np.ascontiguousarray(xs, dtype=np.float32)
+    y = np.empty(len(mm), dtype=np.float64)
+    b = np.empty(len(mm), dtype=np.float64)
+    lib().qo_q4_0_gemv_q8_pairs(m.ref, _p(xq), _p(xs), _p(mm), _p(nn), len(mm), _p(y), _p(b), nthreads)
+    return y, b
+
+
+def q4_0_gemv_q8(m: Mat, xq: np.ndarray, xs: np.ndarray, rows=None, nthreads: int = 1):
+    """(y, bound) float64 [M][rows] of the q4_0 GEMV over int8 activations, for all batch
+    rows and the listed weight rows (all rows when None)."""
+    M = xq.shape[0]
+    rows = np.arange(m.n) if rows is None else np.asarray(rows, dtype=np.int64)
+    mm, nn = np.meshgrid(np.arange(M), rows, indexing="ij")
+    y, b = q4_0_gemv_q8_pairs(m, xq, xs, mm.ravel(), nn.ravel(), nthreads)
+    return y.reshape(M, len(rows)), b.reshape(M, len(rows))
 
 
 def moe_gateup(gate: Mat, up: Mat, x: np.ndarray, xt: int, rows=None, nthreads: int = 1):

@@ -333,6 +333,44 @@ void qo_q6k_gemm_pairs(const qo_mat *w, const int8_t *xq, const float *xs,
     }
 }
 
+/* ------------------------------------------- q4_0 with int8 activations */
+
+/* The integer-dot form of the q4_0 GEMV (quantprobe LAWS.md, Law 4's per-format
+ * amendment, L-15: on the standalone matvec the integer dot product over quantized
+ * activations recovers most of what the unpack costs).  The activations are those of
+ * the quantizer above (xq, xs per 32); per block b of row n:
+ *   I[m][n][b] = sum over the block's 32 columns of (q - 8) * xq   (exact integer)
+ *   y[m][n]    = sum_b d[n][b] * xs[m][b] * I[m][n][b]               (double)
+ * bound = sum_k |w[n][k]| * |xs * xq|.  Sampled (m, n) pairs, like the GEMM above. */
+void qo_q4_0_gemv_q8_pairs(const qo_mat *w, const int8_t *xq, const float *xs,
+                           const int64_t *mm, const int64_t *nn, int64_t npairs,
+                           double *y, double *bound, int32_t nthreads)
+{
+    int64_t k = w->k;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+#endif
+    for (int64_t p = 0; p < npairs; p++) {
+        int64_t m = mm[p], n = nn[p];
+        double acc = 0.0, bnd = 0.0;
+        for (int64_t b = 0; b < k / 32; b++) {
+            int64_t isum = 0;
+            for (int64_t i = 0; i < 32; i++) {
+                int64_t col = b * 32 + i;
+                isum += (int64_t)(qo_q4_0_code(w, n, col) - 8) * (int64_t)xq[m * k + col];
+            }
+            double d = f16_at(w->p1, n * (k / 32) + b);
+            acc += d * (double)xs[m * (k / 32) + b] * (double)isum;
+        }
+        for (int64_t col = 0; col < k; col++)
+            bnd += fabs(qo_weight(w, n, col)) *
+                   fabs((double)xs[m * (k / 32) + col / 32] * (double)xq[m * k + col]);
+        y[p] = acc;
+        if (bound) bound[p] = bnd;
+    }
+}
+
 /* --------------------------------------------------------------- encoders */
 
 /* Pack integer codes [n][k] into the code planes (inverse of the readers above). */

@@ -483,6 +483,53 @@ def test_q6k_gemm_equals_dense_matmul_of_dequantized_operands():
     assert np.allclose(b, np.abs(xhat) @ np.abs(W).T, rtol=1e-13, atol=0)
 
 
+def test_q4_0_gemv_q8_equals_dense_matmul_of_dequantized_operands():
+    # the blocked integer form sum_b d xs I equals W @ (xs * xq) over the reals
+    w = synth.gen_weights(synth.FMT_Q4_0, 7, 320, seed=23)
+    m = oracle.Mat(oracle.Q4_0, 7, 320, w)
+    x = synth.gen_x(3, 320, seed=23)
+    xq, xs = oracle.quant_act(x)
+    y, b = oracle.q4_0_gemv_q8(m, xq, xs)
+    xhat = np.repeat(xs.astype(np.float64), 32, axis=1) * xq
+    W = oracle.dequant(m)
+    assert np.all(np.abs(y - xhat @ W.T) <= 1e-13 * (np.abs(xhat) @ np.abs(W).T))
+    assert np.allclose(b, np.abs(xhat) @ np.abs(W).T, rtol=1e-13, atol=0)
+    # sampled rows are the same numbers as the full call
+    ys, bs = oracle.q4_0_gemv_q8(m, xq, xs, rows=[6, 0, 3])
+    assert np.array_equal(ys, y[:, [6, 0, 3]]) and np.array_equal(bs, b[:, [6, 0, 3]])
+
+
+def test_q4_0_gemv_q8_on_exactly_quantizable_activations_is_the_plain_gemv():
+    # integer activations whose every 32-block reaches +-127 quantize exactly (xs = 1,
+    # xq = x), so the integer form must reproduce the plain double GEMV
+    rng = np.random.default_rng(24)
+    k = 256
+    x = rng.integers(-127, 128, size=(2, k)).astype(np.float32)
+    x[:, ::32] = 127.0 * rng.choice([-1, 1], size=(2, k // 32))
+    w = synth.gen_weights(synth.FMT_Q4_0, 5, k, seed=24)
+    m = oracle.Mat(oracle.Q4_0, 5, k, w)
+    xq, xs = oracle.quant_act(x)
+    assert np.all(xs == 1.0) and np.array_equal(xq.astype(np.float32), x)
+    y, b = oracle.q4_0_gemv_q8(m, xq, xs)
+    yr, br = oracle.gemv(m, x)
+    assert np.allclose(y, yr, rtol=1e-13, atol=0) and np.allclose(b, br, rtol=1e-13, atol=0)
+
+
+def test_q4_0_gemv_q8_constant_codes_closed_form():
+    # every code c: y = sum_b d_b * xs_b * (c - 8) * sum of the block's xq
+    n, k = 3, 128
+    xq = np.random.default_rng(25).integers(-127, 128, size=(2, k)).astype(np.int8)
+    xs = np.array([[0.5, 0.25, 2.0, 1.0], [1.5, 0.125, 4.0, 0.75]], dtype=np.float32)
+    d = np.array([[0x3C00, 0x4000, 0x3800, 0x3C00]] * n, dtype=np.uint16)  # 1, 2, 0.5, 1
+    for c in (0, 8, 15):
+        qs = oracle.pack_q4_0(np.full((n, k), c, dtype=np.int32))
+        m = oracle.Mat(oracle.Q4_0, n, k, {"qs": qs, "d": d})
+        y, _ = oracle.q4_0_gemv_q8(m, xq, xs)
+        blocks = xq.astype(np.int64).reshape(2, 4, 32).sum(axis=2)
+        want = (np.array([1.0, 2.0, 0.5, 1.0]) * xs * (c - 8) * blocks).sum(axis=1)
+        assert np.array_equal(y, np.repeat(want[:, None], n, axis=1)), c
+
+
 def test_moe_gateup_composition():
     gw = synth.gen_weights(synth.FMT_CB4, 8, 256, seed=1, expert=3, matrix=0)
     uw = synth.gen_weights(synth.FMT_CB4, 8, 256, seed=1, expert=3, matrix=1)
