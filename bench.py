@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--only-primary", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--secondary", default="q6_K_gemv,q4_0_batch,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm",
+    ap.add_argument("--secondary", default="q6_K_gemv,q4_0_batch,q4_0_q8,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm",
                     help="comma-separated secondary workloads to run")
     return ap.parse_args()
 
@@ -196,6 +196,52 @@ def gemv_workload(qmv, fmt, shapes, batch, xt, steps, label):
     gbs = sum(algo) / ms / 1e6
     return {"workload": label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "ms_per_step": round(ms, 5), "bytes_per_step": sum(algo), "pool_copies": copies,
+            "path": qmv.last_path(), "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+            "shapes": per_shape}
+
+
+def q4_0_q8_workload(qmv, batch, steps, label):
+    """The q4_0 GEMV over per-32 int8 activations on the three decode shapes (one step = one
+    GEMV per shape, activations quantized beforehand, as they are once per activation vector
+    for every GEMV that reads it).  The same step with one quantizer launch in front of each
+    GEMV is timed too and reported beside it."""
+    import torch
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]
+    per_set = sum(qmv.weight_bytes(synth.FMT_Q4_0, n, k) for n, k in shapes)
+    copies = pool_copies(per_set)
+    mats, xs, qs, ys, algo = [], [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        _, pool = make_pool(qmv, synth.FMT_Q4_0, n, k, seed=i, copies=copies)
+        mats.append(pool)
+        x = torch.from_numpy(synth.gen_x(batch, k, synth.DT_F32, seed=i)).cuda()
+        xs.append(x)
+        qs.append(qmv.quant_act(x))
+        ys.append(torch.empty((batch, n), dtype=torch.float32, device="cuda"))
+        # weights + int8 activations and their scales + outputs
+        algo.append(qmv.weight_bytes(synth.FMT_Q4_0, n, k) + batch * (k + k // 8) + 4 * batch * n)
+
+    def step(i):
+        for s in range(len(shapes)):
+            qmv.gemv_q8(mats[s][i % copies], qs[s][0], qs[s][1], ys[s])
+
+    def step_quant(i):
+        for s in range(len(shapes)):
+            qmv.quant_act(xs[s], qs[s][0], qs[s][1])
+            qmv.gemv_q8(mats[s][i % copies], qs[s][0], qs[s][1], ys[s])
+
+    ms = time_graph(graph_of(step, steps), steps)
+    ms_q = time_graph(graph_of(step_quant, steps), steps)
+    per_shape = []
+    for s, (n, k) in enumerate(shapes):
+        R = max(steps, 40)
+        avg = time_graph(graph_of(lambda i, s=s: qmv.gemv_q8(mats[s][i % copies], qs[s][0], qs[s][1], ys[s]), R), R)
+        qmv.gemv_q8(mats[s][0], qs[s][0], qs[s][1], ys[s])
+        per_shape.append({"shape": f"{n}x{k}", "bytes": algo[s], "avg_launch_ms": round(avg, 5),
+                          "GBps": round(algo[s] / avg / 1e6, 1), "path": qmv.last_path()})
+    gbs = sum(algo) / ms / 1e6
+    return {"workload": label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(ms, 5), "bytes_per_step": sum(algo), "pool_copies": copies,
+            "with_quant_act": {"ms_per_step": round(ms_q, 5), "GBps": round(sum(algo) / ms_q / 1e6, 1)},
             "path": qmv.last_path(), "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
             "shapes": per_shape}
 
@@ -369,6 +415,9 @@ def main():
             sec[f"q4_0_gemv_b{b}"] = gemv_workload(qmv, synth.FMT_Q4_0, [(4096, 4096), (11008, 4096), (4096, 11008)],
                                                    b, synth.DT_F32, 50,
                                                    f"q4_0 GEMV batch {b}, Llama-7B decode shapes, fp32 x")
+        for b in ((1, 4) if "q4_0_q8" in want else ()):
+            sec[f"q4_0_q8_gemv_b{b}"] = q4_0_q8_workload(
+                qmv, b, 50, f"q4_0 GEMV over per-32 int8 activations, batch {b}, Llama-7B decode shapes")
         if "cb4_moe" in want:
             sec["cb4_moe"] = moe_workload(qmv, 64, "4-bit codebook MoE FFN, batch 1, 256 experts top-8, "
                                                    "gate/up 2048x7168 + down 7168x2048, bf16 x")

@@ -68,6 +68,8 @@ def lib():
         L.qmv_validate.argtypes = [P, I32, I32]
         L.qmv_gemv.restype = C.c_int
         L.qmv_gemv.argtypes = [P, I32, P, I32, P, P]
+        L.qmv_gemv_q8.restype = C.c_int
+        L.qmv_gemv_q8.argtypes = [P, I32, P, P, P, P]
         L.qmv_dequant.restype = C.c_int
         L.qmv_dequant.argtypes = [P, P, P]
         L.qmm_quant_act.restype = C.c_int
@@ -206,6 +208,20 @@ def gemv(w: QWeights, x, y=None, stream=None):
     _need(y, (torch.float32,), (m, w.n), "y")
     _check(lib().qmv_gemv(w.ref, m, _ptr(x2), _xt_of(x2), _ptr(y), _stream(stream)), "qmv_gemv")
     return y[0] if squeeze else y
+
+
+def gemv_q8(w: QWeights, xq, xs, y=None, stream=None):
+    """q4_0 GEMV over int8 activations (xq int8 [m][k], xs fp32 [m][k/32], as quant_act
+    writes them); y fp32 [m][n] is allocated unless given."""
+    import torch
+    m = xq.shape[0]
+    _need(xq, (torch.int8,), (m, w.k), "xq")
+    _need(xs, (torch.float32,), (m, w.k // 32), "xs")
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=xq.device)
+    _need(y, (torch.float32,), (m, w.n), "y")
+    _check(lib().qmv_gemv_q8(w.ref, m, _ptr(xq), _ptr(xs), _ptr(y), _stream(stream)), "qmv_gemv_q8")
+    return y
 
 
 def dequant(w: QWeights, out=None, stream=None):

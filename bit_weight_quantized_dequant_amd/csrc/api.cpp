@@ -215,6 +215,17 @@ int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *
     return finish_launch("qmv_gemv", w, m, path);
 }
 
+int qmv_gemv_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *xs, float *y, void *stream) {
+    int rc = qmv_validate(w, m, QMV_F32);
+    if (rc) return rc;
+    if (w->fmt != QMV_Q4_0) return QMV_ERR_FORMAT;
+    if (!xq || !xs || !y) return QMV_ERR_NULL;
+    if (!aligned16(xq) || !aligned16(xs) || !aligned16(y)) return QMV_ERR_ALIGN;
+    const char *path = launch_gemv_q4_0_q8(w, m, xq, xs, y, (hipStream_t)stream);
+    if (!path) return QMV_ERR_LIMIT;
+    return finish_launch("qmv_gemv_q8", w, m, path);
+}
+
 int qmv_dequant(const qmv_weights *w, float *out, void *stream) {
     int rc = qmv_validate(w, 1, QMV_F32);
     if (rc) return rc;

@@ -134,6 +134,24 @@ int qmv_validate(const qmv_weights *w, int32_t m, int32_t xt);
 int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *y, void *stream);
 
 /*
+ * q4_0 decode GEMV over per-32 int8 activations (the integer-dot form; quantprobe
+ * LAWS.md, Law 4's per-format amendment, L-15: integer dot products over quantized
+ * activations recover most of the unpack cost on a standalone matvec):
+ *   y[b][i] = sum_c d[i][c] * xs[b][c] * I[b][i][c],
+ *   I[b][i][c] = sum over the 32 weights of block c of (q[i][j] - 8) * xq[b][j]  (exact int),
+ * scaled and accumulated in fp32.  xq / xs are what qmm_quant_act writes for x, so one
+ * quantization serves every GEMV that reads the same activations.
+ *   w : QMV_Q4_0 only (QMV_ERR_FORMAT otherwise).
+ *   xq: device int8 [m][k]; xs: device fp32 [m][k/32]; y: device fp32 [m][n]; each
+ *       16-byte aligned (QMV_ERR_ALIGN).  m: 1..QMV_MAX_BATCH.
+ *   Bounds: k <= 16384; the staged activations, 40 * (64 * m * ceil(k / 2048) + 1) bytes,
+ *   within one workgroup's LDS (every m * k <= 65536 fits); n < 2^31.  QMV_ERR_LIMIT
+ *   otherwise.
+ *   Errors: any QMV_ERR_* from qmv_validate; QMV_ERR_NULL; QMV_ERR_HIP.
+ */
+int qmv_gemv_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *xs, float *y, void *stream);
+
+/*
  * Dequantize W to dense fp32 out[n][k] (device).  Every q4_0, q6_K, CB4 and CB8
  * weight is exactly representable in fp32 and is written exactly; additive-code
  * weights are s times the fp32 sum of the codebook entries (exact when the entries
