@@ -211,8 +211,8 @@ def gemv(w: QWeights, x, y=None, stream=None):
 
 
 def gemv_q8(w: QWeights, xq, xs, y=None, stream=None):
-    """q4_0 GEMV over int8 activations (xq int8 [m][k], xs fp32 [m][k/32], as quant_act
-    writes them); y fp32 [m][n] is allocated unless given."""
+    """q4_0 or q6_K GEMV over int8 activations (xq int8 [m][k], xs fp32 [m][k/32], as
+    quant_act writes them); y fp32 [m][n] is allocated unless given."""
     import torch
     m = xq.shape[0]
     _need(xq, (torch.int8,), (m, w.k), "xq")

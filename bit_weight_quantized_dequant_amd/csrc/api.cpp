@@ -218,10 +218,11 @@ int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *
 int qmv_gemv_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *xs, float *y, void *stream) {
     int rc = qmv_validate(w, m, QMV_F32);
     if (rc) return rc;
-    if (w->fmt != QMV_Q4_0) return QMV_ERR_FORMAT;
+    if (w->fmt != QMV_Q4_0 && w->fmt != QMV_Q6_K) return QMV_ERR_FORMAT;
     if (!xq || !xs || !y) return QMV_ERR_NULL;
     if (!aligned16(xq) || !aligned16(xs) || !aligned16(y)) return QMV_ERR_ALIGN;
-    const char *path = launch_gemv_q4_0_q8(w, m, xq, xs, y, (hipStream_t)stream);
+    const char *path = w->fmt == QMV_Q4_0 ? launch_gemv_q4_0_q8(w, m, xq, xs, y, (hipStream_t)stream)
+                                          : launch_gemv_q6k_q8(w, m, xq, xs, y, (hipStream_t)stream);
     if (!path) return QMV_ERR_LIMIT;
     return finish_launch("qmv_gemv_q8", w, m, path);
 }

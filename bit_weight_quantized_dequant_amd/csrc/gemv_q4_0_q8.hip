@@ -42,7 +42,36 @@ constexpr size_t q8_lds_bytes(int m, int bpl) { return (size_t)q8_slots(m, bpl) 
 // Blocks (32 bytes of xq each) each thread stages.
 constexpr int q8_blocks_per_thread(int wg, int m, int bpl) { return (m * bpl * 64 + wg - 1) / wg; }
 
+// Adds block b (clamped to bc) of the row to acc[m] for every batch row (nothing when b is
+// past the row end).
+template <int M>
+QMV_DEV void q4_block(uint4 w, uint16_t dbits, int b, int bc, int nblk, const uint4 *xlo, const uint4 *xhi,
+                      const float2 *meta, float (&acc)[M]) {
+    const float d = h2f(dbits);
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        const uint4 lo = xlo[m * nblk + bc], hi = xhi[m * nblk + bc];
+        const float2 mt = meta[m * nblk + bc];
+        int a = __float_as_int(mt.y);
+        a = __builtin_amdgcn_sdot4((int)(w.x & 0x0F0F0F0Fu), (int)lo.x, a, false);
+        a = __builtin_amdgcn_sdot4((int)(w.y & 0x0F0F0F0Fu), (int)lo.y, a, false);
+        a = __builtin_amdgcn_sdot4((int)(w.z & 0x0F0F0F0Fu), (int)lo.z, a, false);
+        a = __builtin_amdgcn_sdot4((int)(w.w & 0x0F0F0F0Fu), (int)lo.w, a, false);
+        int h = __builtin_amdgcn_sdot4((int)((w.x & 0xF0F0F0F0u) ^ 0x80808080u), (int)hi.x, 0, false);
+        h = __builtin_amdgcn_sdot4((int)((w.y & 0xF0F0F0F0u) ^ 0x80808080u), (int)hi.y, h, false);
+        h = __builtin_amdgcn_sdot4((int)((w.z & 0xF0F0F0F0u) ^ 0x80808080u), (int)hi.z, h, false);
+        h = __builtin_amdgcn_sdot4((int)((w.w & 0xF0F0F0F0u) ^ 0x80808080u), (int)hi.w, h, false);
+        const float t = (float)((a << 4) + h) * mt.x;
+        const float v = fmaf(d, t, acc[m]);
+        acc[m] = b < nblk ? v : acc[m];
+    }
+}
+
 // One wave per weight row, all m batch rows; lane l owns blocks l, l + 64, ...
+// ROLL (more than 8 batch-row x block products per lane): the blocks are walked in a rolled
+// loop with the next block's loads in flight during this one's dots; unrolled, the compiler
+// keeps every block's activation reads live and runs out of registers.  Otherwise every
+// block of the lane is loaded up front.
 template <int WG, int M, int BPL>
 __global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_q8_kernel(const uint8_t *__restrict__ qs,
                                                                   const uint16_t *__restrict__ dsc,
@@ -53,6 +82,8 @@ __global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_q8_kernel(const uint8_
     constexpr int WAVES = WG / 64;
     constexpr int SLOTS = q8_slots(M, BPL);
     constexpr int XPT = q8_blocks_per_thread(WG, M, BPL);
+    constexpr bool ROLL = M * BPL > 8;
+    constexpr int NU = ROLL ? 1 : BPL;             // blocks held in registers before the barrier
     const int nblk = k >> 5;
     const int mb_total = M * nblk;                 // (batch row, block) pairs, m-major
     uint4 *xlo = lds4;                             // bytes 0..15 of each block
@@ -75,12 +106,12 @@ __global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_q8_kernel(const uint8_
     }
     __builtin_amdgcn_sched_barrier(0);  // the activation loads are issued before the weights'
 
-    uint4 q[BPL];
-    uint16_t dd[BPL];
+    uint4 q[NU];
+    uint16_t dd[NU];
     const uint4 *qrow = (const uint4 *)(qs + (int64_t)rowc * (k >> 1));
     const uint16_t *drow = dsc + (int64_t)rowc * nblk;
 #pragma unroll
-    for (int u = 0; u < BPL; u++) {
+    for (int u = 0; u < NU; u++) {
         int b = lane + 64 * u;
         b = b < nblk ? b : nblk - 1;
         q[u] = ld_stream16(qrow + b);
@@ -105,28 +136,24 @@ __global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_q8_kernel(const uint8_
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; m++) acc[m] = 0.f;
+    if constexpr (ROLL) {
+        uint4 qc = q[0];
+        uint16_t dc = dd[0];
+#pragma unroll 1
+        for (int u = 0; u < BPL; u++) {
+            const int b = lane + 64 * u, bn = b + 64;
+            const int bnc = bn < nblk ? bn : nblk - 1;  // past the end: re-read, unused
+            const uint4 qn = ld_stream16(qrow + bnc);
+            const uint16_t dn = drow[bnc];
+            q4_block<M>(qc, dc, b, b < nblk ? b : nblk - 1, nblk, xlo, xhi, meta, acc);
+            qc = qn;
+            dc = dn;
+        }
+    } else {
 #pragma unroll
-    for (int u = 0; u < BPL; u++) {
-        const int b = lane + 64 * u;
-        const int bc = b < nblk ? b : nblk - 1;
-        const uint4 w = q[u];
-        const float d = h2f(dd[u]);
-#pragma unroll
-        for (int m = 0; m < M; m++) {
-            const uint4 lo = xlo[m * nblk + bc], hi = xhi[m * nblk + bc];
-            const float2 mt = meta[m * nblk + bc];
-            int a = __float_as_int(mt.y);
-            a = __builtin_amdgcn_sdot4((int)(w.x & 0x0F0F0F0Fu), (int)lo.x, a, false);
-            a = __builtin_amdgcn_sdot4((int)(w.y & 0x0F0F0F0Fu), (int)lo.y, a, false);
-            a = __builtin_amdgcn_sdot4((int)(w.z & 0x0F0F0F0Fu), (int)lo.z, a, false);
-            a = __builtin_amdgcn_sdot4((int)(w.w & 0x0F0F0F0Fu), (int)lo.w, a, false);
-            int h = __builtin_amdgcn_sdot4((int)((w.x & 0xF0F0F0F0u) ^ 0x80808080u), (int)hi.x, 0, false);
-            h = __builtin_amdgcn_sdot4((int)((w.y & 0xF0F0F0F0u) ^ 0x80808080u), (int)hi.y, h, false);
-            h = __builtin_amdgcn_sdot4((int)((w.z & 0xF0F0F0F0u) ^ 0x80808080u), (int)hi.z, h, false);
-            h = __builtin_amdgcn_sdot4((int)((w.w & 0xF0F0F0F0u) ^ 0x80808080u), (int)hi.w, h, false);
-            const float t = (float)((a << 4) + h) * mt.x;
-            const float v = fmaf(d, t, acc[m]);
-            acc[m] = b < nblk ? v : acc[m];
+        for (int u = 0; u < BPL; u++) {
+            const int b = lane + 64 * u;
+            q4_block<M>(q[u], dd[u], b, b < nblk ? b : nblk - 1, nblk, xlo, xhi, meta, acc);
         }
     }
 #pragma unroll

@@ -29,6 +29,9 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
 // q4_0 over per-32 int8 activations (xq int8 [m][k], xs fp32 [m][k/32]).
 const char *launch_gemv_q4_0_q8(const qmv_weights *w, int m, const int8_t *xq, const float *xs, float *y,
                                 hipStream_t s);
+// q6_K over per-32 int8 activations (the same arithmetic as the q6_K contraction).
+const char *launch_gemv_q6k_q8(const qmv_weights *w, int m, const int8_t *xq, const float *xs, float *y,
+                               hipStream_t s);
 const char *launch_gemv_q6k(const qmv_weights *w, int m, const void *x, int xt, float *y,
                             hipStream_t s);
 const char *launch_gemv_cb4(const qmv_weights *w, int m, const void *x, int xt, float *y,

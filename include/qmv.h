@@ -134,19 +134,22 @@ int qmv_validate(const qmv_weights *w, int32_t m, int32_t xt);
 int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *y, void *stream);
 
 /*
- * q4_0 decode GEMV over per-32 int8 activations (the integer-dot form; quantprobe
- * LAWS.md, Law 4's per-format amendment, L-15: integer dot products over quantized
- * activations recover most of the unpack cost on a standalone matvec):
- *   y[b][i] = sum_c d[i][c] * xs[b][c] * I[b][i][c],
- *   I[b][i][c] = sum over the 32 weights of block c of (q[i][j] - 8) * xq[b][j]  (exact int),
- * scaled and accumulated in fp32.  xq / xs are what qmm_quant_act writes for x, so one
- * quantization serves every GEMV that reads the same activations.
- *   w : QMV_Q4_0 only (QMV_ERR_FORMAT otherwise).
+ * Decode GEMV over per-32 int8 activations (the integer-dot form; quantprobe LAWS.md,
+ * Law 4's per-format amendment, L-15: integer dot products over quantized activations
+ * recover most of the unpack cost on a standalone matvec).  xq / xs are what
+ * qmm_quant_act writes for x, so one quantization serves every GEMV that reads the same
+ * activations.  Exact integer block sums, scaled and accumulated in fp32:
+ *   q4_0: y[b][i] = sum_c d[i][c] * xs[b][c] * I[b][i][c],
+ *         I = sum over the 32 weights of block c of (q - 8) * xq;
+ *   q6_K: y[b][i] = sum_s d[i][s] * sum_{c in s} xs[b][c] * I[b][i][c],
+ *         I = sum over the two 16-weight sub-blocks j of block c of
+ *             sc[i][j] * sum (q - 32) * xq   (the arithmetic of qmm_gemm_q8).
+ *   w : QMV_Q4_0 or QMV_Q6_K (QMV_ERR_FORMAT otherwise).
  *   xq: device int8 [m][k]; xs: device fp32 [m][k/32]; y: device fp32 [m][n]; each
  *       16-byte aligned (QMV_ERR_ALIGN).  m: 1..QMV_MAX_BATCH.
- *   Bounds: k <= 16384; the staged activations, 40 * (64 * m * ceil(k / 2048) + 1) bytes,
- *   within one workgroup's LDS (every m * k <= 65536 fits); n < 2^31.  QMV_ERR_LIMIT
- *   otherwise.
+ *   Bounds: k <= 16384; the staged activations within one workgroup's LDS, i.e.
+ *   40 * (64 * m * ceil(k / 2048) + 1) bytes for q4_0 and 24 * (256 * m * ceil(k / 4096)
+ *   + 1) for q6_K (every m * k <= 65536 fits both); n < 2^31.  QMV_ERR_LIMIT otherwise.
  *   Errors: any QMV_ERR_* from qmv_validate; QMV_ERR_NULL; QMV_ERR_HIP.
  */
 int qmv_gemv_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *xs, float *y, void *stream);

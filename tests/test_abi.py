@@ -155,7 +155,8 @@ def test_gemv_q8_argument_errors():
     # checked on the host before any HIP call
     L = qmv.lib()
     nz = 1 << 20
-    assert L.qmv_gemv_q8(_fake(qmv.Q6_K, 8, 256).ref, 1, nz, nz, nz, None) == -3   # q4_0 only
+    assert L.qmv_gemv_q8(_fake(qmv.CB4, 8, 256).ref, 1, nz, nz, nz, None) == -3    # q4_0 and q6_K only
+    assert L.qmv_gemv_q8(_fake(qmv.Q6_K, 8, 16384 + 256).ref, 1, nz, nz, nz, None) == -9
     assert L.qmv_gemv_q8(_fake(qmv.Q4_0, 8, 64).ref, 1, None, nz, nz, None) == -1
     assert L.qmv_gemv_q8(_fake(qmv.Q4_0, 8, 64).ref, 9, nz, nz, nz, None) == -6    # batch > 8
     assert L.qmv_gemv_q8(_fake(qmv.Q4_0, 8, 64).ref, 1, nz + 8, nz, nz, None) == -5
