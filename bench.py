@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--only-primary", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--secondary", default="q6_K_gemv,q4_0_batch,q4_0_q8,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm",
+    ap.add_argument("--secondary", default="q6_K_gemv,q6_K_decode,q4_0_batch,q4_0_q8,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm",
                     help="comma-separated secondary workloads to run")
     return ap.parse_args()
 
@@ -200,25 +200,25 @@ def gemv_workload(qmv, fmt, shapes, batch, xt, steps, label):
             "shapes": per_shape}
 
 
-def q4_0_q8_workload(qmv, batch, steps, label):
-    """The q4_0 GEMV over per-32 int8 activations on the three decode shapes (one step = one
-    GEMV per shape, activations quantized beforehand, as they are once per activation vector
-    for every GEMV that reads it).  The same step with one quantizer launch in front of each
-    GEMV is timed too and reported beside it."""
+def q8_workload(qmv, fmt, batch, steps, label):
+    """The GEMV over per-32 int8 activations (q4_0 or q6_K) on the three decode shapes (one
+    step = one GEMV per shape, activations quantized beforehand, as they are once per
+    activation vector for every GEMV that reads it).  The same step with one quantizer
+    launch in front of each GEMV is timed too and reported beside it."""
     import torch
     shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]
-    per_set = sum(qmv.weight_bytes(synth.FMT_Q4_0, n, k) for n, k in shapes)
+    per_set = sum(qmv.weight_bytes(fmt, n, k) for n, k in shapes)
     copies = pool_copies(per_set)
     mats, xs, qs, ys, algo = [], [], [], [], []
     for i, (n, k) in enumerate(shapes):
-        _, pool = make_pool(qmv, synth.FMT_Q4_0, n, k, seed=i, copies=copies)
+        _, pool = make_pool(qmv, fmt, n, k, seed=i, copies=copies)
         mats.append(pool)
         x = torch.from_numpy(synth.gen_x(batch, k, synth.DT_F32, seed=i)).cuda()
         xs.append(x)
         qs.append(qmv.quant_act(x))
         ys.append(torch.empty((batch, n), dtype=torch.float32, device="cuda"))
         # weights + int8 activations and their scales + outputs
-        algo.append(qmv.weight_bytes(synth.FMT_Q4_0, n, k) + batch * (k + k // 8) + 4 * batch * n)
+        algo.append(qmv.weight_bytes(fmt, n, k) + batch * (k + k // 8) + 4 * batch * n)
 
     def step(i):
         for s in range(len(shapes)):
@@ -416,8 +416,15 @@ def main():
                                                    b, synth.DT_F32, 50,
                                                    f"q4_0 GEMV batch {b}, Llama-7B decode shapes, fp32 x")
         for b in ((1, 4) if "q4_0_q8" in want else ()):
-            sec[f"q4_0_q8_gemv_b{b}"] = q4_0_q8_workload(
-                qmv, b, 50, f"q4_0 GEMV over per-32 int8 activations, batch {b}, Llama-7B decode shapes")
+            sec[f"q4_0_q8_gemv_b{b}"] = q8_workload(
+                qmv, synth.FMT_Q4_0, b, 50, f"q4_0 GEMV over per-32 int8 activations, batch {b}, Llama-7B decode shapes")
+        if "q6_K_decode" in want:
+            sec["q6_K_gemv_llama"] = gemv_workload(qmv, synth.FMT_Q6_K, [(4096, 4096), (11008, 4096), (4096, 11008)],
+                                                   1, synth.DT_F32, 50,
+                                                   "q6_K GEMV batch 1, Llama-7B decode shapes, fp32 x")
+        for b in ((1, 4) if "q6_K_decode" in want else ()):
+            sec[f"q6_K_q8_gemv_b{b}"] = q8_workload(
+                qmv, synth.FMT_Q6_K, b, 50, f"q6_K GEMV over per-32 int8 activations, batch {b}, Llama-7B decode shapes")
         if "cb4_moe" in want:
             sec["cb4_moe"] = moe_workload(qmv, 64, "4-bit codebook MoE FFN, batch 1, 256 experts top-8, "
                                                    "gate/up 2048x7168 + down 7168x2048, bf16 x")
