@@ -58,6 +58,11 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"libqmv.so not built ({LIB_PATH}); run "
                               "`python bit_weight_quantized_dequant_amd/build.py`")
+        # torch carries its own HIP and HSA runtimes: loaded first, they are the ones the
+        # library binds to (its libamdhip64 dependency resolves to the library already in
+        # the process).  Loaded after the library, a second HSA runtime would start and the
+        # two would not share devices, memory or streams.
+        import torch  # noqa: F401
         L = C.CDLL(LIB_PATH)
         P, I32, I64 = C.c_void_p, C.c_int32, C.c_int64
         L.qmv_plane_bytes.restype = I64

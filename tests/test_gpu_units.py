@@ -98,3 +98,26 @@ def test_quantizer_golden_and_edge_blocks(qmv):
     assert np.array_equal(xq, rq)
     assert np.array_equal(xs.view(np.uint32), rs.view(np.uint32))
     assert xq[0, :32].tolist() == g["a_xq"] and xq[0, 64:96].tolist() == g["c_xq"]
+
+
+def test_library_loaded_before_torch(qmv):
+    # torch carries its own HIP runtime; the binding imports torch before it opens the library,
+    # so a program that loads the library first still runs one runtime (checked in a fresh
+    # process, since this one has imported torch already)
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = (
+        "import sys; sys.path[:0] = [%r, %r]\n"
+        "import bit_weight_quantized_dequant_amd as q\n"
+        "q.lib()\n"
+        "import torch, numpy as np, synth, oracle\n"
+        "x = synth.gen_x(2, 256, seed=3)\n"
+        "xq, xs = q.quant_act(torch.from_numpy(x).cuda())\n"
+        "torch.cuda.synchronize()\n"
+        "oq, os_ = oracle.quant_act(x)\n"
+        "assert np.array_equal(xq.cpu().numpy(), oq) and np.array_equal(xs.cpu().numpy(), os_)\n"
+        "print('ok')\n" % (os.path.dirname(here), here))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=100)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
