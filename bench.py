@@ -163,6 +163,28 @@ def q4_0_workload(qmv, steps, warmup):
             "copies": copies, "pool_bytes": copies * per_set, "shapes": per_shape}
 
 
+def read_ceiling(qmv, sizes, steps):
+    """The stream-read ceiling: the library's read-only kernel over a rotating pool of
+    distinct buffers of each size (cold, as the GEMVs' pools), and once over 4 GiB."""
+    import torch
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = []
+    for b in sizes:
+        b16 = (b + 15) // 16 * 16
+        copies = pool_copies(b16)
+        pool = torch.zeros((copies, b16), dtype=torch.uint8, device="cuda")
+        R = max(steps, 60)
+        avg = time_graph(graph_of(lambda i: qmv.read_ceiling(pool[i % copies], sink), R), R)
+        out.append({"bytes": b16, "avg_launch_ms": round(avg, 5), "GBps": round(b16 / avg / 1e6, 1)})
+        del pool
+    big = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
+    avg = time_graph(graph_of(lambda i: qmv.read_ceiling(big, sink), 5), 5)
+    large = {"bytes": big.numel(), "avg_launch_ms": round(avg, 4), "GBps": round(big.numel() / avg / 1e6, 1)}
+    del big
+    torch.cuda.synchronize()
+    return {"kernel": "read_ceiling_kernel (128-bit nontemporal loads only)", "sizes": out, "large": large}
+
+
 def gemv_workload(qmv, fmt, shapes, batch, xt, steps, label):
     """Batch-`batch` GEMVs over `shapes` (one step = one GEMV per shape), rotating pool."""
     import torch
@@ -406,6 +428,12 @@ def main():
         "shapes": prim["shapes"],
     }
     if not a.only_primary:
+        # the plain-read floor for each primary shape's bytes, same pool protocol
+        rc = read_ceiling(qmv, [sh["bytes"] for sh in prim["shapes"]], a.steps)
+        for sh, c in zip(out["shapes"], rc["sizes"]):
+            sh["read_ceiling_ms"] = c["avg_launch_ms"]
+            sh["frac_of_read_ceiling"] = round(c["avg_launch_ms"] / sh["avg_launch_ms"], 4)
+        out["read_ceiling"] = rc
         sec = {}
         want = set(a.secondary.split(","))
         if "q6_K_gemv" in want:

@@ -74,6 +74,8 @@ def lib():
         L.qmv_gemv.restype = C.c_int
         L.qmv_gemv.argtypes = [P, I32, P, I32, P, P]
         L.qmv_gemv_q8.restype = C.c_int
+        L.qmv_read_ceiling.restype = C.c_int
+        L.qmv_read_ceiling.argtypes = [P, I64, P, P]
         L.qmv_gemv_q8.argtypes = [P, I32, P, P, P, P]
         L.qmv_dequant.restype = C.c_int
         L.qmv_dequant.argtypes = [P, P, P]
@@ -227,6 +229,17 @@ def gemv_q8(w: QWeights, xq, xs, y=None, stream=None):
     _need(y, (torch.float32,), (m, w.n), "y")
     _check(lib().qmv_gemv_q8(w.ref, m, _ptr(xq), _ptr(xs), _ptr(y), _stream(stream)), "qmv_gemv_q8")
     return y
+
+
+def read_ceiling(t, sink, stream=None):
+    """Measurement only: read every byte of device tensor t (contiguous, a multiple of 16
+    bytes) and nothing else; sink is a device int32/uint32 tensor of at least one element."""
+    import torch
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("t: must be a contiguous device tensor")
+    _need(sink, (torch.int32,), None, "sink")
+    _check(lib().qmv_read_ceiling(_ptr(t), t.numel() * t.element_size(), _ptr(sink), _stream(stream)),
+           "qmv_read_ceiling")
 
 
 def dequant(w: QWeights, out=None, stream=None):

@@ -247,6 +247,15 @@ int qmm_quant_act(const float *x, int32_t m, int64_t k, int8_t *xq, float *xs, v
     return finish_launch("qmm_quant_act", nullptr, m, path);
 }
 
+int qmv_read_ceiling(const void *p, int64_t bytes, uint32_t *sink, void *stream) {
+    if (!p || !sink) return QMV_ERR_NULL;
+    if (bytes <= 0 || bytes % 16) return QMV_ERR_SHAPE;
+    if (!aligned16(p) || ((uintptr_t)sink & 3u)) return QMV_ERR_ALIGN;
+    const char *path = launch_read_ceiling(p, bytes, sink, (hipStream_t)stream);
+    if (!path) return QMV_ERR_LIMIT;
+    return finish_launch("qmv_read_ceiling", nullptr, 1, path);
+}
+
 int64_t qmm_workspace_bytes(const qmv_weights *w, int32_t m) {
     if (!w) return QMV_ERR_NULL;
     if (w->fmt != QMV_Q6_K) return QMV_ERR_FORMAT;

@@ -41,6 +41,8 @@ const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, f
 const char *launch_gemv_cb8(const qmv_weights *w, int m, const void *x, int xt, float *y,
                             hipStream_t s);
 const char *launch_dequant(const qmv_weights *w, float *out, hipStream_t s);
+// The stream-read ceiling: reads `bytes` (a multiple of 16) from p and nothing else.
+const char *launch_read_ceiling(const void *p, int64_t bytes, uint32_t *sink, hipStream_t s);
 const char *launch_quant_act(const float *x, int m, int64_t k, int8_t *xq, float *xs, hipStream_t s);
 // plane: the registered pre-expanded H/L planes of w (int8 [n][k] each, H then L), or
 // nullptr for the in-kernel expansion of the codes.

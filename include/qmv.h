@@ -172,6 +172,20 @@ int qmv_dequant(const qmv_weights *w, float *out, void *stream);
  */
 int qmm_quant_act(const float *x, int32_t m, int64_t k, int8_t *xq, float *xs, void *stream);
 
+/*
+ * Measurement: the stream-read ceiling ("LLMs on the Xiaomi TV Box", §11.5 E10: measure the
+ * streaming-read ceiling first; quantprobe LAWS.md, Law 4: decode is bytes over bandwidth).
+ * Reads `bytes` bytes at p with the GEMVs' access pattern (128-bit nontemporal loads, one
+ * contiguous piece per workgroup) and does nothing else, so its time is the floor for a
+ * kernel that reads that many bytes.  Not part of the GEMV or GEMM path.
+ *   p: device, 16-byte aligned; bytes: > 0, a multiple of 16 (QMV_ERR_SHAPE otherwise);
+ *   sink: device uint32, written only if the XOR of all words read equals 0x9E3779B9
+ *   (practically never; it keeps the loads from being removed).
+ *   Errors: QMV_ERR_NULL, QMV_ERR_SHAPE, QMV_ERR_ALIGN, QMV_ERR_LIMIT (more than 2^31
+ *   workgroups), QMV_ERR_HIP.
+ */
+int qmv_read_ceiling(const void *p, int64_t bytes, uint32_t *sink, void *stream);
+
 /* Workspace bytes qmm_gemm needs for m activation rows (xq and xs), or < 0 on error. */
 int64_t qmm_workspace_bytes(const qmv_weights *w, int32_t m);
 

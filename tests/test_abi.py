@@ -161,3 +161,14 @@ def test_gemv_q8_argument_errors():
     assert L.qmv_gemv_q8(_fake(qmv.Q4_0, 8, 64).ref, 9, nz, nz, nz, None) == -6    # batch > 8
     assert L.qmv_gemv_q8(_fake(qmv.Q4_0, 8, 64).ref, 1, nz + 8, nz, nz, None) == -5
     assert L.qmv_gemv_q8(_fake(qmv.Q4_0, 8, 16384 + 32).ref, 1, nz, nz, nz, None) == -9
+
+
+def test_read_ceiling_argument_errors():
+    L = qmv.lib()
+    nz = 1 << 20
+    assert L.qmv_read_ceiling(None, 64, nz, None) == -1
+    assert L.qmv_read_ceiling(nz, 64, None, None) == -1
+    assert L.qmv_read_ceiling(nz, 0, nz, None) == -2
+    assert L.qmv_read_ceiling(nz, 40, nz, None) == -2
+    assert L.qmv_read_ceiling(nz + 8, 64, nz, None) == -5
+    assert L.qmv_read_ceiling(nz, 64, nz + 2, None) == -5

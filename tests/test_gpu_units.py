@@ -121,3 +121,16 @@ def test_library_loaded_before_torch(qmv):
         "print('ok')\n" % (os.path.dirname(here), here))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=100)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+
+
+def test_read_ceiling_reads_and_writes_nothing(qmv):
+    # the measurement kernel leaves its sink alone for ordinary data (the XOR of a zero
+    # buffer is 0, not the sentinel), and covers ragged sizes
+    import torch
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    for nbytes in (16, 4096 * 16 + 48, 25362432):
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        qmv.read_ceiling(buf, sink)
+        torch.cuda.synchronize()
+        assert qmv.last_path() == "read-ceiling.16B-per-thread"
+        assert sink.item() == 7
