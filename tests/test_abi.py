@@ -172,3 +172,14 @@ def test_read_ceiling_argument_errors():
     assert L.qmv_read_ceiling(nz, 40, nz, None) == -2
     assert L.qmv_read_ceiling(nz + 8, 64, nz, None) == -5
     assert L.qmv_read_ceiling(nz, 64, nz + 2, None) == -5
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # one GPU only: the bench says so and exits before touching a device
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in (r.stdout + r.stderr)
