@@ -163,7 +163,7 @@ def q4_0_workload(qmv, steps, warmup):
             "copies": copies, "pool_bytes": copies * per_set, "shapes": per_shape}
 
 
-def read_ceiling(qmv, sizes, steps):
+def read_ceiling(qmv, sizes, steps, large=True):
     """The stream-read ceiling: the library's read-only kernel over a rotating pool of
     distinct buffers of each size (cold, as the GEMVs' pools), and once over 4 GiB."""
     import torch
@@ -177,6 +177,8 @@ def read_ceiling(qmv, sizes, steps):
         avg = time_graph(graph_of(lambda i: qmv.read_ceiling(pool[i % copies], sink), R), R)
         out.append({"bytes": b16, "avg_launch_ms": round(avg, 5), "GBps": round(b16 / avg / 1e6, 1)})
         del pool
+    if not large:
+        return {"kernel": "read_ceiling_kernel (128-bit nontemporal loads only)", "sizes": out}
     big = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
     avg = time_graph(graph_of(lambda i: qmv.read_ceiling(big, sink), 5), 5)
     large = {"bytes": big.numel(), "avg_launch_ms": round(avg, 4), "GBps": round(big.numel() / avg / 1e6, 1)}
@@ -215,10 +217,12 @@ def gemv_workload(qmv, fmt, shapes, batch, xt, steps, label):
         qmv.gemv(mats[s][0], xs[s], ys[s])
         per_shape.append({"shape": f"{n}x{k}", "bytes": algo[s], "avg_launch_ms": round(avg, 5),
                           "GBps": round(algo[s] / avg / 1e6, 1), "path": qmv.last_path()})
+    path = qmv.last_path()
+    add_ceiling(qmv, per_shape, steps)
     gbs = sum(algo) / ms / 1e6
     return {"workload": label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "ms_per_step": round(ms, 5), "bytes_per_step": sum(algo), "pool_copies": copies,
-            "path": qmv.last_path(), "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+            "path": path, "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
             "shapes": per_shape}
 
 
@@ -260,12 +264,22 @@ def q8_workload(qmv, fmt, batch, steps, label):
         qmv.gemv_q8(mats[s][0], qs[s][0], qs[s][1], ys[s])
         per_shape.append({"shape": f"{n}x{k}", "bytes": algo[s], "avg_launch_ms": round(avg, 5),
                           "GBps": round(algo[s] / avg / 1e6, 1), "path": qmv.last_path()})
+    path = qmv.last_path()
+    add_ceiling(qmv, per_shape, steps)
     gbs = sum(algo) / ms / 1e6
     return {"workload": label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "ms_per_step": round(ms, 5), "bytes_per_step": sum(algo), "pool_copies": copies,
             "with_quant_act": {"ms_per_step": round(ms_q, 5), "GBps": round(sum(algo) / ms_q / 1e6, 1)},
-            "path": qmv.last_path(), "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+            "path": path, "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
             "shapes": per_shape}
+
+
+def add_ceiling(qmv, per_shape, steps):
+    """Per shape: the stream-read ceiling for its bytes and the kernel's fraction of it."""
+    rc = read_ceiling(qmv, [sh["bytes"] for sh in per_shape], steps, large=False)
+    for sh, c in zip(per_shape, rc["sizes"]):
+        sh["read_ceiling_ms"] = c["avg_launch_ms"]
+        sh["frac_of_read_ceiling"] = round(c["avg_launch_ms"] / sh["avg_launch_ms"], 4)
 
 
 def moe_workload(qmv, tokens, label):
