@@ -376,11 +376,14 @@ template <bool EXP>
 const char *launch_gemm(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs,
                         float *y, int32_t *partials, hipStream_t s) {
     const int64_t n = w->n;
-    // 64-row tiles when they give at least two workgroups per CU, else 32-row tiles
+    // 64-row tiles when they give at least two workgroups per CU (one, when copying
+    // registered planes: 4096x11008 at M = 512 then runs 288-292 against 276-287 TOPS with
+    // 32-row tiles, while the in-kernel expansion keeps 32-row tiles there, 256-266 against
+    // 220-221), else 32-row tiles
     const int64_t tiles64 = ((n + 63) / 64) * ((m + BM - 1) / BM);
     const char *fp = forced_path();  // test-only overrides of the tile width and prefetch distance
     const bool wide = strcmp(fp, "gemm.w64") == 0 ? true : strcmp(fp, "gemm.w32") == 0 ? false
-                                                      : tiles64 >= 2 * (int64_t)device_info().num_cus;
+                                                      : tiles64 >= (EXP ? 1 : 2) * (int64_t)device_info().num_cus;
     if (partials) {
         if (wide) launch_tiles<2, true, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
         else launch_tiles<1, true, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
