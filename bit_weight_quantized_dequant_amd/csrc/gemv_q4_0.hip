@@ -290,13 +290,58 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_chunked_kernel(const uint8_t *__
         __syncthreads();
         const int b = c * 64 + lane;
         const float d = h2f(dc);
+        if constexpr (M <= 2) {
 #pragma unroll
-        for (int m = 0; m < M; m++) {
-            float xb[32];
+            for (int m = 0; m < M; m++) {
+                float xb[32];
 #pragma unroll
-            for (int i = 0; i < 8; i++) *(float4 *)(xb + 4 * i) = sx4[(m * 64 + lane) * XS4 + i];
-            const float v = fmaf(d, dot_q4_mix(qc, xb), acc[m]);
-            acc[m] = b < nblk ? v : acc[m];
+                for (int i = 0; i < 8; i++) *(float4 *)(xb + 4 * i) = sx4[(m * 64 + lane) * XS4 + i];
+                const float v = fmaf(d, dot_q4_mix(qc, xb), acc[m]);
+                acc[m] = b < nblk ? v : acc[m];
+            }
+        } else {
+            // three or more batch rows: the block's 32 weights (q - 8) expanded once to fp32
+            // (exact: a nibble under the binary16 exponent of 1024, one packed half subtract,
+            // a conversion), then one fp32 FMA per weight and batch row, v_fmac_f32 instead of
+            // v_fma_mix_f32: the same exact products in fewer cycles once the expansion is
+            // shared by enough rows
+            float wq[32];
+            const uint32_t wv[4] = {qc.x, qc.y, qc.z, qc.w};
+            const qmv_h2 off = {(_Float16)-1032.f, (_Float16)-1032.f};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t w = wv[i];
+                const qmv_h2 l02 = as_h2(and_or(w, 0x000F000Fu, 0x64006400u)) + off;         // bytes 0, 2 low
+                const qmv_h2 l13 = as_h2(and_or(w >> 8, 0x000F000Fu, 0x64006400u)) + off;    // bytes 1, 3 low
+                const qmv_h2 h02 = as_h2(and_or(w >> 4, 0x000F000Fu, 0x64006400u)) + off;    // bytes 0, 2 high
+                const qmv_h2 h13 = as_h2(and_or(w >> 12, 0x000F000Fu, 0x64006400u)) + off;   // bytes 1, 3 high
+                wq[4 * i + 0] = (float)l02.x;
+                wq[4 * i + 1] = (float)l13.x;
+                wq[4 * i + 2] = (float)l02.y;
+                wq[4 * i + 3] = (float)l13.y;
+                wq[16 + 4 * i + 0] = (float)h02.x;
+                wq[16 + 4 * i + 1] = (float)h13.x;
+                wq[16 + 4 * i + 2] = (float)h02.y;
+                wq[16 + 4 * i + 3] = (float)h13.y;
+            }
+            // materialise the fp32 weights: otherwise every use folds the conversion back
+            // into a v_fma_mix_f32, once per batch row
+#pragma unroll
+            for (int i = 0; i < 32; i++) asm volatile("" : "+v"(wq[i]));
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                float xb[32];
+#pragma unroll
+                for (int i = 0; i < 8; i++) *(float4 *)(xb + 4 * i) = sx4[(m * 64 + lane) * XS4 + i];
+                float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int i = 0; i < 32; i += 2) {
+                    s0 = fmaf(wq[i], xb[i], s0);
+                    s1 = fmaf(wq[i + 1], xb[i + 1], s1);
+                }
+                const float v = fmaf(d, s0 + s1, acc[m]);
+                acc[m] = b < nblk ? v : acc[m];
+            }
         }
         qc = qn;
         dc = dn;
