@@ -416,7 +416,8 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
     if (bpl > 8 || m > 1 || strcmp(fp, "q4_0.chunked") == 0) {
         if ((int64_t)m * 64 * XS * (int64_t)sizeof(float) > device_info().lds_per_block) return nullptr;
         const bool ok = xt == QMV_F32 ? launch_chunked<0>(m, w, x, y, s) : launch_chunked<1>(m, w, x, y, s);
-        return ok ? "q4_0.lds-x-chunked.fma-mix" : nullptr;
+        if (!ok) return nullptr;
+        return m >= 3 ? "q4_0.lds-x-chunked.fmac" : "q4_0.lds-x-chunked.fma-mix";
     }
     // batch 1: two rows per wave (each staged activation block read once for both) while both
     // rows' blocks fit in registers (bpl <= 4); one row per wave otherwise, on request (test

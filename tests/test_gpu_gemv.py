@@ -59,7 +59,8 @@ def q4_path(m, k):
     # one-shot kernel, two rows per wave while the blocks per lane are at most 4
     bpl = -(-(k // 32) // 64)
     if bpl > 8 or m > 1:
-        return "q4_0.lds-x-chunked.fma-mix"
+        # from three batch rows up the weights are expanded to fp32 once per block
+        return "q4_0.lds-x-chunked.fmac" if m >= 3 else "q4_0.lds-x-chunked.fma-mix"
     return "q4_0.lds-x.fma-mix.2row" if bpl <= 4 else "q4_0.lds-x.fma-mix"
 
 
@@ -95,7 +96,7 @@ def test_q4_0_full_size_sampled(qmv, n, k):
 def test_q4_0_full_size_batched_sampled(qmv, n, k, m):
     # the batch workloads the benchmark times (K-chunked kernel), at their full sizes
     run_case(qmv, synth.FMT_Q4_0, n, k, m, synth.DT_F32, seed=m, rows=sample_rows(n),
-             expect_path="q4_0.lds-x-chunked.fma-mix")
+             expect_path=q4_path(m, k))
 
 
 def test_q4_0_unit_vector_returns_column_exactly(qmv):
@@ -149,7 +150,7 @@ def test_q4_0_chunked_unit_vector_returns_column_exactly(qmv):
         e[r, j] = 1.0
     y = qmv.gemv(W, x_to_device(e, synth.DT_F32))
     torch.cuda.synchronize()
-    assert qmv.last_path() == "q4_0.lds-x-chunked.fma-mix"
+    assert qmv.last_path() == q4_path(m, k)
     y = y.cpu().numpy()
     for r, j in enumerate(cols[:m]):
         assert np.array_equal(y[r], dense[:, j]), j
