@@ -17,7 +17,8 @@
 //     an exactly cancelling pair gives 0.  The weight is applied to every batch row with
 //     an fp32 FMA (decoded once for all rows);
 //   * the 64 lane partials are summed with DPP and scaled by s[n];
-//   * batches run two rows per wave: each activation read from LDS serves both rows.
+//   * batches run two rows per wave (four at batch 8 on tall matrices): each activation
+//     read from LDS serves all of them.
 // Rows whose length is not a multiple of 64 take a plain kernel (byte loads, one K chunk
 // staged at a time).
 #include <cstring>
@@ -270,12 +271,18 @@ void launch_stream(const qmv_weights *w, const void *x, float *y, hipStream_t s)
 
 // Rows per wave of the streaming kernel: two for batches (each activation read from LDS
 // serves both rows, which the batch's LDS traffic needs) when there are rows for at least one
-// such workgroup per CU, else one; test overrides "aq.r1" / "aq.r2" force either.
+// such workgroup per CU, else one; four at batch 8 with rows for one such workgroup per CU
+// (14336x4096: 34.7 -> 28.9 us for the 2-bit code, 39.2 -> 33.3 for the 3-bit one; at batch 4
+// and on 4096-row matrices the halved occupancy loses); test overrides "aq.r1" / "aq.r2" /
+// "aq.r4" force any of them.
 int stream_rows(int m, int64_t n) {
     const char *fp = forced_path();
     if (strcmp(fp, "aq.r1") == 0) return 1;
     if (strcmp(fp, "aq.r2") == 0) return 2;
-    return m > 1 && n >= 2 * WAVES * (int64_t)device_info().num_cus ? 2 : 1;
+    if (strcmp(fp, "aq.r4") == 0) return 4;
+    const int64_t cus = device_info().num_cus;
+    if (m >= 8 && n >= 4 * WAVES * cus) return 4;
+    return m > 1 && n >= 2 * WAVES * cus ? 2 : 1;
 }
 
 template <int NC, int M, int XT>
@@ -283,7 +290,9 @@ void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     const int n = (int)w->n, k = (int)w->k;
     const dim3 grid((n + WAVES - 1) / WAVES);
     if (k % 64 == 0) {
-        if (stream_rows(M, n) == 2) launch_stream<NC, M, 2, XT>(w, x, y, s);
+        const int r = stream_rows(M, n);
+        if (r == 4) launch_stream<NC, M, 4, XT>(w, x, y, s);
+        else if (r == 2) launch_stream<NC, M, 2, XT>(w, x, y, s);
         else launch_stream<NC, M, 1, XT>(w, x, y, s);
     } else {
         hipLaunchKernelGGL((aq_ragged_kernel<NC, M, XT>), grid, dim3(WG), ragged_lds(NC, M), s,
@@ -322,6 +331,8 @@ const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, f
         ok = xt == QMV_F32 ? dispatch_m<3, 0>(m, w, x, y, s) : dispatch_m<3, 1>(m, w, x, y, s);
     if (!ok) return nullptr;
     if (!str) return nc == 2 ? "aq2x8.ragged.lds-codebook.fma-mix" : "aq3x8.ragged.lds-codebook.fma-mix";
+    if (stream_rows(m, w->n) == 4)
+        return nc == 2 ? "aq2x8.stream.lds-codebook.fma-mix.4row" : "aq3x8.stream.lds-codebook.fma-mix.4row";
     if (stream_rows(m, w->n) == 2)
         return nc == 2 ? "aq2x8.stream.lds-codebook.fma-mix.2row" : "aq3x8.stream.lds-codebook.fma-mix.2row";
     return nc == 2 ? "aq2x8.stream.lds-codebook.fma-mix" : "aq3x8.stream.lds-codebook.fma-mix";

@@ -338,13 +338,18 @@ AQ_SMALL = [(1, 8), (5, 24), (9, 64), (33, 1000), (64, 4096), (17, 4096 + 8), (4
             (5, 4160), (3, 8192 + 192)]
 
 
+def aq_rows(m, n):
+    # rows per wave of the streaming kernel: two for batches over at least 2 x 8 rows per CU
+    # (4096 on 256 CUs), four at batch 8 over 4 x 8 rows per CU (8192)
+    return ".4row" if m >= 8 and n >= 8192 else ".2row" if m > 1 and n >= 4096 else ""
+
+
 def aq_path(fmt, k, m=1, n=1):
-    # the streaming kernel when k % 64 == 0 (two rows per wave for batches over at least
-    # 2 x 8 rows per CU, 4096 on 256 CUs), else the ragged one
+    # the streaming kernel when k % 64 == 0, else the ragged one
     name = "aq2x8" if fmt == synth.FMT_AQ2X8 else "aq3x8"
     if k % 64:
         return f"{name}.ragged.lds-codebook.fma-mix"
-    return f"{name}.stream.lds-codebook.fma-mix" + (".2row" if m > 1 and n >= 4096 else "")
+    return f"{name}.stream.lds-codebook.fma-mix" + aq_rows(m, n)
 
 
 @pytest.mark.parametrize("n,k", AQ_SMALL)
@@ -398,16 +403,19 @@ def test_aq_batched_multi_step(qmv, m, xt):
 
 @pytest.mark.parametrize("fmt", [synth.FMT_AQ2X8, synth.FMT_AQ3X8])
 @pytest.mark.parametrize("force,m,n", [("aq.r2", 1, 37), ("aq.r1", 4, 37), ("", 3, 17), ("", 3, 4096 + 17),
-                                       ("aq.r2", 2, 1)])
+                                       ("aq.r2", 2, 1), ("aq.r4", 1, 37), ("aq.r4", 4, 203), ("aq.r4", 8, 6),
+                                       ("", 8, 8192 + 17)])
 def test_aq_rows_per_wave(qmv, monkeypatch, fmt, force, m, n):
-    # one or two rows per wave either way round; odd row counts leave the last wave's second
-    # row past the end
+    # one, two or four rows per wave, forced or by default; row counts that are not a multiple
+    # of the rows per workgroup leave the last wave's later rows past the end
     if force:
         monkeypatch.setenv("QMV_FORCE_PATH", force)
     k = 4096 + 64
     name = "aq2x8" if fmt == synth.FMT_AQ2X8 else "aq3x8"
-    two = force == "aq.r2" or (not force and m > 1 and n >= 4096)
-    run_case(qmv, fmt, n, k, m, synth.DT_F32, seed=n + m, expect_path=f"{name}.stream.lds-codebook.fma-mix" + (".2row" if two else ""))
+    rows = {"aq.r1": "", "aq.r2": ".2row", "aq.r4": ".4row"}.get(force, aq_rows(m, n))
+    sample = sample_rows(n) if n > 4096 else None
+    run_case(qmv, fmt, n, k, m, synth.DT_F32, seed=n + m, rows=sample,
+             expect_path=f"{name}.stream.lds-codebook.fma-mix" + rows)
 
 
 @pytest.mark.parametrize("n,k", AQ_SMALL)
