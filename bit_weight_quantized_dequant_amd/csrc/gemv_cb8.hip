@@ -7,15 +7,18 @@
 // has, would cost 32 bits per weight in codebook bytes alone).
 //
 // Kernel (the streaming skeleton of gemv_stream.h; the format takes k % 64 == 0):
-//   * each wave copies its row's codebook (512 bytes, one 8-byte load per lane) into its
-//     own LDS slice, so one ds_read_u16 returns the fp16 weight for an index;
+//   * each wave copies its row's codebook (256 fp16 entries, one 8-byte load per lane)
+//     into its own LDS slice; at batch 3 and from batch 5 up it expands the entries to
+//     exact fp32 there, so one ds_read_b32 returns the weight of an index as fp32 and no
+//     conversion is left in the dot (otherwise ds_read_u16 and v_fma_mix_f32);
 //   * lane l owns unit l of each 4096-weight step: 64 index bytes, four 128-bit loads,
 //     prefetched a step ahead;
-//   * per dword of 4 indices: two masks form 2 * index in the two 16-bit halves of two
-//     registers (even and odd bytes), one SDWA add per weight selects the half and adds
-//     the slice address, one ds_read_u16 fetches the weight; v_fma_mix_f32 multiplies
-//     the fp16 weight by the fp32 activation (exact product); each looked-up weight is
-//     used for every batch row;
+//   * per dword of 4 indices: two masks form 4 * index (fp32 slice) or 2 * index (fp16)
+//     in the two 16-bit halves of two registers (even and odd bytes), one SDWA add per
+//     weight selects the half and adds the slice address, one LDS read fetches the
+//     weight; each looked-up weight feeds one FMA per batch row (exact product, fp32
+//     sum); on the fp32 path the reads of the next dword are in flight during the FMAs
+//     of this one, and each row keeps two partial sums (even and odd dwords);
 //   * the 64 lane partials are summed with DPP.
 #include "device_common.h"
 #include "gemv_stream.h"
@@ -41,13 +44,23 @@ QMV_DEV float lds_h(uint32_t a) {
     return h2f(*(const __attribute__((address_space(3))) uint16_t *)(uintptr_t)a);
 }
 
+QMV_DEV float lds_f(uint32_t a) { return *(const __attribute__((address_space(3))) float *)(uintptr_t)a; }
+
+// The fp32-slice path (expanded codebook, v_fmac_f32, pipelined reads) at batch 3 and from
+// batch 5 up.  At batch 4 it needs 138 VGPRs, which costs rows of at most 4096 weights
+// their second workgroup per CU (7168x2048: 14.2 -> 17.6 us) and spills when capped at
+// 128, so batch 4 keeps the fp16 path like batch 1 and 2 (measured on one device in turn:
+// batch 3 10.6/13.4 -> 10.3/11.8 us, batch 8 16.2/30.5 -> 14.9/28.0 us at 2048x7168 and
+// 7168x2048).
+constexpr bool f32_tab(int m) { return m == 3 || m >= 5; }
+
 struct Cb8Policy {
     static constexpr int R = 1;  // rows per wave
     struct Codes {
         uint4 q[4];  // index bytes 0..63 of the unit
     };
     const uint8_t *irow;  // this row's indices
-    uint32_t tb;          // LDS byte address of this wave's codebook
+    uint32_t tb;          // LDS byte address of this wave's codebook slice
 
     __device__ __forceinline__ void load(Codes &c, int unit) const {
         const uint8_t *p = irow + (int64_t)unit * 64;
@@ -55,30 +68,107 @@ struct Cb8Policy {
         for (int i = 0; i < 4; i++) c.q[i] = ld_stream16(p + 16 * i);
     }
 
+    // The 4 weights of dword i; the slice holds fp32 (4 * index) or fp16 (2 * index).
     template <int M>
-    __device__ __forceinline__ void dot(const Codes &c, const float *xu, float (&s)[M]) const {
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const uint4 q4 = c.q[i >> 2];
-            const uint32_t w = (i & 3) == 0 ? q4.x : (i & 3) == 1 ? q4.y : (i & 3) == 2 ? q4.z : q4.w;
+    __device__ __forceinline__ void lookup(const Codes &c, int i, float (&v)[4]) const {
+        const uint4 q4 = c.q[i >> 2];
+        const uint32_t w = (i & 3) == 0 ? q4.x : (i & 3) == 1 ? q4.y : (i & 3) == 2 ? q4.z : q4.w;
+        if constexpr (f32_tab(M)) {
+            const uint32_t ev = (w << 2) & 0x03FC03FCu;  // 4 * index of bytes 0 and 2
+            const uint32_t od = (w >> 6) & 0x03FC03FCu;  // 4 * index of bytes 1 and 3
+            v[0] = lds_f(add_half<0>(tb, ev));
+            v[1] = lds_f(add_half<0>(tb, od));
+            v[2] = lds_f(add_half<1>(tb, ev));
+            v[3] = lds_f(add_half<1>(tb, od));
+        } else {
             const uint32_t ev = (w << 1) & 0x01FE01FEu;  // 2 * index of bytes 0 and 2
             const uint32_t od = (w >> 7) & 0x01FE01FEu;  // 2 * index of bytes 1 and 3
-            const float v0 = lds_h(add_half<0>(tb, ev)), v1 = lds_h(add_half<0>(tb, od));
-            const float v2 = lds_h(add_half<1>(tb, ev)), v3 = lds_h(add_half<1>(tb, od));
+            v[0] = lds_h(add_half<0>(tb, ev));
+            v[1] = lds_h(add_half<0>(tb, od));
+            v[2] = lds_h(add_half<1>(tb, ev));
+            v[3] = lds_h(add_half<1>(tb, od));
+        }
+    }
+
+    // The 4 weights of dword i and the activations of every batch row for them.
+    template <int M>
+    __device__ __forceinline__ void fetch(const Codes &c, const float *xu, int i, float (&v)[4], float4 (&xv)[M]) const {
+        lookup<M>(c, i, v);
 #pragma unroll
-            for (int m = 0; m < M; m++) {
-                const float4 xv = *(const float4 *)(xu + m * stream::XBUF + 4 * i);
-                float t = s[m];
-                t = fmaf(v0, xv.x, t);
-                t = fmaf(v1, xv.y, t);
-                t = fmaf(v2, xv.z, t);
-                s[m] = fmaf(v3, xv.w, t);
+        for (int m = 0; m < M; m++) xv[m] = *(const float4 *)(xu + m * stream::XBUF + 4 * i);
+    }
+
+    template <int M>
+    __device__ __forceinline__ static void fma4(const float (&v)[4], const float4 (&xv)[M], float (&t)[M]) {
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            float a = t[m];
+            a = fmaf(v[0], xv[m].x, a);
+            a = fmaf(v[1], xv[m].y, a);
+            a = fmaf(v[2], xv[m].z, a);
+            t[m] = fmaf(v[3], xv[m].w, a);
+        }
+    }
+
+    // Pins the sums here: without it the FMAs sink to the end of the unit and every
+    // looked-up weight and activation of the unit stays live.
+    template <int M>
+    __device__ __forceinline__ static void pin(float (&t)[M]) {
+#pragma unroll
+        for (int m = 0; m < M; m++) asm volatile("" : "+v"(t[m]));
+    }
+
+    // fp16 path: straight-line code, left to the scheduler, each batch row's activations
+    // read next to its FMAs (the fp16 weight is converted inside v_fma_mix_f32).  fp32
+    // path: the reads of dword i + 1 are issued before the FMAs of dword i and nothing
+    // else is hoisted (left alone, the scheduler hoisted every activation read of the
+    // unit: 256 VGPRs at batch 4, spills at batch 8), two partial sums per batch row.
+    template <int M>
+    __device__ __forceinline__ void dot(const Codes &c, const float *xu, float (&s)[M]) const {
+        float v[2][4];
+        float4 xv[2][M];
+        if constexpr (!f32_tab(M)) {
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                lookup<M>(c, i, v[0]);
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    const float4 x4 = *(const float4 *)(xu + m * stream::XBUF + 4 * i);
+                    float a = s[m];
+                    a = fmaf(v[0][0], x4.x, a);
+                    a = fmaf(v[0][1], x4.y, a);
+                    a = fmaf(v[0][2], x4.z, a);
+                    s[m] = fmaf(v[0][3], x4.w, a);
+                }
             }
+        } else {
+            float t[2][M];
+#pragma unroll
+            for (int m = 0; m < M; m++) t[0][m] = s[m], t[1][m] = 0.f;
+            fetch<M>(c, xu, 0, v[0], xv[0]);
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                fetch<M>(c, xu, i + 1, v[1], xv[1]);
+                __builtin_amdgcn_sched_barrier(0);
+                fma4<M>(v[0], xv[0], t[0]);
+                pin<M>(t[0]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (i + 2 < 16) fetch<M>(c, xu, i + 2, v[0], xv[0]);
+                __builtin_amdgcn_sched_barrier(0);
+                fma4<M>(v[1], xv[1], t[1]);
+                pin<M>(t[1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int m = 0; m < M; m++) s[m] = t[0][m] + t[1][m];
         }
     }
 };
 
-// LDS layout: the activation buffers (xfloats floats), then one 512-byte codebook per wave.
+constexpr int tab_bytes(int m) { return f32_tab(m) ? 1024 : 512; }
+
+// LDS layout: the activation buffers (xfloats floats), then one codebook slice per wave:
+// 512 B of fp16 (an fp32 slice would cost batch 1 a workgroup per CU) or 1 KB of fp32.
 template <int M, int XT>
 __global__ void __launch_bounds__(WG) cb8_stream_kernel(const uint8_t *__restrict__ idx,
                                                         const uint16_t *__restrict__ cb,
@@ -87,12 +177,17 @@ __global__ void __launch_bounds__(WG) cb8_stream_kernel(const uint8_t *__restric
     extern __shared__ float4 lds4[];
     float *sx = (float *)lds4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint16_t *tab = (uint16_t *)(sx + xfloats) + wave * 256;
+    constexpr int TB = tab_bytes(M);
+    char *tab = (char *)(sx + xfloats) + wave * TB;
     const int row = blockIdx.x * WAVES + wave;
     const int rowc = row < n ? row : n - 1;
 
     const u32x2 e = __builtin_nontemporal_load((const u32x2 *)(cb + (int64_t)rowc * 256 + 4 * lane));
-    *(uint2 *)(tab + 4 * lane) = make_uint2(e.x, e.y);  // visible after the walk's first barrier
+    // visible after the walk's first barrier
+    if constexpr (TB == 1024)
+        *(float4 *)(tab + 16 * lane) = make_float4(lo_h(e.x), hi_h(e.x), lo_h(e.y), hi_h(e.y));
+    else
+        *(uint2 *)(tab + 8 * lane) = make_uint2(e.x, e.y);
 
     Cb8Policy pol{idx + (int64_t)rowc * k, (uint32_t)(uintptr_t)tab};
     float acc[M];
@@ -106,7 +201,7 @@ __global__ void __launch_bounds__(WG) cb8_stream_kernel(const uint8_t *__restric
     }
 }
 
-size_t lds_of(int m, int64_t k) { return stream::x_lds_bytes(m, k) + (size_t)WAVES * 512; }
+size_t lds_of(int m, int64_t k) { return stream::x_lds_bytes(m, k) + (size_t)WAVES * tab_bytes(m); }
 
 template <int M, int XT>
 void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
@@ -137,7 +232,8 @@ const char *launch_gemv_cb8(const qmv_weights *w, int m, const void *x, int xt, 
     if (w->n > INT32_MAX || w->k > INT32_MAX / 8 || w->k % 64) return nullptr;
     if ((int64_t)lds_of(m, w->k) > device_info().lds_per_block) return nullptr;
     const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, w, x, y, s) : dispatch_m<1>(m, w, x, y, s);
-    return ok ? "cb8.stream.lds-table.fma-mix" : nullptr;
+    if (!ok) return nullptr;
+    return f32_tab(m) ? "cb8.stream.lds-f32-table.fmac" : "cb8.stream.lds-table.fma-mix";
 }
 
 }  // namespace qmv

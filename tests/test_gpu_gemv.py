@@ -478,9 +478,11 @@ def test_cb8_small_full_parity(qmv, n, k, xt):
 
 
 @pytest.mark.parametrize("m,xt,k", [(2, synth.DT_BF16, 2048), (3, synth.DT_F32, 7168), (4, synth.DT_BF16, 12288),
-                                    (5, synth.DT_F32, 4160), (8, synth.DT_BF16, 7168)])
+                                    (5, synth.DT_F32, 4160), (8, synth.DT_BF16, 7168), (6, synth.DT_F32, 16384 + 64),
+                                    (7, synth.DT_BF16, 64), (4, synth.DT_F32, 4096), (3, synth.DT_BF16, 4160)])
 def test_cb8_batched(qmv, m, xt, k):
-    run_case(qmv, synth.FMT_CB8, 29, k, m, xt, seed=m + 17, expect_path="cb8.stream.lds-table.fma-mix")
+    path = "cb8.stream.lds-f32-table.fmac" if m == 3 or m >= 5 else "cb8.stream.lds-table.fma-mix"
+    run_case(qmv, synth.FMT_CB8, 29, k, m, xt, seed=m + 17, expect_path=path)
 
 
 @pytest.mark.parametrize("n,k", [(2048, 7168), (7168, 2048), (129280, 7168)])
