@@ -89,6 +89,66 @@ QMV_DEV float unit_dot(const Unit &w, int u, const float *xu) {
     return h2f(w.d) * r;
 }
 
+// The unit's sum for every batch row at once (batch 3 and up): each dword of codes is
+// centred and converted to exact fp32 once and then applied with v_fmac_f32 to every
+// row (unit_dot per row would repeat the unpack M times and convert inside each
+// v_fma_mix_f32).  r[m] = d * sum over the unit of (q - 32) * sc * x[m], x[m] at
+// xu + m * xstride.
+template <int M>
+QMV_DEV void unit_dot_rows(const Unit &w, int u, const float *xu, int xstride, float (&r)[M]) {
+    const uint32_t A[4] = {w.a.x, w.a.y, w.a.z, w.a.w};
+    const uint32_t B[4] = {w.b.x, w.b.y, w.b.z, w.b.w};
+    const uint32_t H[4] = {w.h.x, w.h.y, w.h.z, w.h.w};
+    const qmv_h2 off = {(_Float16)-1056.f, (_Float16)-1056.f};
+    float s[4][M];
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+#pragma unroll
+        for (int m = 0; m < M; m++) s[t][m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        uint32_t q[4];
+        q[0] = and_or(H[i] << 4, 0x30303030u, A[i] & 0x0F0F0F0Fu);
+        q[1] = and_or(H[i] << 2, 0x30303030u, B[i] & 0x0F0F0F0Fu);
+        q[2] = and_or(H[i], 0x30303030u, (A[i] >> 4) & 0x0F0F0F0Fu);
+        q[3] = and_or(H[i] >> 2, 0x30303030u, (B[i] >> 4) & 0x0F0F0F0Fu);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const qmv_h2 e0 = as_h2(and_or(q[t], 0x00FF00FFu, 0x64006400u)) + off;       // bytes 0 and 2
+            const qmv_h2 e1 = as_h2(and_or(q[t] >> 8, 0x00FF00FFu, 0x64006400u)) + off;  // bytes 1 and 3
+            float c0 = (float)e0.x, c1 = (float)e1.x, c2 = (float)e0.y, c3 = (float)e1.y;
+            // converted here, once, rather than folded into a v_fma_mix_f32 per row
+            asm volatile("" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const float4 xv = *(const float4 *)(xu + m * xstride + 16 * t + 4 * i);
+                float a = s[t][m];
+                a = fmaf(c0, xv.x, a);
+                a = fmaf(c1, xv.y, a);
+                a = fmaf(c2, xv.z, a);
+                s[t][m] = fmaf(c3, xv.w, a);
+            }
+            // the sums are formed here: otherwise the FMAs sink to the end of the unit and
+            // every activation read of the unit is hoisted and held (spills from batch 3)
+#pragma unroll
+            for (int m = 0; m < M; m++) asm volatile("" : "+v"(s[t][m]));
+        }
+    }
+    const int h = (u >> 1) & 1, odd = u & 1;
+    const uint32_t lo = h ? w.s16.z : w.s16.x, hi = h ? w.s16.w : w.s16.y;
+    const float sc0 = (float)(int8_t)(lo >> (8 * odd)), sc1 = (float)(int8_t)(lo >> (8 * odd + 16));
+    const float sc2 = (float)(int8_t)(hi >> (8 * odd)), sc3 = (float)(int8_t)(hi >> (8 * odd + 16));
+    const float d = h2f(w.d);
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        float v = sc0 * s[0][m];
+        v = fmaf(sc1, s[1][m], v);
+        v = fmaf(sc2, s[2][m], v);
+        v = fmaf(sc3, s[3][m], v);
+        r[m] = d * v;
+    }
+}
+
 // Lane l of a wave: when G > 1 the wave covers G rows, lane l taking unit l % U of row
 // l / U (U = 64 / G units per row, the whole row in one chunk); when G == 1 it covers one
 // row and K is walked in chunks of 64 units, lane l taking unit l of each chunk.  Per
@@ -97,7 +157,7 @@ QMV_DEV float unit_dot(const Unit &w, int u, const float *xu) {
 // sits around a load (row and unit indices are clamped); activations of chunk row m, unit
 // slot j sit at sx[(m * 64 + j) * US], run t at +16 t.
 template <int M, int XT>
-__global__ void __launch_bounds__(WG) gemv_q6k_kernel(const uint8_t *__restrict__ ql,
+__global__ void __launch_bounds__(WG, M == 4 ? 4 : 2) gemv_q6k_kernel(const uint8_t *__restrict__ ql,
                                                       const uint8_t *__restrict__ qh,
                                                       const int8_t *__restrict__ scp,
                                                       const uint16_t *__restrict__ dp,
@@ -141,10 +201,17 @@ __global__ void __launch_bounds__(WG) gemv_q6k_kernel(const uint8_t *__restrict_
         __syncthreads();
         const int u = c * CUN + ul;
         const int uc = u < nu ? u : nu - 1;
+        if constexpr (M >= 3) {
+            float r[M];
+            unit_dot_rows<M>(use, uc, sx + (uc - c * CUN) * US, CUN * US, r);
 #pragma unroll
-        for (int m = 0; m < M; m++) {
-            const float v = acc[m] + unit_dot(use, uc, sx + (m * CUN + (uc - c * CUN)) * US);
-            acc[m] = u < nu ? v : acc[m];
+            for (int m = 0; m < M; m++) acc[m] = u < nu ? acc[m] + r[m] : acc[m];
+        } else {
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const float v = acc[m] + unit_dot(use, uc, sx + (m * CUN + (uc - c * CUN)) * US);
+                acc[m] = u < nu ? v : acc[m];
+            }
         }
     };
     Unit w0, w1;
@@ -198,7 +265,9 @@ const char *launch_gemv_q6k(const qmv_weights *w, int m, const void *x, int xt, 
     if (nu < 64 && 64 % nu == 0) G = (int)(64 / nu);
     const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, w, x, y, G, s) : dispatch_m<1>(m, w, x, y, G, s);
     if (!ok) return nullptr;
-    return G > 1 ? "q6_K.lds-x.fma-mix.rowgroup" : "q6_K.lds-x.fma-mix";
+    const char *path[2][2] = {{"q6_K.lds-x.fma-mix", "q6_K.lds-x.fma-mix.rowgroup"},
+                              {"q6_K.lds-x.fmac", "q6_K.lds-x.fmac.rowgroup"}};
+    return path[m >= 3][G > 1];
 }
 
 }  // namespace qmv

@@ -173,10 +173,18 @@ def test_q6k_parity_config_256x1024_seed0(qmv):
     print("max |err| / sum|w||x| =", err)
 
 
-@pytest.mark.parametrize("m", [2, 4, 8])
+def q6_path(m, k):
+    # one unit-dot per batch row up to batch 2 (fp16 codes converted inside the FMA), each
+    # code converted once and applied to every row with fp32 FMAs from batch 3 up; rows of
+    # fewer than 64 units that divide 64 go several to a wave
+    base = "q6_K.lds-x.fmac" if m >= 3 else "q6_K.lds-x.fma-mix"
+    return base + ".rowgroup" if k // 64 < 64 and 64 % (k // 64) == 0 else base
+
+
+@pytest.mark.parametrize("m", [2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("xt", [synth.DT_F32, synth.DT_BF16])
 def test_q6k_batched(qmv, m, xt):
-    run_case(qmv, synth.FMT_Q6_K, 70, 2048, m, xt, seed=m + 100)
+    run_case(qmv, synth.FMT_Q6_K, 70, 2048, m, xt, seed=m + 100, expect_path=q6_path(m, 2048))
 
 
 @pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096)])
@@ -187,12 +195,13 @@ def test_q6k_large_sampled(qmv, n, k):
 @pytest.mark.parametrize("n,k,m,xt", [(4, 32768, 1, synth.DT_F32), (33, 20480, 1, synth.DT_F32),
                                       (70, 11008, 2, synth.DT_F32), (70, 11008, 4, synth.DT_BF16),
                                       (41, 11008, 8, synth.DT_F32), (9, 4352, 8, synth.DT_BF16),
-                                      (17, 8192, 3, synth.DT_F32), (3, 256, 8, synth.DT_F32)])
+                                      (17, 8192, 3, synth.DT_F32), (3, 256, 8, synth.DT_F32),
+                                      (29, 4096, 4, synth.DT_F32), (13, 12288 + 256, 6, synth.DT_BF16),
+                                      (8, 1024, 3, synth.DT_BF16), (64, 16384, 7, synth.DT_F32)])
 def test_q6k_k_chunked_batches(qmv, n, k, m, xt):
     # K is walked 4096 activations at a time: one, two (even), three and five (odd) chunks,
     # ragged last chunks (11008 = 2 * 4096 + 2816, 4352 = 4096 + 256), batches up to 8
-    path = "q6_K.lds-x.fma-mix.rowgroup" if k // 64 < 64 and 64 % (k // 64) == 0 else "q6_K.lds-x.fma-mix"
-    run_case(qmv, synth.FMT_Q6_K, n, k, m, xt, seed=n + k + m, expect_path=path)
+    run_case(qmv, synth.FMT_Q6_K, n, k, m, xt, seed=n + k + m, expect_path=q6_path(m, k))
 
 
 def test_q6k_chunked_unit_vector_returns_column_exactly(qmv):
@@ -207,7 +216,7 @@ def test_q6k_chunked_unit_vector_returns_column_exactly(qmv):
         e[r, j] = 1.0
     y = qmv.gemv(W, x_to_device(e, synth.DT_F32))
     torch.cuda.synchronize()
-    assert qmv.last_path() == "q6_K.lds-x.fma-mix"
+    assert qmv.last_path() == q6_path(m, k)
     y = y.cpu().numpy()
     for r, j in enumerate(cols):
         assert np.array_equal(y[r], dense[:, j]), j
