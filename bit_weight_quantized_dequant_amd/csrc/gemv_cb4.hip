@@ -263,13 +263,16 @@ bool dispatch_m(int m, int cpl, const Cb4Args &a, hipStream_t s) {
 // 32-weight index chunk (16 bytes) and four codebook entries (8 bytes; the wave's 64 lanes
 // together hold the step's 16 codebooks), the next step's are loaded while this one is
 // computed (two register sets alternate), and each looked-up weight is used for all M
-// activation rows.  One row per wave.
+// activation rows.  One row per wave.  The wave's codebook slice holds the step's entries
+// expanded to exact fp32 (1 KB), so a lookup is one ds_read_b32 of 4 * index and the
+// products are plain v_fmac_f32 (no conversion per batch row, none of the dependency
+// stalls of back-to-back v_fma_mix_f32).
 constexpr int KCB = 2048;
 constexpr int RXS = 64 * XS;  // floats of one activation row's staged step
 
 struct StepData {
     uint4 q;  // index chunk
-    uint2 t;  // codebook entries 4 lane .. 4 lane + 3 of the step
+    uint2 t;  // codebook entries 4 lane .. 4 lane + 3 of the step (fp16)
 };
 
 // Step c's bytes for this lane, with clamped (in-bounds) indices past the row's end.
@@ -281,18 +284,21 @@ QMV_DEV void load_step(StepData &d, const uint8_t *idx_row, const uint16_t *cb_r
     d.t = make_uint2(v.x, v.y);
 }
 
-// s[m] += sum over one 32-weight chunk of cb[idx] * x[m]; activation row m at xb + m RXS.
+QMV_DEV float lds_f(uint32_t a) { return *(const __attribute__((address_space(3))) float *)(uintptr_t)a; }
+
+// s[m] += sum over one 32-weight chunk of cb[idx] * x[m]; activation row m at xb + m RXS,
+// the chunk's fp32 codebook at LDS byte address tb.
 template <int M>
 QMV_DEV void chunk_dot_m(uint4 q, uint32_t tb, const float *xb, float (&s)[M]) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const uint32_t ev = (w[j] << 1) & 0x1E1E1E1Eu;
-        const uint32_t od = (w[j] >> 3) & 0x1E1E1E1Eu;
-        const float v[8] = {lds_h(add_byte<0>(tb, ev)), lds_h(add_byte<0>(tb, od)),
-                            lds_h(add_byte<1>(tb, ev)), lds_h(add_byte<1>(tb, od)),
-                            lds_h(add_byte<2>(tb, ev)), lds_h(add_byte<2>(tb, od)),
-                            lds_h(add_byte<3>(tb, ev)), lds_h(add_byte<3>(tb, od))};
+        const uint32_t ev = (w[j] << 2) & 0x3C3C3C3Cu;  // 4 * index of weights 0, 2, 4, 6
+        const uint32_t od = (w[j] >> 2) & 0x3C3C3C3Cu;  // 4 * index of weights 1, 3, 5, 7
+        const float v[8] = {lds_f(add_byte<0>(tb, ev)), lds_f(add_byte<0>(tb, od)),
+                            lds_f(add_byte<1>(tb, ev)), lds_f(add_byte<1>(tb, od)),
+                            lds_f(add_byte<2>(tb, ev)), lds_f(add_byte<2>(tb, od)),
+                            lds_f(add_byte<3>(tb, ev)), lds_f(add_byte<3>(tb, od))};
 #pragma unroll
         for (int m = 0; m < M; m++) {
             const float4 x0 = *(const float4 *)(xb + m * RXS + 8 * j);
@@ -307,6 +313,10 @@ QMV_DEV void chunk_dot_m(uint4 q, uint32_t tb, const float *xb, float (&s)[M]) {
             a = fmaf(v[6], x1.z, a);
             s[m] = fmaf(v[7], x1.w, a);
         }
+        // the sums are formed here: otherwise the FMAs can sink to the chunk's end with
+        // every activation read of the chunk held live
+#pragma unroll
+        for (int m = 0; m < M; m++) asm volatile("" : "+v"(s[m]));
     }
 }
 
@@ -321,7 +331,7 @@ __global__ void __launch_bounds__(WG) cb4_chunked_kernel(const uint8_t *__restri
     extern __shared__ float4 lds4[];
     float *sx = (float *)lds4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint16_t *tab = (uint16_t *)(sx + M * RXS) + wave * 256;
+    float *tab = sx + M * RXS + wave * 256;
     const int nchunk = k >> 5, nst = (nchunk + 63) / 64;
     const int row = blockIdx.x * WAVES + wave;
     const int rowc = row < n ? row : n - 1;
@@ -343,7 +353,7 @@ __global__ void __launch_bounds__(WG) cb4_chunked_kernel(const uint8_t *__restri
 #pragma unroll
         for (int m = 0; m < M; m++)
             *(float4 *)(sx + m * RXS + (threadIdx.x >> 3) * XS + (threadIdx.x & 7) * 4) = xv[m];
-        *(uint2 *)(tab + 4 * lane) = use.t;
+        *(float4 *)(tab + 4 * lane) = make_float4(lo_h(use.t.x), hi_h(use.t.x), lo_h(use.t.y), hi_h(use.t.y));
         __syncthreads();
         const int ci = c * 64 + lane;
         const int lc = ci < nchunk ? lane : nchunk - 1 - c * 64;
@@ -371,7 +381,7 @@ __global__ void __launch_bounds__(WG) cb4_chunked_kernel(const uint8_t *__restri
     }
 }
 
-constexpr size_t chunked_lds(int m) { return (size_t)m * RXS * 4 + (size_t)WAVES * 256 * 2; }
+constexpr size_t chunked_lds(int m) { return (size_t)m * RXS * 4 + (size_t)WAVES * 256 * 4; }
 
 template <int M, int XT>
 void launch_chunked(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
@@ -406,10 +416,17 @@ const char *launch_gemv_cb4(const qmv_weights *w, int m, const void *x, int xt, 
     const int64_t k = w->k, nchunk = k / 32;
     const int cpl = (int)((nchunk + 63) / 64);
     if (w->n > INT32_MAX || k > INT32_MAX / 8) return nullptr;
-    if (cpl > 8 || (int64_t)m * k > 16384 || (int64_t)lds_need(m, k, 1) > device_info().lds_per_block) {
+    // From batch 3 up the K-chunked kernel also where the one-shot kernel would fit: at
+    // 7168x2048 it measured 8.7 / 9.6 / 13.7 us at batch 3 / 4 / 8 against 10.2 / 12.9 /
+    // 22.7 (the one-shot kernel redoes each lookup per batch row); batch 2 is even and
+    // batch 1 is faster one-shot.  Test override "cb4.chunked": the K-chunked kernel at
+    // any size.
+    const bool force_chunked = std::strcmp(forced_path(), "cb4.chunked") == 0;
+    if (force_chunked || m >= 3 || cpl > 8 || (int64_t)m * k > 16384 ||
+        (int64_t)lds_need(m, k, 1) > device_info().lds_per_block) {
         if ((int64_t)chunked_lds(m) > device_info().lds_per_block) return nullptr;
         const bool ok = xt == QMV_F32 ? dispatch_chunked<0>(m, w, x, y, s) : dispatch_chunked<1>(m, w, x, y, s);
-        return ok ? "cb4.lds-table-chunked.fma-mix" : nullptr;
+        return ok ? "cb4.lds-f32-table-chunked.fmac" : nullptr;
     }
     Cb4Args a{(const uint8_t *)w->codes, nullptr, (const uint16_t *)w->codebook, nullptr, 0, 0, x, y, nullptr,
               (int)w->n, (int)k, 1};

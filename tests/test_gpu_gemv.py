@@ -288,9 +288,11 @@ def test_cb4_small_full_parity(qmv, n, k, xt):
     run_case(qmv, synth.FMT_CB4, n, k, 1, xt, seed=n + k, expect_path="cb4.lds-table.fma-mix")
 
 
-@pytest.mark.parametrize("m", [2, 4])
+@pytest.mark.parametrize("m", [2, 3, 4, 8])
 def test_cb4_batched(qmv, m):
-    run_case(qmv, synth.FMT_CB4, 40, 2048, m, synth.DT_BF16, seed=m + 7)
+    # the one-shot kernel up to batch 2, the K-chunked one from batch 3 up
+    path = "cb4.lds-f32-table-chunked.fmac" if m >= 3 else "cb4.lds-table.fma-mix"
+    run_case(qmv, synth.FMT_CB4, 40, 2048, m, synth.DT_BF16, seed=m + 7, expect_path=path)
 
 
 @pytest.mark.parametrize("n,k", [(2048, 7168), (7168, 2048)])
@@ -305,8 +307,18 @@ def test_cb4_expert_shapes_sampled(qmv, n, k):
 def test_cb4_k_chunked_batches(qmv, n, k, m, xt):
     # K walked 2048 weights at a time: even and odd step counts, ragged last steps down to
     # one 128-weight group (16512 = 8 * 2048 + 128, 4224 = 2 * 2048 + 128), batches up to 8
-    path = "cb4.lds-table-chunked.fma-mix" if (m * k > 16384 or k > 16384) else "cb4.lds-table.fma-mix"
+    path = "cb4.lds-f32-table-chunked.fmac" if (m >= 3 or m * k > 16384 or k > 16384) else "cb4.lds-table.fma-mix"
     run_case(qmv, synth.FMT_CB4, n, k, m, xt, seed=n + k + m, expect_path=path)
+
+
+@pytest.mark.parametrize("n,k,m,xt", [(1, 128, 1, synth.DT_F32), (9, 384, 3, synth.DT_BF16), (40, 2048, 4, synth.DT_F32),
+                                      (65, 2176, 6, synth.DT_BF16), (23, 4096, 7, synth.DT_F32),
+                                      (16, 2048, 8, synth.DT_BF16)])
+def test_cb4_chunked_forced_small(qmv, monkeypatch, n, k, m, xt):
+    # the K-chunked kernel where the one-shot kernel would run: one step, ragged single
+    # steps, several batch rows
+    monkeypatch.setenv("QMV_FORCE_PATH", "cb4.chunked")
+    run_case(qmv, synth.FMT_CB4, n, k, m, xt, seed=n + k + m, expect_path="cb4.lds-f32-table-chunked.fmac")
 
 
 def test_cb4_chunked_unit_vector_returns_codebook_entry_exactly(qmv):
@@ -321,7 +333,7 @@ def test_cb4_chunked_unit_vector_returns_codebook_entry_exactly(qmv):
         e[r, j] = 1.0
     y = qmv.gemv(W, x_to_device(e, synth.DT_F32))
     torch.cuda.synchronize()
-    assert qmv.last_path() == "cb4.lds-table-chunked.fma-mix"
+    assert qmv.last_path() == "cb4.lds-f32-table-chunked.fmac"
     y = y.cpu().numpy()
     for r, j in enumerate(cols):
         assert np.array_equal(y[r], dense[:, j]), j
