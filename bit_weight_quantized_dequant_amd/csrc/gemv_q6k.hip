@@ -18,16 +18,15 @@
 // exponent of 1024 and one packed half subtract gives q - 32 exactly; v_fma_mix_f32
 // multiplies it by the fp32 activation exactly.  Per run the kernel applies its
 // sub-scale, and d once per unit.
+#include <cstring>
+
 #include "device_common.h"
 #include "qmv_internal.h"
 
 namespace qmv {
 namespace {
 
-constexpr int WG = 512;
-constexpr int WAVES = WG / 64;
 constexpr int US = 68;    // floats per staged 64-activation unit
-constexpr int CUN = 64;   // units per K chunk (4096 activations)
 
 // sum_j (q_j - 32) x_j over the four bytes (values 0..63) of dword q and x[0..3], exact products.
 QMV_DEV float dot4_c32(uint32_t q, float4 xv, float acc) {
@@ -156,22 +155,23 @@ QMV_DEV void unit_dot_rows(const Unit &w, int u, const float *xu, int xstride, f
 // issued during the previous one), then the LDS writes, a barrier, the dots.  No branch
 // sits around a load (row and unit indices are clamped); activations of chunk row m, unit
 // slot j sit at sx[(m * 64 + j) * US], run t at +16 t.
-template <int M, int XT>
-__global__ void __launch_bounds__(WG, M == 4 ? 4 : 2) gemv_q6k_kernel(const uint8_t *__restrict__ ql,
+template <int M, int XT, int WGT, int CU>
+__global__ void __launch_bounds__(WGT, M == 4 ? 4 : 2) gemv_q6k_kernel(const uint8_t *__restrict__ ql,
                                                       const uint8_t *__restrict__ qh,
                                                       const int8_t *__restrict__ scp,
                                                       const uint16_t *__restrict__ dp,
                                                       const void *__restrict__ x,
                                                       float *__restrict__ y, int n, int k, int G) {
     extern __shared__ float lds[];
-    constexpr int XPT = M * (CUN * 16) / WG;  // 16-byte activation pieces per thread per chunk
+    constexpr int WAVES_ = WGT / 64;
+    constexpr int XPT = M * (CU * 16) / WGT;  // 16-byte activation pieces per thread per chunk
     const int nu = k >> 6;
-    const int nch = G > 1 ? 1 : (nu + CUN - 1) / CUN;
     float *sx = lds;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int U = G > 1 ? 64 / G : CUN;
+    const int U = 64 / G;                     // units of a row per chunk (CU when nch > 1)
+    const int nch = (nu + U - 1) / U;
     const int sub = lane / U, ul = lane % U;
-    const int row = (blockIdx.x * WAVES + wave) * G + sub;
+    const int row = (blockIdx.x * WAVES_ + wave) * G + sub;
     const int rowc = row < n ? row : n - 1;
     float acc[M];
 #pragma unroll
@@ -180,36 +180,36 @@ __global__ void __launch_bounds__(WG, M == 4 ? 4 : 2) gemv_q6k_kernel(const uint
     // the row's last unit past the end), then the LDS writes and the dots with `use`.  Two
     // register sets alternate, so no copy waits on the loads just issued.
     auto step = [&](int c, const Unit &use, Unit &fill) {
-        const int k0 = c * CUN * 64;
-        const int kq = min(CUN * 64, k - k0) >> 2;  // 16-byte pieces of this chunk, per row
+        const int k0 = c * CU * 64;
+        const int kq = min(CU * 64, k - k0) >> 2;  // 16-byte pieces of this chunk, per row
         float4 xv[XPT];
 #pragma unroll
         for (int j = 0; j < XPT; j++) {
-            const int p = threadIdx.x + j * WG, m = p >> 10, e = p & 1023;
+            const int p = threadIdx.x + j * WGT, m = p / (CU * 16), e = p % (CU * 16);
             xv[j] = ld_act4<XT>(x, (int64_t)m * k + k0 + 4 * (e < kq ? e : kq - 1));
         }
-        const int un = (c + 1) * CUN + ul;
+        const int un = (c + 1) * CU + ul;
         load_unit(fill, ql, qh, scp, dp, rowc, k, un < nu ? un : nu - 1);
         __builtin_amdgcn_sched_barrier(0);  // every load is issued before the LDS writes wait
         if (c) __syncthreads();  // the previous chunk's activations are consumed
 #pragma unroll
         for (int j = 0; j < XPT; j++) {
-            const int p = threadIdx.x + j * WG, m = p >> 10, e = 4 * (p & 1023);
+            const int p = threadIdx.x + j * WGT, m = p / (CU * 16), e = 4 * (p % (CU * 16));
             const int slot = 4 * (e >> 8) + 2 * ((e >> 7) & 1) + ((e >> 4) & 1);
-            *(float4 *)(sx + (m * CUN + slot) * US + 16 * ((e >> 5) & 3) + (e & 15)) = xv[j];
+            *(float4 *)(sx + (m * CU + slot) * US + 16 * ((e >> 5) & 3) + (e & 15)) = xv[j];
         }
         __syncthreads();
-        const int u = c * CUN + ul;
+        const int u = c * CU + ul;
         const int uc = u < nu ? u : nu - 1;
         if constexpr (M >= 3) {
             float r[M];
-            unit_dot_rows<M>(use, uc, sx + (uc - c * CUN) * US, CUN * US, r);
+            unit_dot_rows<M>(use, uc, sx + (uc - c * CU) * US, CU * US, r);
 #pragma unroll
             for (int m = 0; m < M; m++) acc[m] = u < nu ? acc[m] + r[m] : acc[m];
         } else {
 #pragma unroll
             for (int m = 0; m < M; m++) {
-                const float v = acc[m] + unit_dot(use, uc, sx + (m * CUN + (uc - c * CUN)) * US);
+                const float v = acc[m] + unit_dot(use, uc, sx + (m * CU + (uc - c * CU)) * US);
                 acc[m] = u < nu ? v : acc[m];
             }
         }
@@ -227,29 +227,43 @@ __global__ void __launch_bounds__(WG, M == 4 ? 4 : 2) gemv_q6k_kernel(const uint
     }
 }
 
-constexpr size_t lds_bytes(int m) { return (size_t)m * CUN * US * sizeof(float); }
+constexpr size_t lds_bytes(int m, int cu) { return (size_t)m * cu * US * sizeof(float); }
 
-template <int M, int XT>
+// WGT threads per workgroup, CU units staged per chunk: <512, 64> (one row per wave, or G
+// short rows), or <256, 32> (two rows per wave, each lane one unit of a 32-unit chunk):
+// from batch 5 up the staged activations of a 64-unit chunk (m x 17 KB) leave room for one
+// 512-thread workgroup per CU, which then waits on its loads with nothing to overlap; the
+// half chunk lets two 256-thread workgroups share a CU.
+template <int M, int XT, int WGT, int CU>
 void launch(const qmv_weights *w, const void *x, float *y, int G, hipStream_t s) {
     const int n = (int)w->n, k = (int)w->k;
-    const int rows_per_wg = WAVES * G;
+    const int rows_per_wg = WGT / 64 * G;
     const int grid = (n + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((gemv_q6k_kernel<M, XT>), dim3(grid), dim3(WG), lds_bytes(M), s,
+    hipLaunchKernelGGL((gemv_q6k_kernel<M, XT, WGT, CU>), dim3(grid), dim3(WGT), lds_bytes(M, CU), s,
                        (const uint8_t *)w->codes, (const uint8_t *)w->codes_hi, (const int8_t *)w->scales,
                        (const uint16_t *)w->super, x, y, n, k, G);
 }
 
 template <int XT>
-bool dispatch_m(int m, const qmv_weights *w, const void *x, float *y, int G, hipStream_t s) {
+bool dispatch_m(int m, bool half, const qmv_weights *w, const void *x, float *y, int G, hipStream_t s) {
+    if (half) {
+        switch (m) {
+        case 5: launch<5, XT, 256, 32>(w, x, y, G, s); return true;
+        case 6: launch<6, XT, 256, 32>(w, x, y, G, s); return true;
+        case 7: launch<7, XT, 256, 32>(w, x, y, G, s); return true;
+        case 8: launch<8, XT, 256, 32>(w, x, y, G, s); return true;
+        }
+        return false;
+    }
     switch (m) {
-    case 1: launch<1, XT>(w, x, y, G, s); return true;
-    case 2: launch<2, XT>(w, x, y, G, s); return true;
-    case 3: launch<3, XT>(w, x, y, G, s); return true;
-    case 4: launch<4, XT>(w, x, y, G, s); return true;
-    case 5: launch<5, XT>(w, x, y, G, s); return true;
-    case 6: launch<6, XT>(w, x, y, G, s); return true;
-    case 7: launch<7, XT>(w, x, y, G, s); return true;
-    case 8: launch<8, XT>(w, x, y, G, s); return true;
+    case 1: launch<1, XT, 512, 64>(w, x, y, G, s); return true;
+    case 2: launch<2, XT, 512, 64>(w, x, y, G, s); return true;
+    case 3: launch<3, XT, 512, 64>(w, x, y, G, s); return true;
+    case 4: launch<4, XT, 512, 64>(w, x, y, G, s); return true;
+    case 5: launch<5, XT, 512, 64>(w, x, y, G, s); return true;
+    case 6: launch<6, XT, 512, 64>(w, x, y, G, s); return true;
+    case 7: launch<7, XT, 512, 64>(w, x, y, G, s); return true;
+    case 8: launch<8, XT, 512, 64>(w, x, y, G, s); return true;
     }
     return false;
 }
@@ -259,12 +273,18 @@ bool dispatch_m(int m, const qmv_weights *w, const void *x, float *y, int G, hip
 const char *launch_gemv_q6k(const qmv_weights *w, int m, const void *x, int xt, float *y, hipStream_t s) {
     const int64_t n = w->n, k = w->k, nu = k / 64;
     if (n > INT32_MAX || k > INT32_MAX / 8) return nullptr;
-    if ((int64_t)lds_bytes(m) > device_info().lds_per_block) return nullptr;
-    // G rows at a time when a row has fewer than 64 units and 64 is a multiple of them.
+    // batch 5 and up: 256-thread workgroups over 32-unit chunks (test override "q6_K.wg512":
+    // the 512-thread form)
+    const bool half = m >= 5 && std::strcmp(forced_path(), "q6_K.wg512") != 0;
+    if ((int64_t)lds_bytes(m, half ? 32 : 64) > device_info().lds_per_block) return nullptr;
+    // G rows at a time when a row has fewer than 64 units and 64 is a multiple of them; at
+    // least two (32 units of a row per chunk) in the 256-thread form.
     int G = 1;
     if (nu < 64 && 64 % nu == 0) G = (int)(64 / nu);
-    const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, w, x, y, G, s) : dispatch_m<1>(m, w, x, y, G, s);
+    if (half && G < 2) G = 2;
+    const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, half, w, x, y, G, s) : dispatch_m<1>(m, half, w, x, y, G, s);
     if (!ok) return nullptr;
+    if (half) return "q6_K.lds-x.fmac.wg256";
     const char *path[2][2] = {{"q6_K.lds-x.fma-mix", "q6_K.lds-x.fma-mix.rowgroup"},
                               {"q6_K.lds-x.fmac", "q6_K.lds-x.fmac.rowgroup"}};
     return path[m >= 3][G > 1];

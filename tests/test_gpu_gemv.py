@@ -176,7 +176,10 @@ def test_q6k_parity_config_256x1024_seed0(qmv):
 def q6_path(m, k):
     # one unit-dot per batch row up to batch 2 (fp16 codes converted inside the FMA), each
     # code converted once and applied to every row with fp32 FMAs from batch 3 up; rows of
-    # fewer than 64 units that divide 64 go several to a wave
+    # fewer than 64 units that divide 64 go several to a wave; from batch 5 up 256-thread
+    # workgroups over half chunks (two rows per wave)
+    if m >= 5:
+        return "q6_K.lds-x.fmac.wg256"
     base = "q6_K.lds-x.fmac" if m >= 3 else "q6_K.lds-x.fma-mix"
     return base + ".rowgroup" if k // 64 < 64 and 64 % (k // 64) == 0 else base
 
@@ -202,6 +205,21 @@ def test_q6k_k_chunked_batches(qmv, n, k, m, xt):
     # K is walked 4096 activations at a time: one, two (even), three and five (odd) chunks,
     # ragged last chunks (11008 = 2 * 4096 + 2816, 4352 = 4096 + 256), batches up to 8
     run_case(qmv, synth.FMT_Q6_K, n, k, m, xt, seed=n + k + m, expect_path=q6_path(m, k))
+
+
+@pytest.mark.parametrize("n,k,m,xt", [(41, 11008, 8, synth.DT_F32), (9, 4352, 5, synth.DT_BF16), (3, 256, 6, synth.DT_F32),
+                                      (70, 3072, 7, synth.DT_F32), (13, 2048, 8, synth.DT_BF16)])
+@pytest.mark.parametrize("path", ["default", "q6_K.wg512"])
+def test_q6k_batch5_forms(qmv, monkeypatch, n, k, m, xt, path):
+    # batches 5-8 in both workgroup forms: 32-unit chunks (ragged: 3072 = 48 units, 4352 =
+    # 68), rows of one and four units per chunk, and the 512-thread form on request
+    if path != "default":
+        monkeypatch.setenv("QMV_FORCE_PATH", path)
+        k64 = k // 64
+        expect = "q6_K.lds-x.fmac.rowgroup" if k64 < 64 and 64 % k64 == 0 else "q6_K.lds-x.fmac"
+    else:
+        expect = q6_path(m, k)
+    run_case(qmv, synth.FMT_Q6_K, n, k, m, xt, seed=n + k + m, expect_path=expect)
 
 
 def test_q6k_chunked_unit_vector_returns_column_exactly(qmv):
