@@ -20,6 +20,8 @@
 //     sum); on the fp32 path the reads of the next dword are in flight during the FMAs
 //     of this one, and each row keeps two partial sums (even and odd dwords);
 //   * the 64 lane partials are summed with DPP.
+#include <cstring>
+
 #include "device_common.h"
 #include "gemv_stream.h"
 #include "qmv_internal.h"
@@ -27,8 +29,6 @@
 namespace qmv {
 namespace {
 
-using stream::WG;
-using stream::WAVES;
 using stream::XU;
 
 // base + 16-bit half H of v, in one v_add_u32 with an SDWA word select on the second source.
@@ -54,8 +54,10 @@ QMV_DEV float lds_f(uint32_t a) { return *(const __attribute__((address_space(3)
 // 7168x2048).
 constexpr bool f32_tab(int m) { return m == 3 || m >= 5; }
 
+template <int L>
 struct Cb8Policy {
-    static constexpr int R = 1;  // rows per wave
+    static constexpr int R = 1;  // rows per lane group
+    static constexpr int XB = stream::xbuf_of(L);  // floats between batch rows' staged steps
     struct Codes {
         uint4 q[4];  // index bytes 0..63 of the unit
     };
@@ -95,7 +97,7 @@ struct Cb8Policy {
     __device__ __forceinline__ void fetch(const Codes &c, const float *xu, int i, float (&v)[4], float4 (&xv)[M]) const {
         lookup<M>(c, i, v);
 #pragma unroll
-        for (int m = 0; m < M; m++) xv[m] = *(const float4 *)(xu + m * stream::XBUF + 4 * i);
+        for (int m = 0; m < M; m++) xv[m] = *(const float4 *)(xu + m * XB + 4 * i);
     }
 
     template <int M>
@@ -133,7 +135,7 @@ struct Cb8Policy {
                 lookup<M>(c, i, v[0]);
 #pragma unroll
                 for (int m = 0; m < M; m++) {
-                    const float4 x4 = *(const float4 *)(xu + m * stream::XBUF + 4 * i);
+                    const float4 x4 = *(const float4 *)(xu + m * XB + 4 * i);
                     float a = s[m];
                     a = fmaf(v[0][0], x4.x, a);
                     a = fmaf(v[0][1], x4.y, a);
@@ -167,61 +169,87 @@ struct Cb8Policy {
 
 constexpr int tab_bytes(int m) { return f32_tab(m) ? 1024 : 512; }
 
-// LDS layout: the activation buffers (xfloats floats), then one codebook slice per wave:
+// L lanes per row: 64 (one row per wave, 512-thread workgroups, 4096-weight steps) or 32
+// (two rows per wave, 256-thread workgroups, 2048-weight steps).  From batch 5 up the
+// activations of a 4096-weight step (m x 17 KB, one buffer) leave room for one 512-thread
+// workgroup per CU, which then waits on its loads with nothing to overlap; the half step
+// lets two workgroups share a CU.
+// LDS layout: the activation buffers (xfloats floats), then one codebook slice per row:
 // 512 B of fp16 (an fp32 slice would cost batch 1 a workgroup per CU) or 1 KB of fp32.
-template <int M, int XT>
-__global__ void __launch_bounds__(WG) cb8_stream_kernel(const uint8_t *__restrict__ idx,
-                                                        const uint16_t *__restrict__ cb,
-                                                        const void *__restrict__ x, float *__restrict__ y,
-                                                        int n, int k, int xfloats) {
+template <int M, int XT, int L>
+__global__ void __launch_bounds__(stream::wg_of(L)) cb8_stream_kernel(const uint8_t *__restrict__ idx,
+                                                                      const uint16_t *__restrict__ cb,
+                                                                      const void *__restrict__ x,
+                                                                      float *__restrict__ y, int n, int k,
+                                                                      int xfloats) {
     extern __shared__ float4 lds4[];
+    constexpr int G = 64 / L;  // rows per wave
+    constexpr int WAVES_ = stream::wg_of(L) / 64;
+    constexpr int TB = tab_bytes(M);
     float *sx = (float *)lds4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    constexpr int TB = tab_bytes(M);
-    char *tab = (char *)(sx + xfloats) + wave * TB;
-    const int row = blockIdx.x * WAVES + wave;
+    const int sub = lane / L, ul = lane % L;
+    char *tab = (char *)(sx + xfloats) + (wave * G + sub) * TB;
+    const int row = (blockIdx.x * WAVES_ + wave) * G + sub;
     const int rowc = row < n ? row : n - 1;
 
-    const u32x2 e = __builtin_nontemporal_load((const u32x2 *)(cb + (int64_t)rowc * 256 + 4 * lane));
-    // visible after the walk's first barrier
-    if constexpr (TB == 1024)
-        *(float4 *)(tab + 16 * lane) = make_float4(lo_h(e.x), hi_h(e.x), lo_h(e.y), hi_h(e.y));
-    else
-        *(uint2 *)(tab + 8 * lane) = make_uint2(e.x, e.y);
+    // the row's 256 entries over its L lanes; visible after the walk's first barrier
+    const uint16_t *cbr = cb + (int64_t)rowc * 256;
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        const int j = 4 * (ul + L * h);  // first of this lane's four entries
+        const u32x2 e = __builtin_nontemporal_load((const u32x2 *)(cbr + j));
+        if constexpr (TB == 1024)
+            *(float4 *)(tab + 4 * j) = make_float4(lo_h(e.x), hi_h(e.x), lo_h(e.y), hi_h(e.y));
+        else
+            *(uint2 *)(tab + 2 * j) = make_uint2(e.x, e.y);
+    }
 
-    Cb8Policy pol{idx + (int64_t)rowc * k, (uint32_t)(uintptr_t)tab};
+    Cb8Policy<L> pol{idx + (int64_t)rowc * k, (uint32_t)(uintptr_t)tab};
     float acc[M];
 #pragma unroll
     for (int m = 0; m < M; m++) acc[m] = 0.f;
-    stream::walk_row<Cb8Policy, M, XT>(pol, x, k, sx, acc);
+    stream::walk_row<Cb8Policy<L>, M, XT, L>(pol, x, k, sx, acc);
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        const float t = wave_sum(acc[m]);
-        if (lane == 0 && row < n) y[(int64_t)m * n + row] = t;
+        const float t = L == 64 ? wave_sum(acc[m]) : group_sum(acc[m], L);
+        if (ul == 0 && row < n) y[(int64_t)m * n + row] = t;
     }
 }
 
-size_t lds_of(int m, int64_t k) { return stream::x_lds_bytes(m, k) + (size_t)WAVES * tab_bytes(m); }
+size_t lds_of(int m, int64_t k, int l) {
+    return stream::x_lds_bytes(m, k, l) + (size_t)(stream::wg_of(l) / l) * tab_bytes(m);
+}
 
-template <int M, int XT>
+template <int M, int XT, int L>
 void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     const int n = (int)w->n, k = (int)w->k;
-    hipLaunchKernelGGL((cb8_stream_kernel<M, XT>), dim3((n + WAVES - 1) / WAVES), dim3(WG), lds_of(M, k), s,
-                       (const uint8_t *)w->codes, (const uint16_t *)w->codebook, x, y, n, k,
-                       (int)(stream::x_lds_bytes(M, k) / 4));
+    constexpr int ROWS = stream::wg_of(L) / L;  // rows per workgroup: 8
+    hipLaunchKernelGGL((cb8_stream_kernel<M, XT, L>), dim3((n + ROWS - 1) / ROWS), dim3(stream::wg_of(L)),
+                       lds_of(M, k, L), s, (const uint8_t *)w->codes, (const uint16_t *)w->codebook, x, y, n, k,
+                       (int)(stream::x_lds_bytes(M, k, L) / 4));
 }
 
 template <int XT>
-bool dispatch_m(int m, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
+bool dispatch_m(int m, bool half, const qmv_weights *w, const void *x, float *y, hipStream_t s) {
+    if (half) {
+        switch (m) {
+        case 5: launch<5, XT, 32>(w, x, y, s); return true;
+        case 6: launch<6, XT, 32>(w, x, y, s); return true;
+        case 7: launch<7, XT, 32>(w, x, y, s); return true;
+        case 8: launch<8, XT, 32>(w, x, y, s); return true;
+        }
+        return false;
+    }
     switch (m) {
-    case 1: launch<1, XT>(w, x, y, s); return true;
-    case 2: launch<2, XT>(w, x, y, s); return true;
-    case 3: launch<3, XT>(w, x, y, s); return true;
-    case 4: launch<4, XT>(w, x, y, s); return true;
-    case 5: launch<5, XT>(w, x, y, s); return true;
-    case 6: launch<6, XT>(w, x, y, s); return true;
-    case 7: launch<7, XT>(w, x, y, s); return true;
-    case 8: launch<8, XT>(w, x, y, s); return true;
+    case 1: launch<1, XT, 64>(w, x, y, s); return true;
+    case 2: launch<2, XT, 64>(w, x, y, s); return true;
+    case 3: launch<3, XT, 64>(w, x, y, s); return true;
+    case 4: launch<4, XT, 64>(w, x, y, s); return true;
+    case 5: launch<5, XT, 64>(w, x, y, s); return true;
+    case 6: launch<6, XT, 64>(w, x, y, s); return true;
+    case 7: launch<7, XT, 64>(w, x, y, s); return true;
+    case 8: launch<8, XT, 64>(w, x, y, s); return true;
     }
     return false;
 }
@@ -230,9 +258,17 @@ bool dispatch_m(int m, const qmv_weights *w, const void *x, float *y, hipStream_
 
 const char *launch_gemv_cb8(const qmv_weights *w, int m, const void *x, int xt, float *y, hipStream_t s) {
     if (w->n > INT32_MAX || w->k > INT32_MAX / 8 || w->k % 64) return nullptr;
-    if ((int64_t)lds_of(m, w->k) > device_info().lds_per_block) return nullptr;
-    const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, w, x, y, s) : dispatch_m<1>(m, w, x, y, s);
+    // Batch 5 and up on matrices of at least 16 rows per CU (two 8-row workgroups per CU):
+    // the half-step form.  With fewer rows it would leave one 4-wave workgroup per CU
+    // (2048x7168 at batch 5: 11.6 -> 13.2 us; 7168x2048: 21.1 -> 11.2 us).  Test overrides
+    // "cb8.half" and "cb8.wg512" force either form from batch 5 up.
+    const char *fp = forced_path();
+    const bool half = m >= 5 && std::strcmp(fp, "cb8.wg512") != 0 &&
+                      (w->n >= 16 * (int64_t)device_info().num_cus || std::strcmp(fp, "cb8.half") == 0);
+    if ((int64_t)lds_of(m, w->k, half ? 32 : 64) > device_info().lds_per_block) return nullptr;
+    const bool ok = xt == QMV_F32 ? dispatch_m<0>(m, half, w, x, y, s) : dispatch_m<1>(m, half, w, x, y, s);
     if (!ok) return nullptr;
+    if (half) return "cb8.stream.lds-f32-table.fmac.half-step";
     return f32_tab(m) ? "cb8.stream.lds-f32-table.fmac" : "cb8.stream.lds-table.fma-mix";
 }
 

@@ -39,52 +39,60 @@ constexpr int KC = 4096;
 constexpr int XU = 68;
 constexpr int XBUF = 64 * XU;  // floats of one batch row's staged step
 
+// The half-step form (L = 32 lanes per row, two rows per wave, 256-thread workgroups,
+// 2048-weight steps) stages half as many activations per workgroup; L = 64 is the form
+// described above.
+constexpr int wg_of(int l) { return 8 * l; }
+constexpr int kc_of(int l) { return 64 * l; }
+constexpr int xbuf_of(int l) { return l * XU; }
+
 // LDS floats of the activation buffers for batch m and a row of k weights.
 constexpr int nbuf(int m) { return m <= 4 ? 2 : 1; }
-inline size_t x_lds_bytes(int m, int64_t k) {
-    const int bufs = k > KC ? nbuf(m) : 1;
-    return (size_t)bufs * m * XBUF * sizeof(float);
+inline size_t x_lds_bytes(int m, int64_t k, int l = 64) {
+    const int bufs = k > kc_of(l) ? nbuf(m) : 1;
+    return (size_t)bufs * m * xbuf_of(l) * sizeof(float);
 }
 
 // Thread t loads 16-byte pieces t and t + WG of each batch row's step (a step row is
 // 1024 pieces; pieces past the row's end are clamped to its last piece).
-template <int M, int XT>
+template <int M, int XT, int L = 64>
 QMV_DEV void load_x(float4 (&xv)[2 * M], const void *x, int k, int c) {
-    const int k0 = c * KC;
-    const int kq = min(KC, k - k0) >> 2;
+    const int k0 = c * kc_of(L);
+    const int kq = min(kc_of(L), k - k0) >> 2;
 #pragma unroll
     for (int j = 0; j < 2 * M; j++) {
-        const int m = j >> 1, e = threadIdx.x + (j & 1) * WG;
+        const int m = j >> 1, e = threadIdx.x + (j & 1) * wg_of(L);
         xv[j] = ld_act4<XT>(x, (int64_t)m * k + k0 + 4 * (e < kq ? e : kq - 1));
     }
 }
 
 // Piece e of a step row holds weights 4e .. 4e+3: unit e >> 4, offset 4 (e & 15).
-template <int M>
+template <int M, int L = 64>
 QMV_DEV void store_x(const float4 (&xv)[2 * M], float *buf) {
 #pragma unroll
     for (int j = 0; j < 2 * M; j++) {
-        const int m = j >> 1, e = threadIdx.x + (j & 1) * WG;
-        *(float4 *)(buf + m * XBUF + (e >> 4) * XU + 4 * (e & 15)) = xv[j];
+        const int m = j >> 1, e = threadIdx.x + (j & 1) * wg_of(L);
+        *(float4 *)(buf + m * xbuf_of(L) + (e >> 4) * XU + 4 * (e & 15)) = xv[j];
     }
 }
 
 // Walk the wave's row(s): acc[r * M + m] += sum over row r's k weights of w * x[m].  `sx` holds nbuf(M)
 // activation buffers when k > KC, one otherwise; every thread of the workgroup calls
 // this with the same k (the barriers are workgroup-wide).
-template <class P, int M, int XT>
+template <class P, int M, int XT, int L = 64>
 QMV_DEV void walk_row(const P &pol, const void *x, int k, float *sx, float (&acc)[P::R * M]) {
     constexpr int RM = P::R * M;
     constexpr bool TWO = nbuf(M) == 2;
-    const int lane = threadIdx.x & 63;
-    const int nunits = k >> 6, nst = (nunits + 63) >> 6;
+    constexpr int XB = xbuf_of(L);
+    const int lane = threadIdx.x & (L - 1);  // this lane's unit slot in a step of its row
+    const int nunits = k >> 6, nst = (nunits + L - 1) / L;
     typename P::Codes c0, c1;
     float4 xv[2 * M];
 
-    load_x<M, XT>(xv, x, k, 0);
+    load_x<M, XT, L>(xv, x, k, 0);
     pol.load(c0, lane < nunits ? lane : nunits - 1);
     __builtin_amdgcn_sched_barrier(0);
-    store_x<M>(xv, sx);
+    store_x<M, L>(xv, sx);
     __syncthreads();
 
     // One step; MORE = there is a next step to prefetch.  The choice is made outside the
@@ -93,13 +101,13 @@ QMV_DEV void walk_row(const P &pol, const void *x, int k, float *sx, float (&acc
     auto step = [&](auto more_tag, int c, const typename P::Codes &use, typename P::Codes &fill) {
         constexpr bool MORE = decltype(more_tag)::value;
         if (MORE) {
-            load_x<M, XT>(xv, x, k, c + 1);
-            const int un = (c + 1) * 64 + lane;
+            load_x<M, XT, L>(xv, x, k, c + 1);
+            const int un = (c + 1) * L + lane;
             pol.load(fill, un < nunits ? un : nunits - 1);
         }
-        const float *buf = sx + (TWO ? (c & 1) * M * XBUF : 0);
-        const int u = c * 64 + lane;
-        const int uc = u < nunits ? lane : nunits - 1 - c * 64;
+        const float *buf = sx + (TWO ? (c & 1) * M * XB : 0);
+        const int u = c * L + lane;
+        const int uc = u < nunits ? lane : nunits - 1 - c * L;
         float s[RM];
 #pragma unroll
         for (int m = 0; m < RM; m++) s[m] = 0.f;
@@ -111,7 +119,7 @@ QMV_DEV void walk_row(const P &pol, const void *x, int k, float *sx, float (&acc
         for (int m = 0; m < RM; m++) acc[m] = u < nunits ? acc[m] + s[m] : acc[m];
         if (MORE) {
             if (!TWO) __syncthreads();  // every wave is done with the only buffer
-            store_x<M>(xv, sx + (TWO ? ((c + 1) & 1) * M * XBUF : 0));
+            store_x<M, L>(xv, sx + (TWO ? ((c + 1) & 1) * M * XB : 0));
             __syncthreads();
         }
     };

@@ -520,8 +520,33 @@ def test_cb8_small_full_parity(qmv, n, k, xt):
                                     (5, synth.DT_F32, 4160), (8, synth.DT_BF16, 7168), (6, synth.DT_F32, 16384 + 64),
                                     (7, synth.DT_BF16, 64), (4, synth.DT_F32, 4096), (3, synth.DT_BF16, 4160)])
 def test_cb8_batched(qmv, m, xt, k):
-    path = "cb8.stream.lds-f32-table.fmac" if m == 3 or m >= 5 else "cb8.stream.lds-table.fma-mix"
-    run_case(qmv, synth.FMT_CB8, 29, k, m, xt, seed=m + 17, expect_path=path)
+    run_case(qmv, synth.FMT_CB8, 29, k, m, xt, seed=m + 17, expect_path=cb8_path(m, 29))
+
+
+def cb8_path(m, n=0, force=None):
+    # fp16 codebook slice at batch 1, 2 and 4; fp32 slice at 3 and from 5 up, where the
+    # half-step form (two rows per wave, 2048-weight steps) runs on matrices of at least 16
+    # rows per CU, or when forced
+    import torch
+    if m >= 5:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        half = force == "cb8.half" or (force is None and n >= 16 * cus)
+        return "cb8.stream.lds-f32-table.fmac.half-step" if half else "cb8.stream.lds-f32-table.fmac"
+    return "cb8.stream.lds-f32-table.fmac" if m == 3 else "cb8.stream.lds-table.fma-mix"
+
+
+@pytest.mark.parametrize("n,k,m,xt", [(29, 7168, 8, synth.DT_BF16), (17, 2048 + 64, 5, synth.DT_F32),
+                                      (3, 64, 6, synth.DT_BF16), (40, 16384 + 64, 7, synth.DT_F32),
+                                      (2048, 7168, 8, synth.DT_BF16), (7168, 2048, 6, synth.DT_BF16)])
+@pytest.mark.parametrize("path", ["default", "cb8.half", "cb8.wg512"])
+def test_cb8_batch5_forms(qmv, monkeypatch, n, k, m, xt, path):
+    # batches 5-8 in both forms: ragged half steps (2112 = 2048 + 64), a single unit, odd
+    # row counts (a wave's second row past n), full-size shapes on sampled rows
+    force = None if path == "default" else path
+    if force:
+        monkeypatch.setenv("QMV_FORCE_PATH", force)
+    rows = sample_rows(n) if n > 512 else None
+    run_case(qmv, synth.FMT_CB8, n, k, m, xt, seed=n + k + m, rows=rows, expect_path=cb8_path(m, n, force))
 
 
 @pytest.mark.parametrize("n,k", [(2048, 7168), (7168, 2048), (129280, 7168)])
