@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--only-primary", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--secondary", default="q6_K_gemv,q6_K_decode,q4_0_batch,q4_0_q8,batch4_other,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm",
+    ap.add_argument("--secondary", default="q6_K_gemv,q6_K_decode,q4_0_batch,q4_0_q8,batch4_other,batch8_other,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm",
                     help="comma-separated secondary workloads to run")
     return ap.parse_args()
 
@@ -475,6 +475,16 @@ def main():
                                                "4-bit codebook GEMV batch 4, 2048x7168 + 7168x2048, bf16 x")
             sec["cb8_gemv_b4"] = gemv_workload(qmv, synth.FMT_CB8, [(2048, 7168), (7168, 2048)], 4, synth.DT_BF16, 50,
                                                "8-bit codebook GEMV batch 4, 2048x7168 + 7168x2048, bf16 x")
+        if "batch8_other" in want:
+            # batch 8 for the formats the q4_0 batch lines do not cover
+            sec["q6_K_gemv_b8"] = gemv_workload(qmv, synth.FMT_Q6_K, [(4096, 4096), (11008, 4096), (4096, 11008)],
+                                                8, synth.DT_F32, 50, "q6_K GEMV batch 8, Llama-7B decode shapes, fp32 x")
+            sec["cb4_gemv_b8"] = gemv_workload(qmv, synth.FMT_CB4, [(2048, 7168), (7168, 2048)], 8, synth.DT_BF16, 50,
+                                               "4-bit codebook GEMV batch 8, 2048x7168 + 7168x2048, bf16 x")
+            sec["cb8_gemv_b8"] = gemv_workload(qmv, synth.FMT_CB8, [(2048, 7168), (7168, 2048)], 8, synth.DT_BF16, 50,
+                                               "8-bit codebook GEMV batch 8, 2048x7168 + 7168x2048, bf16 x")
+            sec["aq2x8_gemv_b8"] = gemv_workload(qmv, synth.FMT_AQ2X8, [(14336, 4096), (4096, 14336)], 8,
+                                                 synth.DT_BF16, 50, "2-bit additive GEMV batch 8, 14336x4096 + 4096x14336, bf16 x")
         if "cb4_moe" in want:
             sec["cb4_moe"] = moe_workload(qmv, 64, "4-bit codebook MoE FFN, batch 1, 256 experts top-8, "
                                                    "gate/up 2048x7168 + down 7168x2048, bf16 x")
