@@ -55,9 +55,10 @@ QMV_DEV float sum_hf(uint32_t a, float f) {
 
 // Table rows of codebook b at LDS byte address tab + b * 4096 + 16 * code.  R rows per wave:
 // lane l owns unit l of each of the R rows, and each activation read serves all of them.
-template <int NC, int RR>
+template <int NC, int RR, int L = 64>
 struct AqPolicy {
-    static constexpr int R = RR;  // rows per wave
+    static constexpr int R = RR;  // rows per lane group
+    static constexpr int XB = stream::xbuf_of(L);  // floats between batch rows' staged steps
     struct Codes {
         uint32_t w[R][2 * NC];  // row r: byte NC * g + b = code b of group g
     };
@@ -114,7 +115,7 @@ struct AqPolicy {
             }
 #pragma unroll
             for (int m = 0; m < M; m++) {
-                const float *xg = xu + m * stream::XBUF + 8 * g;
+                const float *xg = xu + m * XB + 8 * g;
                 const float4 x0 = *(const float4 *)xg, x1 = *(const float4 *)(xg + 4);
 #pragma unroll
                 for (int r = 0; r < R; r++) {
@@ -134,29 +135,35 @@ struct AqPolicy {
     }
 };
 
-// LDS layout: the activation buffers (xfloats floats), then the NC tables.
-template <int NC, int M, int R, int XT>
-__global__ void __launch_bounds__(WG) aq_stream_kernel(const uint8_t *__restrict__ codes,
-                                                       const uint16_t *__restrict__ cbk,
-                                                       const uint16_t *__restrict__ srow,
-                                                       const void *__restrict__ x, float *__restrict__ y,
-                                                       int n, int k, int xfloats) {
+// LDS layout: the activation buffers (xfloats floats), then the NC tables.  L lanes per
+// row group: 64 (one group of R rows per wave, 512-thread workgroups, 4096-weight steps)
+// or 32 (two groups per wave, 256-thread workgroups, 2048-weight steps: half the staged
+// activations, so two workgroups share a CU from batch 5 up).
+template <int NC, int M, int R, int XT, int L = 64>
+__global__ void __launch_bounds__(stream::wg_of(L)) aq_stream_kernel(const uint8_t *__restrict__ codes,
+                                                                     const uint16_t *__restrict__ cbk,
+                                                                     const uint16_t *__restrict__ srow,
+                                                                     const void *__restrict__ x,
+                                                                     float *__restrict__ y, int n, int k,
+                                                                     int xfloats) {
     extern __shared__ float4 lds4[];
+    constexpr int WG_ = stream::wg_of(L), WAVES_ = WG_ / 64, G = 64 / L;
     float *sx = (float *)lds4;
     uint4 *tab = (uint4 *)(sx + xfloats);
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int row0 = (blockIdx.x * WAVES + wave) * R;  // this wave's rows: row0 .. row0 + R - 1
+    const int sub = lane / L, ul = lane % L;
+    const int row0 = ((blockIdx.x * WAVES_ + wave) * G + sub) * R;  // this group's rows: row0 .. row0 + R - 1
 
     // NC * 256 table rows of 16 bytes; threads past the end rewrite the last row
     const uint4 *src = (const uint4 *)cbk;
 #pragma unroll
-    for (int i = 0; i < (NC * 256 + WG - 1) / WG; i++) {
-        const int e = threadIdx.x + i * WG;
+    for (int i = 0; i < (NC * 256 + WG_ - 1) / WG_; i++) {
+        const int e = threadIdx.x + i * WG_;
         const int ec = e < NC * 256 ? e : NC * 256 - 1;
         tab[ec] = src[ec];
     }
 
-    AqPolicy<NC, R> pol;
+    AqPolicy<NC, R, L> pol;
     pol.tab = (uint32_t)(uintptr_t)tab;
 #pragma unroll
     for (int r = 0; r < R; r++) {
@@ -166,7 +173,7 @@ __global__ void __launch_bounds__(WG) aq_stream_kernel(const uint8_t *__restrict
     float acc[R * M];
 #pragma unroll
     for (int m = 0; m < R * M; m++) acc[m] = 0.f;
-    stream::walk_row<AqPolicy<NC, R>, M, XT>(pol, x, k, sx, acc);
+    stream::walk_row<AqPolicy<NC, R, L>, M, XT, L>(pol, x, k, sx, acc);
 
 #pragma unroll
     for (int r = 0; r < R; r++) {
@@ -174,8 +181,8 @@ __global__ void __launch_bounds__(WG) aq_stream_kernel(const uint8_t *__restrict
         const float s = h2f(srow[row < n ? row : n - 1]);
 #pragma unroll
         for (int m = 0; m < M; m++) {
-            const float t = wave_sum(acc[r * M + m]);
-            if (lane == 0 && row < n) y[(int64_t)m * n + row] = s * t;
+            const float t = L == 64 ? wave_sum(acc[r * M + m]) : group_sum(acc[r * M + m], L);
+            if (ul == 0 && row < n) y[(int64_t)m * n + row] = s * t;
         }
     }
 }
@@ -258,15 +265,29 @@ __global__ void __launch_bounds__(WG) aq_ragged_kernel(const uint8_t *__restrict
     }
 }
 
-size_t stream_lds(int nc, int m, int64_t k) { return stream::x_lds_bytes(m, k) + (size_t)nc * 4096; }
+size_t stream_lds(int nc, int m, int64_t k, int l = 64) { return stream::x_lds_bytes(m, k, l) + (size_t)nc * 4096; }
 size_t ragged_lds(int nc, int m) { return (size_t)nc * 4096 + (size_t)m * 64 * XU * 4; }
 
-template <int NC, int M, int R, int XT>
+template <int NC, int M, int R, int XT, int L = 64>
 void launch_stream(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     const int n = (int)w->n, k = (int)w->k;
-    hipLaunchKernelGGL((aq_stream_kernel<NC, M, R, XT>), dim3((n + WAVES * R - 1) / (WAVES * R)), dim3(WG),
-                       stream_lds(NC, M, k), s, (const uint8_t *)w->codes, (const uint16_t *)w->codebook,
-                       (const uint16_t *)w->scales, x, y, n, k, (int)(stream::x_lds_bytes(M, k) / 4));
+    constexpr int ROWS = stream::wg_of(L) / L * R;  // rows per workgroup: 8 R
+    hipLaunchKernelGGL((aq_stream_kernel<NC, M, R, XT, L>), dim3((n + ROWS - 1) / ROWS), dim3(stream::wg_of(L)),
+                       stream_lds(NC, M, k, L), s, (const uint8_t *)w->codes, (const uint16_t *)w->codebook,
+                       (const uint16_t *)w->scales, x, y, n, k, (int)(stream::x_lds_bytes(M, k, L) / 4));
+}
+
+// The half-step form at batch 5-7, two rows per lane group, on matrices with rows for two
+// of its 16-row workgroups per CU (14336x4096, 2-bit / 3-bit: batch 5 25.9 -> 23.4 /
+// 31.3 -> 28.6 us, batch 7 32.2 -> 29.5 / 37.2 -> 34.4 us); at batch 8 four rows per wave
+// in the full-step form stay faster (29.1 against 32.7 us).  Test overrides "aq.half" (any
+// size and batch from 5) and "aq.wg512" (never).
+bool stream_half(int m, int64_t n) {
+    const char *fp = forced_path();
+    if (m < 5 || strcmp(fp, "aq.wg512") == 0 || strcmp(fp, "aq.r1") == 0 || strcmp(fp, "aq.r2") == 0 ||
+        strcmp(fp, "aq.r4") == 0)
+        return false;
+    return strcmp(fp, "aq.half") == 0 || (m < 8 && n >= 32 * (int64_t)device_info().num_cus);
 }
 
 // Rows per wave of the streaming kernel: two for batches (each activation read from LDS
@@ -291,6 +312,12 @@ void launch(const qmv_weights *w, const void *x, float *y, hipStream_t s) {
     const dim3 grid((n + WAVES - 1) / WAVES);
     if (k % 64 == 0) {
         const int r = stream_rows(M, n);
+        if constexpr (M >= 5) {
+            if (stream_half(M, n)) {
+                launch_stream<NC, M, 2, XT, 32>(w, x, y, s);
+                return;
+            }
+        }
         if (r == 4) launch_stream<NC, M, 4, XT>(w, x, y, s);
         else if (r == 2) launch_stream<NC, M, 2, XT>(w, x, y, s);
         else launch_stream<NC, M, 1, XT>(w, x, y, s);
@@ -322,7 +349,8 @@ const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, f
     if (w->n > INT32_MAX || w->k > INT32_MAX / 8) return nullptr;
     const int nc = w->fmt == QMV_AQ3X8 ? 3 : 2;
     const bool str = w->k % 64 == 0;
-    const size_t lds = str ? stream_lds(nc, m, w->k) : ragged_lds(nc, m);
+    const bool half = str && stream_half(m, w->n);
+    const size_t lds = !str ? ragged_lds(nc, m) : stream_lds(nc, m, w->k, half ? 32 : 64);
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
     bool ok;
     if (nc == 2)
@@ -331,6 +359,8 @@ const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, f
         ok = xt == QMV_F32 ? dispatch_m<3, 0>(m, w, x, y, s) : dispatch_m<3, 1>(m, w, x, y, s);
     if (!ok) return nullptr;
     if (!str) return nc == 2 ? "aq2x8.ragged.lds-codebook.fma-mix" : "aq3x8.ragged.lds-codebook.fma-mix";
+    if (half)
+        return nc == 2 ? "aq2x8.stream.lds-codebook.fma-mix.2row.half-step" : "aq3x8.stream.lds-codebook.fma-mix.2row.half-step";
     if (stream_rows(m, w->n) == 4)
         return nc == 2 ? "aq2x8.stream.lds-codebook.fma-mix.4row" : "aq3x8.stream.lds-codebook.fma-mix.4row";
     if (stream_rows(m, w->n) == 2)

@@ -379,7 +379,10 @@ AQ_SMALL = [(1, 8), (5, 24), (9, 64), (33, 1000), (64, 4096), (17, 4096 + 8), (4
 
 def aq_rows(m, n):
     # rows per wave of the streaming kernel: two for batches over at least 2 x 8 rows per CU
-    # (4096 on 256 CUs), four at batch 8 over 4 x 8 rows per CU (8192)
+    # (4096 on 256 CUs), four at batch 8 over 4 x 8 rows per CU (8192); at batch 5-7 over
+    # 2 x 16 rows per CU (8192) the half-step form, two rows per 32-lane group
+    if 5 <= m <= 7 and n >= 8192:
+        return ".2row.half-step"
     return ".4row" if m >= 8 and n >= 8192 else ".2row" if m > 1 and n >= 4096 else ""
 
 
@@ -389,6 +392,20 @@ def aq_path(fmt, k, m=1, n=1):
     if k % 64:
         return f"{name}.ragged.lds-codebook.fma-mix"
     return f"{name}.stream.lds-codebook.fma-mix" + aq_rows(m, n)
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_AQ2X8, synth.FMT_AQ3X8])
+@pytest.mark.parametrize("n,k,m,xt", [(37, 4096 + 64, 5, synth.DT_BF16), (6, 2048, 8, synth.DT_F32),
+                                      (19, 64, 6, synth.DT_BF16), (33, 8192 + 2048, 7, synth.DT_F32)])
+@pytest.mark.parametrize("force", ["aq.half", "aq.wg512"])
+def test_aq_batch5_forms(qmv, monkeypatch, fmt, n, k, m, xt, force):
+    # batches 5-8 in the half-step form (two rows per 32-lane group, 2048-weight steps) and
+    # in the full-step form on request: ragged steps, one unit, row counts not a multiple
+    # of the 16 rows of a half-step workgroup
+    monkeypatch.setenv("QMV_FORCE_PATH", force)
+    name = "aq2x8" if fmt == synth.FMT_AQ2X8 else "aq3x8"
+    expect = f"{name}.stream.lds-codebook.fma-mix" + (".2row.half-step" if force == "aq.half" else aq_rows(min(m, 4), n))
+    run_case(qmv, fmt, n, k, m, xt, seed=n + k + m, expect_path=expect)
 
 
 @pytest.mark.parametrize("n,k", AQ_SMALL)
@@ -443,7 +460,7 @@ def test_aq_batched_multi_step(qmv, m, xt):
 @pytest.mark.parametrize("fmt", [synth.FMT_AQ2X8, synth.FMT_AQ3X8])
 @pytest.mark.parametrize("force,m,n", [("aq.r2", 1, 37), ("aq.r1", 4, 37), ("", 3, 17), ("", 3, 4096 + 17),
                                        ("aq.r2", 2, 1), ("aq.r4", 1, 37), ("aq.r4", 4, 203), ("aq.r4", 8, 6),
-                                       ("", 8, 8192 + 17)])
+                                       ("", 8, 8192 + 17), ("", 6, 8192 + 17)])
 def test_aq_rows_per_wave(qmv, monkeypatch, fmt, force, m, n):
     # one, two or four rows per wave, forced or by default; row counts that are not a multiple
     # of the rows per workgroup leave the last wave's later rows past the end
