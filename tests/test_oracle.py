@@ -334,7 +334,7 @@ def test_aq3_gemv_exact_rational_tiny():
 
 def test_cb8_closed_forms():
     # one index per row: y = cb[row][v] * sum(x)   ("row-sum times scale"); x = e_j gives column j
-    n, k = 6, 64
+    n, k = 6, 48
     v = np.array([0, 17, 128, 200, 255, 99])
     cb = f16(np.sort(np.random.default_rng(3).normal(0, 0.02, (n, 256)), axis=1))
     m = oracle.Mat(oracle.CB8, n, k, {"idx": np.repeat(v[:, None], k, axis=1).astype(np.uint8), "cb": cb})
@@ -343,10 +343,10 @@ def test_cb8_closed_forms():
     sx = float(np.sum(x[0].astype(np.float64)))
     for r in range(n):
         assert abs(y[0, r] - float(cb[r, v[r]]) * sx) <= 1e-15 * float(np.sum(np.abs(x)))
-    w = synth.gen_weights(synth.FMT_CB8, 5, 64, seed=2)
-    m = oracle.Mat(oracle.CB8, 5, 64, w)
-    for j in (0, 13, 63):
-        e = np.zeros((1, 64), dtype=np.float32)
+    w = synth.gen_weights(synth.FMT_CB8, 5, 48, seed=2)
+    m = oracle.Mat(oracle.CB8, 5, 48, w)
+    for j in (0, 13, 47):
+        e = np.zeros((1, 48), dtype=np.float32)
         e[0, j] = 1.0
         assert np.array_equal(oracle.gemv(m, e)[0][0], w["cb"].astype(np.float64)[np.arange(5), w["idx"][:, j]])
 
@@ -439,6 +439,62 @@ def test_quantizer_properties_random():
     # negating x negates xq exactly (round half away from zero is odd-symmetric)
     xqn, xsn = oracle.quant_act(-x)
     assert np.array_equal(xqn, -xq) and np.array_equal(xsn, xs)
+
+
+def _binary32_half_ulp(v: Fraction) -> Fraction:
+    """Half the spacing of binary32 values around the positive value v (normal range)."""
+    e = v.numerator.bit_length() - v.denominator.bit_length()
+    if Fraction(2) ** e > v:
+        e -= 1
+    return Fraction(2) ** (e - 24)
+
+
+def test_quantizer_division_trap_block():
+    # A block whose quotients round, in binary32, to exactly k + 1/2, so xq must be k + 1
+    # (away from zero).  On the marked elements an oracle that divided in binary64 (the
+    # exact quotient is below k + 1/2) or multiplied by fl32(1/xs) (the product lands
+    # below k + 1/2) would give k.
+    g = load_golden("quant_act.txt")
+    x = np.array(g["d_x_bits"], dtype=np.uint32).view(np.float32)
+    xs = np.uint32(g["d_xs_bits"]).view(np.float32)
+    # xs itself: amax / 127 rounded to binary32 (exact rational check of the golden's claim)
+    amax = Fraction(float(x[0]))
+    assert abs(Fraction(float(xs)) - amax / 127) <= _binary32_half_ulp(amax / 127)
+    recip = np.float32(1) / xs  # numpy binary32 division (correctly rounded)
+    for i, (k, trap) in enumerate(zip(g["d_k"], g["d_trap"]), start=1):
+        half = Fraction(2 * abs(k) + 1, 2)
+        q = Fraction(float(abs(x[i]))) / Fraction(float(xs))
+        assert abs(half - q) < _binary32_half_ulp(half)   # rounds to k + 1/2 in binary32
+        if trap & 1:                                      # ... from below: the exact (or
+            assert q < half                               # binary64) quotient rounds to k
+        if trap & 2:                                      # the reciprocal form lands below
+            assert Fraction(float(np.float32(abs(x[i])) * recip)) < half
+    xq, xs_o = oracle.quant_act(x[None, :])
+    assert xs_o.view(np.uint32)[0, 0] == g["d_xs_bits"]
+    assert xq[0].tolist() == g["d_xq"]
+
+
+def test_quantizer_matches_numpy_binary32_reference():
+    # numpy's own binary32 arithmetic over a full activation matrix of the prefill workload:
+    # amax and the two divisions in float32 (IEEE, correctly rounded), the rounding to an
+    # integer done exactly in float64 (trunc(t + copysign(1/2, t)) is exact for binary32 t)
+    x = synth.gen_x(512, 11008, seed=33)
+    x[0, :32] = 0.0                                        # an all-zero block
+    x[1, 32:64] *= np.float32(1e-30)                       # tiny and huge magnitudes
+    x[2, 64:96] *= np.float32(1e30)
+    x[3, 96:128] = np.float32(-2.5)                        # constant block: every value -127
+    blocks = x.reshape(512, -1, 32)
+    amax = np.max(np.abs(blocks), axis=2)
+    xs = amax / np.float32(127)
+    assert xs.dtype == np.float32
+    with np.errstate(invalid="ignore", divide="ignore"):
+        t = (blocks / xs[..., None]).astype(np.float64)
+    assert t.dtype == np.float64
+    ref = np.trunc(t + np.copysign(0.5, t))
+    ref = np.where(amax[..., None] == 0, 0.0, np.clip(ref, -127, 127)).astype(np.int8).reshape(512, -1)
+    xq, xs_o = oracle.quant_act(x)
+    assert np.array_equal(xs_o.view(np.uint32), xs.view(np.uint32))
+    assert np.array_equal(xq, ref)
 
 
 # ------------------------------------------------------------ q6_K GEMM
