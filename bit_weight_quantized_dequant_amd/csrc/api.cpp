@@ -33,7 +33,7 @@ int block_of(int32_t fmt) {
     case QMV_Q6_K: return 256;
     case QMV_CB4: return 128;
     case QMV_AQ2X8: return 8;
-    case QMV_CB8: return 64;
+    case QMV_CB8: return 1;  // one index byte per weight: no block structure
     case QMV_AQ3X8: return 8;
     }
     return 0;
@@ -176,6 +176,8 @@ int qmv_validate(const qmv_weights *w, int32_t m, int32_t xt) {
     const int blk = block_of(w->fmt);
     if (!blk) return QMV_ERR_FORMAT;
     if (w->n <= 0 || w->k <= 0 || w->k % blk) return QMV_ERR_SHAPE;
+    // the 8-bit codebook kernels stream 64 index bytes per lane step; the format has no block
+    if (w->fmt == QMV_CB8 && w->k % 64) return QMV_ERR_SHAPE;
     if (xt != QMV_F32 && xt != QMV_BF16) return QMV_ERR_DTYPE;
     if (m < 1 || m > QMV_MAX_BATCH) return QMV_ERR_BATCH;
     const void *need[5] = {w->codes, nullptr, nullptr, nullptr, nullptr};
@@ -361,7 +363,7 @@ int qmv_moe_ffn(const qmv_weights *gate, const qmv_weights *up, const qmv_weight
     if (n_ids < 1 || n_ids > 64) return QMV_ERR_BATCH;
     if (!ids || !x || !h || !y) return QMV_ERR_NULL;
     if (!aligned16(x) || !aligned16(h) || !aligned16(y) || ((uintptr_t)ids & 3u)) return QMV_ERR_ALIGN;
-    const char *path = launch_moe_ffn(gate, up, down, n_experts, ids, n_ids, x, xt, h, y,
+    const char *path = launch_moe_cb4(gate, up, down, n_experts, ids, n_ids, x, xt, h, y,
                                       (hipStream_t)stream);
     if (!path) return QMV_ERR_LIMIT;
     return finish_launch("qmv_moe_ffn", gate, n_ids, path);

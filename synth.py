@@ -123,8 +123,6 @@ def gen_weights(fmt: int, n: int, k: int, seed: int = 0, expert: int = 0, matrix
         s = _f16(_rng(*key, 3).uniform(0.5, 1.5, n))
         return {"codes": codes, "cbk": cbk, "s": s}
     if fmt == FMT_CB8:
-        if k % 64:
-            raise ValueError("cb8 needs k % 64 == 0")
         idx = rand_bytes(n * k, *key, 1).reshape(n, k)
         cb = np.sort(_rng(*key, 2).normal(0.0, 0.02, (n, 256)), axis=1)
         return {"idx": idx, "cb": _f16(cb)}

@@ -46,7 +46,10 @@ def test_plane_bytes_match_the_format_definitions():
     # 3-bit additive: 3 bytes per 8 weights + 2 B per row + 12 KiB of codebooks
     assert qmv.plane_bytes(qmv.AQ3X8, 14336, 4096, "codes") == 14336 * 512 * 3
     assert qmv.weight_bytes(qmv.AQ3X8, 14336, 4096) == 14336 * 512 * 3 + 2 * 14336 + 12288
-    assert qmv.weight_bytes(qmv.CB8, 4, 96) == -2              # k not a multiple of 64
+    # the 8-bit codebook has no block: any k has a size, but its kernels take k % 64 == 0
+    assert qmv.weight_bytes(qmv.CB8, 4, 96) == 4 * 96 + 4 * 512
+    assert qmv.validate(_fake(qmv.CB8, 4, 96), 1, qmv.F32) == -2
+    assert qmv.validate(_fake(qmv.CB8, 4, 48), 1, qmv.F32) == -2
     assert qmv.plane_bytes(qmv.Q4_0, 4, 32, "codebook") == 0
     assert qmv.weight_bytes(qmv.Q6_K, 4, 100) == -2
     assert qmv.weight_bytes(9, 4, 256) == -3
