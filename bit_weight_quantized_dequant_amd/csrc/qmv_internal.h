@@ -52,8 +52,5 @@ const char *launch_expand_q6k(const qmv_weights *w, int8_t *plane, hipStream_t s
 const char *launch_moe_cb4(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,
                            int n_experts, const int32_t *ids, int n_ids, const void *x, int xt,
                            float *h, float *y, hipStream_t s);
-const char *launch_moe_ffn(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,
-                           int n_experts, const int32_t *ids, int n_ids, const void *x, int xt,
-                           float *h, float *y, hipStream_t s);
 
 }  // namespace qmv

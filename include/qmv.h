@@ -45,7 +45,8 @@ enum {
     QMV_CB4 = 3,   /* 4-bit index into a 16-entry fp16 codebook per 128 weights along k         */
     QMV_AQ2X8 = 4, /* per 8 weights two 8-bit codes into two 256x8 fp16 codebooks, summed,
                       times an fp16 per-row scale                                               */
-    QMV_CB8 = 5,   /* 8-bit index into a 256-entry fp16 codebook per output row; k % 64 == 0   */
+    QMV_CB8 = 5,   /* 8-bit index into a 256-entry fp16 codebook per output row (no block
+                      structure; the GEMV and dequant kernels take k % 64 == 0)              */
     QMV_AQ3X8 = 6  /* as AQ2X8 with three codes and three codebooks per 8 weights              */
 };
 
@@ -56,7 +57,8 @@ enum { QMV_F32 = 0, QMV_BF16 = 1 };
 enum {
     QMV_OK = 0,
     QMV_ERR_NULL = -1,      /* a required pointer is NULL                                        */
-    QMV_ERR_SHAPE = -2,     /* n, k <= 0, or k not a multiple of the format's block             */
+    QMV_ERR_SHAPE = -2,     /* n, k <= 0, or k not a multiple of the format's block (for
+                               QMV_CB8 in qmv_validate and the calls that use it: of 64)     */
     QMV_ERR_FORMAT = -3,    /* unknown format, or an operation the format does not support       */
     QMV_ERR_DTYPE = -4,     /* unknown activation dtype                                          */
     QMV_ERR_ALIGN = -5,     /* a plane, x or y pointer is not 16-byte aligned                   */
@@ -108,15 +110,26 @@ enum { QMV_PLANE_CODES = 0, QMV_PLANE_CODES_HI = 1, QMV_PLANE_SCALES = 2, QMV_PL
        QMV_PLANE_CODEBOOK = 4 };
 
 /* Host only (no HIP call).  Bytes of one plane of an n x k matrix in format fmt
- * (0 for a plane the format does not use), or a negative QMV_ERR_* code. */
+ * (0 for a plane the format does not use), or a negative QMV_ERR_* code.
+ * Byte accounting of the stored format: a decode GEMV's time is its bytes over the
+ * bandwidth (quantprobe LAWS.md, Law 4), so the plane sizes are the unit every
+ * throughput figure is priced in ("57 · r54 — MINFER_MMQ_Q6K_EXP", §2.2: the bytes a
+ * plane occupies reconcile exactly with its census). */
 int64_t qmv_plane_bytes(int32_t fmt, int64_t n, int64_t k, int32_t plane);
 
-/* Host only.  Sum of qmv_plane_bytes over all planes: the bytes a GEMV must stream. */
+/* Host only.  Sum of qmv_plane_bytes over all planes: the bytes a GEMV must stream
+ * (quantprobe LAWS.md, Law 4 and its per-format amendment: scales and codebooks count,
+ * the format's metadata density is part of its price).  Negative QMV_ERR_* code for an
+ * unknown format (QMV_ERR_FORMAT) or a bad shape (QMV_ERR_SHAPE). */
 int64_t qmv_weight_bytes(int32_t fmt, int64_t n, int64_t k);
 
 /* Host only (no HIP call, no dereference of device pointers).  Checks the
  * descriptor for a GEMV with batch m and activation dtype xt: format, shape,
- * required planes non-NULL and 16-byte aligned, 1 <= m <= QMV_MAX_BATCH. */
+ * required planes non-NULL and 16-byte aligned, 1 <= m <= QMV_MAX_BATCH.
+ * Returns QMV_OK or the first failing QMV_ERR_* code (FORMAT, SHAPE, DTYPE, BATCH,
+ * NULL, ALIGN, LIMIT, in that order).  Every entry point runs it before launching, so a
+ * bad descriptor fails loudly with a code instead of reaching a kernel ("57 · r54 —
+ * MINFER_MMQ_Q6K_EXP", §3.1: a failure is explicit and named, never a silent path). */
 int qmv_validate(const qmv_weights *w, int32_t m, int32_t xt);
 
 /*
@@ -186,7 +199,12 @@ int qmm_quant_act(const float *x, int32_t m, int64_t k, int8_t *xq, float *xs, v
  */
 int qmv_read_ceiling(const void *p, int64_t bytes, uint32_t *sink, void *stream);
 
-/* Workspace bytes qmm_gemm needs for m activation rows (xq and xs), or < 0 on error. */
+/* Host only.  Workspace bytes qmm_gemm needs for m activation rows: the int8 activations
+ * xq [m][k] and their per-32 scales xs [m][k/32] (at a 256-byte aligned offset), the
+ * activation side of the q6_K int8 contraction ("57 · r54 — MINFER_MMQ_Q6K_EXP", §2.1:
+ * the kernel contracts int8 weights against int8 activations).  The caller allocates
+ * it; the library allocates nothing.  Negative QMV_ERR_* code (NULL, FORMAT for a format
+ * other than q6_K, SHAPE, BATCH for m < 1) on a bad descriptor. */
 int64_t qmm_workspace_bytes(const qmv_weights *w, int32_t m);
 
 /*
@@ -242,7 +260,10 @@ int qmm_register_plane(const qmv_weights *w, void *plane, int64_t plane_bytes, v
 int qmm_unregister_plane(const qmv_weights *w);
 
 /*
- * Mixture-of-experts FFN over routed experts (batch 1 decode):
+ * Mixture-of-experts FFN over routed experts (batch 1 decode).  Per token only the
+ * routed experts' 4-bit codebook weights are streamed, and they dominate the bytes of a
+ * decode step ("Chasing x100", the "inversion" paragraph: routed-expert decode on 4-bit
+ * codebooks runs near the memory read floor):
  *   for each listed expert e = ids[j]:  h[j] = SiLU(G_e x) * (U_e x),  y[j] = D_e h[j]
  * with SiLU(z) = z / (1 + e^-z).  No routing weights are applied; the caller
  * combines y[j].
@@ -263,15 +284,20 @@ int qmv_moe_ffn(const qmv_weights *gate, const qmv_weights *up, const qmv_weight
                 float *h, float *y, void *stream);
 
 /* Label of the kernel variant the calling thread's last successful call launched
- * (a thread-local string owned by the library).  With QMV_DEBUG=1 in the
- * environment every call also prints "qmv: <call> fmt=.. n=.. k=.. m=.. path=.."
- * to stderr. */
+ * (a thread-local string owned by the library; valid until that thread's next call).
+ * With QMV_DEBUG=1 in the environment every call also prints
+ * "qmv: <call> fmt=.. n=.. k=.. m=.. path=.." to stderr.  This is the liveness label of
+ * "57 · r54 — MINFER_MMQ_Q6K_EXP", §2.4: parity cannot tell a fast path that never ran
+ * from one that did, so every launch names its variant and tests and benchmarks count
+ * the labels.  Empty before the thread's first successful call; never NULL. */
 const char *qmv_last_path(void);
 
-/* Static description of a status code. */
+/* Static, library-owned description of a status code ("unknown status" for a code this
+ * version does not define); never NULL.  Pairs with the named failure codes above
+ * ("57 · r54 — MINFER_MMQ_Q6K_EXP", §3.1: a failure is loud and says what it was). */
 const char *qmv_strerror(int code);
 
-/* Library version string. */
+/* Library version string (static, library-owned). */
 const char *qmv_version(void);
 
 #ifdef __cplusplus
