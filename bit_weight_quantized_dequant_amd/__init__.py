@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import weakref
 
 __all__ = [
     "Q4_0", "Q6_K", "CB4", "AQ2X8", "CB8", "AQ3X8", "F32", "BF16", "QmvError", "QWeights", "lib", "plane_bytes",
@@ -313,9 +314,17 @@ def plane_bytes_of(w: QWeights) -> int:
     return lib().qmm_plane_bytes(w.ref)
 
 
+def _forget_plane(desc, plane):
+    # finalizer of a registered QWeights: drop the library's record before the plane's
+    # memory (and the codes' memory, which keys the record) can be reused by another matrix
+    lib().qmm_unregister_plane(C.byref(desc))
+
+
 def register_plane(w: QWeights, plane=None, stream=None):
     """Fill a pre-expanded plane for the q6_K GEMM (allocated here unless given) and record
-    it for w.  Returns the plane tensor, which must be kept alive while it is registered."""
+    it for w.  The plane is kept alive with w; when w is garbage-collected (or
+    unregister_plane is called) the library's record is dropped, so a later matrix whose
+    tensors reuse the same addresses never picks up a stale plane.  Returns the plane."""
     import torch
     need = plane_bytes_of(w)
     if need < 0:
@@ -325,13 +334,20 @@ def register_plane(w: QWeights, plane=None, stream=None):
     _need(plane, (plane.dtype,), None, "plane")
     _check(lib().qmm_register_plane(w.ref, _ptr(plane), plane.numel() * plane.element_size(), _stream(stream)),
            "qmm_register_plane")
-    w._plane = plane
+    old = getattr(w, "_plane_fin", None)
+    if old is not None:
+        old.detach()
+    desc = _W(w._s.fmt, w._s.n, w._s.k, w._s.codes, w._s.codes_hi, w._s.scales, w._s.super, w._s.codebook)
+    w._plane_fin = weakref.finalize(w, _forget_plane, desc, plane)
     return plane
 
 
 def unregister_plane(w: QWeights):
     _check(lib().qmm_unregister_plane(w.ref), "qmm_unregister_plane")
-    w._plane = None
+    fin = getattr(w, "_plane_fin", None)
+    if fin is not None:
+        fin.detach()
+        w._plane_fin = None
 
 
 def moe_ffn(gate: QWeights, up: QWeights, down: QWeights, n_experts: int, ids, x, h=None, y=None,

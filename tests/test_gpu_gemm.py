@@ -2,8 +2,9 @@
 
 Bar: the int32 per-block partials I32[m][n][c] are bit-exact; every output is within
 2e-3 * sum_k |w| |x_hat| of the oracle's double result (x_hat = xs * xq, the quantized
-activations, as the oracle defines the GEMM); full workload sizes are checked on
-sampled (m, n) pairs, which the oracle computes one by one.
+activations, as the oracle defines the GEMM); full workload sizes are checked on every
+output of a dozen token rows and every token of several weight rows (the oracle computes
+those pairs one by one; the whole product would take it minutes).
 """
 import numpy as np
 import pytest
@@ -30,6 +31,19 @@ def _setup(qmv, n, k, m, seed):
     x = synth.gen_x(m, k, seed=seed)
     print(f"gemm case n={n} k={k} m={m} seed={seed}", flush=True)
     return w, x, qweights(synth.FMT_Q6_K, n, k, w), torch.from_numpy(x).cuda()
+
+
+def gemm_check_pairs(m, n, seed=1):
+    """(m, n) pairs for a full-size GEMM: every output of 12 token rows (the first, the
+    last, the two around each 128-token tile edge and 4 random ones) and every token of 8
+    weight rows (the first, the last, the two around the 64-row tile edge and 4 random
+    ones); the full product would take the oracle minutes."""
+    rng = np.random.default_rng(seed)
+    toks = sorted({0, m - 1, 127 % m, 128 % m, 255 % m, 256 % m, *rng.integers(0, m, 4).tolist()})
+    rows = sorted({0, n - 1, 63 % n, 64 % n, *rng.integers(0, n, 4).tolist()})
+    a = np.meshgrid(np.array(toks), np.arange(n), indexing="ij")
+    b = np.meshgrid(np.arange(m), np.array(rows), indexing="ij")
+    return np.concatenate([a[0].ravel(), b[0].ravel()]), np.concatenate([a[1].ravel(), b[1].ravel()])
 
 
 @pytest.mark.parametrize("n,k,m", [(32, 256, 32), (64, 512, 128), (70, 768, 45), (130, 1024, 200), (3, 256, 1)])
@@ -66,11 +80,9 @@ def test_gemm_prefill_shapes_sampled(qmv, n, k):
     y = qmv.gemm(W, xd).cpu().numpy()
     torch.cuda.synchronize()
     xq, xs = oracle.quant_act(x)
-    rng = np.random.default_rng(1)
-    mm = np.concatenate([[0, m - 1, 0, m - 1], rng.integers(0, m, 252)])
-    nn = np.concatenate([[0, 0, n - 1, n - 1], rng.integers(0, n, 252)])
-    yr, b = oracle.q6k_gemm_pairs(oracle.Mat(oracle.Q6_K, n, k, w), xq, xs, mm, nn, nthreads=8)
-    assert_parity(y[mm, nn][None, :], yr[None, :], b[None, :], f"gemm {n}x{k} sampled")
+    mm, nn = gemm_check_pairs(m, n)
+    yr, b = oracle.q6k_gemm_pairs(oracle.Mat(oracle.Q6_K, n, k, w), xq, xs, mm, nn, nthreads=oracle.max_threads())
+    assert_parity(y[mm, nn][None, :], yr[None, :], b[None, :], f"gemm {n}x{k} rows and columns")
     # the exact int32 partials of a few sampled pairs, from the same MFMA path
     import torch as _t
     xq_d, _ = qmv.quant_act(xd)
@@ -134,16 +146,18 @@ def test_plane_holds_the_exact_hi_lo_split(qmv):
     w["sc"][1, 0, :] = -128
     w["sc"][2, 0, :] = 127
     W = qweights(synth.FMT_Q6_K, n, k, w)
-    plane = qmv.register_plane(W)
-    torch.cuda.synchronize()
-    assert qmv.last_path() == "plane.q6k.expand"
-    p = plane.cpu().numpy().view(np.int8).astype(np.int64)
+    try:
+        plane = qmv.register_plane(W)
+        torch.cuda.synchronize()
+        assert qmv.last_path() == "plane.q6k.expand"
+        p = plane.cpu().numpy().view(np.int8).astype(np.int64)
+    finally:
+        qmv.unregister_plane(W)
     H, L = p[: n * k].reshape(n, k), p[n * k: 2 * n * k].reshape(n, k)
     q = oracle.codes(oracle.Mat(oracle.Q6_K, n, k, w)).astype(np.int64)
     sc = np.repeat(w["sc"].reshape(n, k // 16).astype(np.int64), 16, axis=1)
     assert np.array_equal(64 * H + L, sc * (q - 32))
     assert L.min() >= 0 and L.max() <= 63 and H.min() >= -64 and H.max() <= 64
-    qmv.unregister_plane(W)
 
 
 @pytest.mark.parametrize("n,k,m", [(64, 512, 128), (70, 768, 45), (257, 2048, 130), (4096, 1024, 512), (3, 256, 1),
@@ -161,13 +175,15 @@ def test_gemm_with_plane_is_byte_identical(qmv, monkeypatch, n, k, m, force):
     assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split"
     p0 = qmv.partials(W, xq)
     qmv.register_plane(W)
-    y1 = qmv.gemm_q8(W, xq, xs)
-    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
-    p1 = qmv.partials(W, xq)
-    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.partials.plane"
-    y2 = qmv.gemm(W, xd)
-    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
-    qmv.unregister_plane(W)
+    try:
+        y1 = qmv.gemm_q8(W, xq, xs)
+        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+        p1 = qmv.partials(W, xq)
+        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.partials.plane"
+        y2 = qmv.gemm(W, xd)
+        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+    finally:
+        qmv.unregister_plane(W)
     y3 = qmv.gemm_q8(W, xq, xs)
     assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split"
     torch.cuda.synchronize()
@@ -196,12 +212,14 @@ def test_plane_labels_opt_out_and_fallback(qmv, monkeypatch):
     monkeypatch.delenv("QMV_Q6K_EXP")
     # registered for 96 rows; a descriptor over the same codes with 95 rows must not use it
     qmv.register_plane(W)
-    W95 = qmv.QWeights(synth.FMT_Q6_K, n - 1, k, W.planes)
-    y95 = qmv.gemm_q8(W95, xq, xs)
-    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split(fallback!)"
-    y_plane = qmv.gemm_q8(W, xq, xs)
-    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
-    qmv.unregister_plane(W)
+    try:
+        W95 = qmv.QWeights(synth.FMT_Q6_K, n - 1, k, W.planes)
+        y95 = qmv.gemm_q8(W95, xq, xs)
+        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split(fallback!)"
+        y_plane = qmv.gemm_q8(W, xq, xs)
+        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+    finally:
+        qmv.unregister_plane(W)
     torch.cuda.synchronize()
     ref = ref.cpu().numpy()
     assert np.array_equal(y_off.cpu().numpy().view(np.int32), ref.view(np.int32))
@@ -218,15 +236,42 @@ def test_gemm_prefill_shapes_with_plane(qmv, n, k):
     w, x, W, xd = _setup(qmv, n, k, m, seed=0)
     y0 = qmv.gemm(W, xd)
     qmv.register_plane(W)
-    y1 = qmv.gemm(W, xd)
-    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
-    qmv.unregister_plane(W)
+    try:
+        y1 = qmv.gemm(W, xd)
+        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+    finally:
+        qmv.unregister_plane(W)
     torch.cuda.synchronize()
     y0, y1 = y0.cpu().numpy(), y1.cpu().numpy()
     assert np.array_equal(y0.view(np.int32), y1.view(np.int32))
     xq, xs = oracle.quant_act(x)
-    rng = np.random.default_rng(2)
-    mm = np.concatenate([[0, m - 1], rng.integers(0, m, 62)])
-    nn = np.concatenate([[n - 1, 0], rng.integers(0, n, 62)])
-    yr, b = oracle.q6k_gemm_pairs(oracle.Mat(oracle.Q6_K, n, k, w), xq, xs, mm, nn, nthreads=8)
-    assert_parity(y1[mm, nn][None, :], yr[None, :], b[None, :], f"gemm plane {n}x{k} sampled")
+    mm, nn = gemm_check_pairs(m, n, seed=2)
+    yr, b = oracle.q6k_gemm_pairs(oracle.Mat(oracle.Q6_K, n, k, w), xq, xs, mm, nn, nthreads=oracle.max_threads())
+    assert_parity(y1[mm, nn][None, :], yr[None, :], b[None, :], f"gemm plane {n}x{k} rows and columns")
+
+
+def test_collected_weights_leave_no_stale_plane(qmv):
+    # a registered matrix that is garbage-collected without unregister_plane drops the
+    # library's record with it: a new matrix of the same shape whose tensors reuse the freed
+    # addresses must run the in-kernel expansion, not the old plane
+    import gc
+    import torch
+    n, k, m = 64, 512, 40
+    w, x, W, xd = _setup(qmv, n, k, m, seed=11)
+    xq, xs = qmv.quant_act(xd)
+    qmv.register_plane(W)
+    qmv.gemm_q8(W, xq, xs)
+    assert qmv.last_path().endswith(".plane")
+    addr = W.planes["ql"].data_ptr()
+    del W
+    gc.collect()
+    torch.cuda.synchronize()
+    w2 = synth.gen_weights(synth.FMT_Q6_K, n, k, seed=12)
+    W2 = qweights(synth.FMT_Q6_K, n, k, w2)
+    y = qmv.gemm_q8(W2, xq, xs)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split"
+    torch.cuda.synchronize()
+    yr, b = oracle.q6k_gemm_pairs(oracle.Mat(oracle.Q6_K, n, k, w2), *oracle.quant_act(x),
+                                  *[a.ravel() for a in np.meshgrid(np.arange(m), np.arange(n), indexing="ij")])
+    assert_parity(y.cpu().numpy().reshape(1, -1), yr[None, :], b[None, :], "gemm after a collected plane")
+    print("codes address reused:", W2.planes["ql"].data_ptr() == addr)

@@ -2,8 +2,8 @@
 
 Bar: every output within 2e-3 * sum_k |w||x| of the oracle's double result;
 x = e_j returns column j of W bit-exactly; outputs are deterministic and
-row-permutation equivariant bit-for-bit.  Full workload sizes are checked on
-sampled rows (the oracle computes those rows one by one).
+row-permutation equivariant bit-for-bit.  Full workload sizes are checked on every
+output row (the oracle runs multithreaded over rows).
 """
 import numpy as np
 import pytest
@@ -37,16 +37,10 @@ def run_case(qmv, fmt, n, k, m, xt, seed, rows=None, expect_path=None):
     y = y.cpu().numpy()
     om = oracle.Mat(fmt, n, k, w)
     if rows is None:
-        yr, b = oracle.gemv(om, x, xt)
+        yr, b = oracle.gemv(om, x, xt, nthreads=oracle.max_threads())
         return assert_parity(y, yr, b, f"fmt={fmt} {n}x{k} m={m}")
-    yr, b = oracle.gemv(om, x, xt, rows=rows)
+    yr, b = oracle.gemv(om, x, xt, rows=rows, nthreads=oracle.max_threads())
     return assert_parity(y[:, rows], yr, b, f"fmt={fmt} {n}x{k} m={m} sampled")
-
-
-def sample_rows(n, count=96, seed=0):
-    rng = np.random.default_rng(seed)
-    r = set(rng.choice(n, size=min(n, count), replace=False).tolist()) | {0, n - 1}
-    return np.array(sorted(r), dtype=np.int64)
 
 
 # ------------------------------------------------------------------ q4_0
@@ -87,15 +81,15 @@ def test_q4_0_two_rows_per_wave_tails(qmv, n, k, m):
 
 
 @pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096), (4096, 11008)])
-def test_q4_0_full_size_sampled(qmv, n, k):
-    run_case(qmv, synth.FMT_Q4_0, n, k, 1, synth.DT_F32, seed=0, rows=sample_rows(n))
+def test_q4_0_full_size_all_rows(qmv, n, k):
+    run_case(qmv, synth.FMT_Q4_0, n, k, 1, synth.DT_F32, seed=0)
 
 
 @pytest.mark.parametrize("m", [2, 4, 8])
 @pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096), (4096, 11008)])
-def test_q4_0_full_size_batched_sampled(qmv, n, k, m):
+def test_q4_0_full_size_batched_all_rows(qmv, n, k, m):
     # the batch workloads the benchmark times (K-chunked kernel), at their full sizes
-    run_case(qmv, synth.FMT_Q4_0, n, k, m, synth.DT_F32, seed=m, rows=sample_rows(n),
+    run_case(qmv, synth.FMT_Q4_0, n, k, m, synth.DT_F32, seed=m,
              expect_path=q4_path(m, k))
 
 
@@ -191,8 +185,8 @@ def test_q6k_batched(qmv, m, xt):
 
 
 @pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096)])
-def test_q6k_large_sampled(qmv, n, k):
-    run_case(qmv, synth.FMT_Q6_K, n, k, 1, synth.DT_F32, seed=0, rows=sample_rows(n))
+def test_q6k_large_all_rows(qmv, n, k):
+    run_case(qmv, synth.FMT_Q6_K, n, k, 1, synth.DT_F32, seed=0)
 
 
 @pytest.mark.parametrize("n,k,m,xt", [(4, 32768, 1, synth.DT_F32), (33, 20480, 1, synth.DT_F32),
@@ -314,8 +308,8 @@ def test_cb4_batched(qmv, m):
 
 
 @pytest.mark.parametrize("n,k", [(2048, 7168), (7168, 2048)])
-def test_cb4_expert_shapes_sampled(qmv, n, k):
-    run_case(qmv, synth.FMT_CB4, n, k, 1, synth.DT_BF16, seed=0, rows=sample_rows(n))
+def test_cb4_expert_shapes_all_rows(qmv, n, k):
+    run_case(qmv, synth.FMT_CB4, n, k, 1, synth.DT_BF16, seed=0)
 
 
 @pytest.mark.parametrize("n,k,m,xt", [(4, 32768, 1, synth.DT_F32), (33, 20480, 1, synth.DT_BF16),
@@ -380,10 +374,13 @@ AQ_SMALL = [(1, 8), (5, 24), (9, 64), (33, 1000), (64, 4096), (17, 4096 + 8), (4
 def aq_rows(m, n):
     # rows per wave of the streaming kernel: two for batches over at least 2 x 8 rows per CU
     # (4096 on 256 CUs), four at batch 8 over 4 x 8 rows per CU (8192); at batch 5-7 over
-    # 2 x 16 rows per CU (8192) the half-step form, two rows per 32-lane group
-    if 5 <= m <= 7 and n >= 8192:
+    # 2 x 16 rows per CU (8192) the half-step form, two rows per 32-lane group.  The
+    # thresholds scale with the device's CU count, as the library's do.
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if 5 <= m <= 7 and n >= 32 * cus:
         return ".2row.half-step"
-    return ".4row" if m >= 8 and n >= 8192 else ".2row" if m > 1 and n >= 4096 else ""
+    return ".4row" if m >= 8 and n >= 32 * cus else ".2row" if m > 1 and n >= 16 * cus else ""
 
 
 def aq_path(fmt, k, m=1, n=1):
@@ -415,8 +412,8 @@ def test_aq_small_full_parity(qmv, n, k):
 
 @pytest.mark.parametrize("m", [1, 4])
 @pytest.mark.parametrize("n,k", [(14336, 4096), (4096, 14336)])
-def test_aq_config_shapes_sampled(qmv, m, n, k):
-    run_case(qmv, synth.FMT_AQ2X8, n, k, m, synth.DT_BF16, seed=0, rows=sample_rows(n))
+def test_aq_config_shapes_all_rows(qmv, m, n, k):
+    run_case(qmv, synth.FMT_AQ2X8, n, k, m, synth.DT_BF16, seed=0)
 
 
 @pytest.mark.parametrize("m", [2, 3, 8])
@@ -469,8 +466,7 @@ def test_aq_rows_per_wave(qmv, monkeypatch, fmt, force, m, n):
     k = 4096 + 64
     name = "aq2x8" if fmt == synth.FMT_AQ2X8 else "aq3x8"
     rows = {"aq.r1": "", "aq.r2": ".2row", "aq.r4": ".4row"}.get(force, aq_rows(m, n))
-    sample = sample_rows(n) if n > 4096 else None
-    run_case(qmv, fmt, n, k, m, synth.DT_F32, seed=n + m, rows=sample,
+    run_case(qmv, fmt, n, k, m, synth.DT_F32, seed=n + m,
              expect_path=f"{name}.stream.lds-codebook.fma-mix" + rows)
 
 
@@ -481,8 +477,8 @@ def test_aq3_small_full_parity(qmv, n, k):
 
 @pytest.mark.parametrize("m", [1, 4])
 @pytest.mark.parametrize("n,k", [(14336, 4096), (4096, 14336)])
-def test_aq3_config_shapes_sampled(qmv, m, n, k):
-    run_case(qmv, synth.FMT_AQ3X8, n, k, m, synth.DT_BF16, seed=0, rows=sample_rows(n))
+def test_aq3_config_shapes_all_rows(qmv, m, n, k):
+    run_case(qmv, synth.FMT_AQ3X8, n, k, m, synth.DT_BF16, seed=0)
 
 
 @pytest.mark.parametrize("m,xt,k", [(2, synth.DT_F32, 2048), (3, synth.DT_BF16, 8192 + 64), (6, synth.DT_F32, 12288),
@@ -562,14 +558,13 @@ def test_cb8_batch5_forms(qmv, monkeypatch, n, k, m, xt, path):
     force = None if path == "default" else path
     if force:
         monkeypatch.setenv("QMV_FORCE_PATH", force)
-    rows = sample_rows(n) if n > 512 else None
-    run_case(qmv, synth.FMT_CB8, n, k, m, xt, seed=n + k + m, rows=rows, expect_path=cb8_path(m, n, force))
+    run_case(qmv, synth.FMT_CB8, n, k, m, xt, seed=n + k + m, expect_path=cb8_path(m, n, force))
 
 
 @pytest.mark.parametrize("n,k", [(2048, 7168), (7168, 2048), (129280, 7168)])
-def test_cb8_shared_expert_and_head_shapes_sampled(qmv, n, k):
+def test_cb8_shared_expert_and_head_shapes_all_rows(qmv, n, k):
     # the shared expert's gate/up and down, and the output head, at their full sizes
-    run_case(qmv, synth.FMT_CB8, n, k, 1, synth.DT_BF16, seed=0, rows=sample_rows(n))
+    run_case(qmv, synth.FMT_CB8, n, k, 1, synth.DT_BF16, seed=0)
 
 
 def test_cb8_unit_vector_returns_codebook_entry_exactly(qmv):

@@ -67,13 +67,13 @@ def run_moe(qmv, n_experts, dm, dff, ids, seed, rows_h=None, rows_y=None, expect
             continue
         gm = oracle.Mat(oracle.CB4, dff, dm, gh[e])
         um = oracle.Mat(oracle.CB4, dff, dm, uh[e])
-        hr, g, u, bg, bu = oracle.moe_gateup(gm, um, x, oracle.BF16, rows=rows_h, nthreads=8)
+        hr, g, u, bg, bu = oracle.moe_gateup(gm, um, x, oracle.BF16, rows=rows_h, nthreads=oracle.max_threads())
         hj = h[j] if rows_h is None else h[j][rows_h]
         err = np.abs(hj - hr)
         lim = h_bound(g, u, bg, bu)
         assert np.all(np.isfinite(hj)) and np.all(err <= lim), (j, e, float(np.max(err / lim)))
         dmat = oracle.Mat(oracle.CB4, dm, dff, dh[e])
-        yr, by = oracle.gemv(dmat, h[j][None, :].astype(np.float32), oracle.F32, rows=rows_y, nthreads=8)
+        yr, by = oracle.gemv(dmat, h[j][None, :].astype(np.float32), oracle.F32, rows=rows_y, nthreads=oracle.max_threads())
         yj = y[j] if rows_y is None else y[j][rows_y]
         assert_parity(yj[None, :], yr, by, f"down expert {e}")
 
@@ -95,8 +95,6 @@ def test_moe_ragged_sizes(qmv, monkeypatch, force):
 
 def test_moe_deepseek_like_layer_top8_of_256(qmv):
     # 256 experts of gate/up 2048 x 7168 and down 7168 x 2048; top-8 ids for token 0
+    # (every row of h and y of each routed expert is checked)
     ids = synth.gen_moe_ids(1, 256, 8, seed=0)[0]
-    rng = np.random.default_rng(0)
-    rows_h = np.sort(rng.choice(2048, 96, replace=False))
-    rows_y = np.sort(rng.choice(7168, 96, replace=False))
-    run_moe(qmv, n_experts=256, dm=7168, dff=2048, ids=ids, seed=0, rows_h=rows_h, rows_y=rows_y)
+    run_moe(qmv, n_experts=256, dm=7168, dff=2048, ids=ids, seed=0)
