@@ -7,18 +7,25 @@ Inputs are seeded synthetic planes, uploaded before timing; every step reads a
 different copy from a rotating pool of >= 1 GiB so that the 256 MB Infinity Cache
 cannot serve repeated reads (the weights come from HBM, as in decode).
 
-Prints ONE JSON line: value = algorithmic bytes (packed weights + scales + x + y)
-per step / time per step, in GB/s.  `roofline` covers the dominant kernel, timed
-with HIP events on the stream it runs on; `cpu_baseline` times the CPU oracle on
-a bounded sample of the same workload.  `secondary` carries the other workloads
-(q6_K GEMV, 4-bit codebook MoE, 2-bit and 3-bit additive GEMVs, 8-bit codebook GEMV,
-q6_K prefill GEMM) when they run.
+Protocol: every workload is set up first; then `--repeats` rounds each measure every
+workload once, in the same order (interleaved), and each figure is the median over
+the rounds.  Times come from HIP events recorded on the stream the kernels run on,
+around replays of HIP graphs that hold the launches.
+
+Output: one short progress line per workload while it runs, the full record written to
+`--out` (JSON), and as the LAST stdout line a compact JSON record (value = algorithmic
+bytes per step / time per step, in GB/s) with `roofline` for the dominant kernel,
+`cpu_baseline` (the CPU oracle on a bounded sample, one thread and all threads, plus a
+prefill-GEMM leg), the path-label census of every timed launch, and a summary of the
+other workloads (q6_K GEMVs, 4-bit codebook MoE, 2-/3-bit additive GEMVs, 8-bit codebook
+GEMV, q6_K prefill GEMM).
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -32,8 +39,12 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
 POOL_BYTES = 1 << 30           # rotating pool: 4x the 256 MB Infinity Cache
+LLAMA = [(4096, 4096), (11008, 4096), (4096, 11008)]
+EXPERT = [(2048, 7168), (7168, 2048)]
+AQ_SHAPES = [(14336, 4096), (4096, 14336)]
 
 METRIC = "quantized GEMV HBM GB/s (% of peak); q6_K prefill GEMM int8 TOPS (% of peak)"
+DEFAULT_SECONDARY = "q6_K_gemv,q6_K_decode,q4_0_batch,batch4_other,batch8_other,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm"
 
 
 def parse():
@@ -41,15 +52,94 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--repeats", type=int, default=3, help="interleaved rounds; figures are medians")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="per CPU leg")
     ap.add_argument("--only-primary", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--secondary", default="q6_K_gemv,q6_K_decode,q4_0_batch,q4_0_q8,batch4_other,batch8_other,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm",
-                    help="comma-separated secondary workloads to run")
+    ap.add_argument("--secondary", default=DEFAULT_SECONDARY,
+                    help="comma-separated secondary workloads (also: q4_0_q8)")
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "bench_full.json"),
+                    help="where the full record is written")
     return ap.parse_args()
 
+
+def say(msg: str):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ graphs and census
+
+class Census:
+    """Path labels of every timed launch: each captured library call records the label the
+    library reports for it, and every replay of a graph counts its labels again."""
+
+    def __init__(self):
+        self.counts: dict[str, int] = {}
+        self.capturing: list | None = None
+
+    def note(self, qmv):
+        if self.capturing is not None:
+            self.capturing.append(qmv.last_path())
+
+    def add(self, labels, times=1):
+        for lab in labels:
+            self.counts[lab] = self.counts.get(lab, 0) + times
+
+    def summary(self):
+        fb = sum(c for lab, c in self.counts.items() if "fallback" in lab)
+        return {"launches": sum(self.counts.values()), "labels": len(self.counts), "fallback": fb}
+
+
+CENSUS = Census()
+
+
+class Graph:
+    """A HIP graph (torch.cuda.CUDAGraph) replaying fn(0) .. fn(count-1) back to back, with
+    the path labels of the launches it holds.  The library enqueues plain kernel launches on
+    the current stream, so stream capture records them; replays remove Python's per-launch
+    host overhead."""
+
+    def __init__(self, qmv, fn, count):
+        import torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(min(count, 3)):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        self.count = count
+        CENSUS.capturing = []
+        with torch.cuda.graph(self.g):
+            for i in range(count):
+                fn(i)
+        self.labels, CENSUS.capturing = CENSUS.capturing, None
+        torch.cuda.synchronize()
+
+    def time(self, warm=True):
+        """Milliseconds per item of one replay (HIP events on the replay stream)."""
+        import torch
+        if warm:
+            self.g.replay()
+            CENSUS.add(self.labels)
+            torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        self.g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        CENSUS.add(self.labels)
+        return s.elapsed_time(e) / self.count
+
+
+def med(v):
+    return statistics.median(v)
+
+
+# ------------------------------------------------------------------ inputs
 
 def dev_planes(planes: dict):
     import torch
@@ -67,299 +157,299 @@ def make_pool(qmv, fmt, n, k, seed, copies):
     """`copies` distinct device copies of one generated matrix: each plane is one
     [copies, ...] tensor filled by device-side copies, and copy c is its slice c."""
     import torch
-    host = synth.gen_weights(fmt, n, k, seed=seed)
-    first = dev_planes(host)
+    first = dev_planes(synth.gen_weights(fmt, n, k, seed=seed))
     big = {name: torch.empty((copies, *t.shape), dtype=t.dtype, device="cuda") for name, t in first.items()}
     for name, t in first.items():
         big[name][:] = t
     pool = [qmv.QWeights(fmt, n, k, {name: big[name][c] for name in big}) for c in range(copies)]
     pool[0]._keep = big
-    return host, pool
+    return pool
 
 
 def pool_copies(bytes_per_copy):
     return max(2, -(-POOL_BYTES // bytes_per_copy))
 
 
-def graph_of(fn, count):
-    """A HIP graph (torch.cuda.CUDAGraph) that replays fn(0) .. fn(count-1) back to back.
-
-    The library enqueues plain kernel launches on the current stream, so stream capture
-    records them; replaying the graph removes the per-launch host overhead of Python."""
+def x_dev(batch, k, xt, seed):
     import torch
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for i in range(min(count, 3)):
-            fn(i)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(count):
-            fn(i)
-    torch.cuda.synchronize()
-    return g
+    x = synth.gen_x(batch, k, xt, seed=seed)
+    if xt == synth.DT_F32:
+        return torch.from_numpy(x).cuda()
+    return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).cuda()
 
 
-def time_graph(g, count):
-    """Milliseconds per item of one replay of graph g holding `count` items (HIP events
-    recorded on the stream the graph replays on)."""
-    import torch
-    g.replay()
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    g.replay()
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / count
+_POOLS = {}
 
 
-def q4_0_workload(qmv, steps, warmup):
-    import torch
-    shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]
-    per_set = sum(qmv.weight_bytes(synth.FMT_Q4_0, n, k) for n, k in shapes)
-    copies = max(2, -(-POOL_BYTES // per_set))
-    mats, xs, ys, algo = [], [], [], []
-    for i, (n, k) in enumerate(shapes):
-        _, pool = make_pool(qmv, synth.FMT_Q4_0, n, k, seed=i, copies=copies)
-        mats.append(pool)
-        xs.append(torch.from_numpy(synth.gen_x(1, k, seed=i)).cuda())
-        ys.append(torch.empty((1, n), dtype=torch.float32, device="cuda"))
-        algo.append(qmv.weight_bytes(synth.FMT_Q4_0, n, k) + 4 * k + 4 * n)
-
-    def step(i):
-        c = i % copies
-        for s in range(len(shapes)):
-            qmv.gemv(mats[s][c], xs[s], ys[s])
-
-    # warm-up steps, then exactly `steps` timed steps, each set captured in one graph
-    gw = graph_of(lambda i: step(i + 1000), max(1, warmup))
-    gt = graph_of(step, steps)
-    gw.replay()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    gt.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    bytes_step = sum(algo)
-    per_shape = []
-    for s, (n, k) in enumerate(shapes):
-        R = max(steps, 60)
-        g = graph_of(lambda i, s=s: qmv.gemv(mats[s][i % copies], xs[s], ys[s]), R)
-        avg = time_graph(g, R)
-        # contrast only: the same launches on one copy, which stays in the Infinity Cache
-        warm = time_graph(graph_of(lambda i, s=s: qmv.gemv(mats[s][0], xs[s], ys[s]), R), R)
-        qmv.gemv(mats[s][0], xs[s], ys[s])
-        per_shape.append({"shape": f"{n}x{k}", "bytes": algo[s], "avg_launch_ms": avg,
-                          "GBps": algo[s] / avg / 1e6, "frac": algo[s] / avg / 1e6 / HBM_PEAK_GBS,
-                          "warm_one_copy_GBps": round(algo[s] / warm / 1e6, 1),
-                          "path": qmv.last_path()})
-    torch.cuda.synchronize()
-    return {"ms_per_step": ms, "bytes_per_step": bytes_step, "GBps": bytes_step / ms / 1e6,
-            "copies": copies, "pool_bytes": copies * per_set, "shapes": per_shape}
+def shared_pool(qmv, fmt, shapes):
+    """One rotating pool per (format, shapes), shared by the workloads (batch sizes) over it."""
+    key = (fmt, tuple(shapes))
+    if key not in _POOLS:
+        per_set = sum(qmv.weight_bytes(fmt, n, k) for n, k in shapes)
+        copies = pool_copies(per_set)
+        _POOLS[key] = (copies, [make_pool(qmv, fmt, n, k, seed=i, copies=copies) for i, (n, k) in enumerate(shapes)])
+    return _POOLS[key]
 
 
-def read_ceiling(qmv, sizes, steps, large=True):
-    """The stream-read ceiling: the library's read-only kernel over a rotating pool of
-    distinct buffers of each size (cold, as the GEMVs' pools), and once over 4 GiB."""
-    import torch
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    out = []
-    for b in sizes:
-        b16 = (b + 15) // 16 * 16
-        copies = pool_copies(b16)
-        pool = torch.zeros((copies, b16), dtype=torch.uint8, device="cuda")
-        R = max(steps, 60)
-        avg = time_graph(graph_of(lambda i: qmv.read_ceiling(pool[i % copies], sink), R), R)
-        out.append({"bytes": b16, "avg_launch_ms": round(avg, 5), "GBps": round(b16 / avg / 1e6, 1)})
-        del pool
-    if not large:
-        return {"kernel": "read_ceiling_kernel (128-bit nontemporal loads only)", "sizes": out}
-    big = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
-    avg = time_graph(graph_of(lambda i: qmv.read_ceiling(big, sink), 5), 5)
-    large = {"bytes": big.numel(), "avg_launch_ms": round(avg, 4), "GBps": round(big.numel() / avg / 1e6, 1)}
-    del big
-    torch.cuda.synchronize()
-    return {"kernel": "read_ceiling_kernel (128-bit nontemporal loads only)", "sizes": out, "large": large}
+class ReadCeiling:
+    """The stream-read ceiling: the library's read-only kernel over distinct regions of one
+    2 GiB buffer (cold, as the GEMV pools), for a given byte count."""
+
+    def __init__(self, qmv):
+        import torch
+        self.qmv = qmv
+        self.buf = torch.zeros(2 << 30, dtype=torch.uint8, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.graphs = {}
+
+    def graph(self, nbytes, count=60):
+        b16 = (nbytes + 15) // 16 * 16
+        if b16 not in self.graphs:
+            copies = max(2, self.buf.numel() // b16)
+            q = self.qmv
+
+            def fn(i):
+                q.read_ceiling(self.buf[(i % copies) * b16:(i % copies + 1) * b16], self.sink)
+                CENSUS.note(q)
+            self.graphs[b16] = Graph(q, fn, count)
+        return self.graphs[b16]
+
+    def ms(self, nbytes):
+        return self.graph(nbytes).time()
 
 
-def gemv_workload(qmv, fmt, shapes, batch, xt, steps, label):
-    """Batch-`batch` GEMVs over `shapes` (one step = one GEMV per shape), rotating pool."""
-    import torch
-    per_set = sum(qmv.weight_bytes(fmt, n, k) for n, k in shapes)
-    copies = pool_copies(per_set)
-    mats, xs, ys, algo = [], [], [], []
-    xbytes = 4 if xt == synth.DT_F32 else 2
-    for i, (n, k) in enumerate(shapes):
-        _, pool = make_pool(qmv, fmt, n, k, seed=i, copies=copies)
-        mats.append(pool)
-        x = synth.gen_x(batch, k, xt, seed=i)
-        xd = torch.from_numpy(x).cuda() if xt == synth.DT_F32 else \
-            torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).cuda()
-        xs.append(xd)
-        ys.append(torch.empty((batch, n), dtype=torch.float32, device="cuda"))
-        algo.append(qmv.weight_bytes(fmt, n, k) + xbytes * batch * k + 4 * batch * n)
+# ------------------------------------------------------------------ workloads
 
-    def step(i):
-        for s in range(len(shapes)):
-            qmv.gemv(mats[s][i % copies], xs[s], ys[s])
+class GemvWorkload:
+    """Batch-`batch` GEMVs over `shapes` (one step = one GEMV per shape), rotating pool;
+    per shape, the launch time over the cold pool and the read ceiling for its bytes."""
 
-    g = graph_of(step, steps)
-    ms = time_graph(g, steps)
-    per_shape = []
-    for s, (n, k) in enumerate(shapes):
+    def __init__(self, qmv, name, label, fmt, shapes, batch, xt, steps, ceiling, warm_contrast=False):
+        import torch
+        self.qmv, self.name, self.label, self.shapes, self.batch = qmv, name, label, shapes, batch
+        copies, mats = shared_pool(qmv, fmt, shapes)
+        self.copies = copies
+        xb = 4 if xt == synth.DT_F32 else 2
+        self.xs = [x_dev(batch, k, xt, seed=i) for i, (n, k) in enumerate(shapes)]
+        self.ys = [torch.empty((batch, n), dtype=torch.float32, device="cuda") for n, k in shapes]
+        self.algo = [qmv.weight_bytes(fmt, n, k) + xb * batch * k + 4 * batch * n for n, k in shapes]
+        self.ceiling = ceiling
+        q = qmv
+
+        def step(i):
+            for s in range(len(shapes)):
+                q.gemv(mats[s][i % copies], self.xs[s], self.ys[s])
+                CENSUS.note(q)
+        self.step_graph = Graph(qmv, step, steps)
         R = max(steps, 40)
-        avg = time_graph(graph_of(lambda i, s=s: qmv.gemv(mats[s][i % copies], xs[s], ys[s]), R), R)
-        qmv.gemv(mats[s][0], xs[s], ys[s])
-        per_shape.append({"shape": f"{n}x{k}", "bytes": algo[s], "avg_launch_ms": round(avg, 5),
-                          "GBps": round(algo[s] / avg / 1e6, 1), "path": qmv.last_path()})
-    path = qmv.last_path()
-    add_ceiling(qmv, per_shape, steps)
-    gbs = sum(algo) / ms / 1e6
-    return {"workload": label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "ms_per_step": round(ms, 5), "bytes_per_step": sum(algo), "pool_copies": copies,
-            "path": path, "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
-            "shapes": per_shape}
-
-
-def q8_workload(qmv, fmt, batch, steps, label):
-    """The GEMV over per-32 int8 activations (q4_0 or q6_K) on the three decode shapes (one
-    step = one GEMV per shape, activations quantized beforehand, as they are once per
-    activation vector for every GEMV that reads it).  The same step with one quantizer
-    launch in front of each GEMV is timed too and reported beside it."""
-    import torch
-    shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]
-    per_set = sum(qmv.weight_bytes(fmt, n, k) for n, k in shapes)
-    copies = pool_copies(per_set)
-    mats, xs, qs, ys, algo = [], [], [], [], []
-    for i, (n, k) in enumerate(shapes):
-        _, pool = make_pool(qmv, fmt, n, k, seed=i, copies=copies)
-        mats.append(pool)
-        x = torch.from_numpy(synth.gen_x(batch, k, synth.DT_F32, seed=i)).cuda()
-        xs.append(x)
-        qs.append(qmv.quant_act(x))
-        ys.append(torch.empty((batch, n), dtype=torch.float32, device="cuda"))
-        # weights + int8 activations and their scales + outputs
-        algo.append(qmv.weight_bytes(fmt, n, k) + batch * (k + k // 8) + 4 * batch * n)
-
-    def step(i):
+        self.shape_graphs, self.warm_graphs = [], []
         for s in range(len(shapes)):
-            qmv.gemv_q8(mats[s][i % copies], qs[s][0], qs[s][1], ys[s])
+            def one(i, s=s):
+                q.gemv(mats[s][i % copies], self.xs[s], self.ys[s])
+                CENSUS.note(q)
+            self.shape_graphs.append(Graph(qmv, one, R))
+            if warm_contrast:  # the same launches on one copy, which stays in the Infinity Cache
+                def warm(i, s=s):
+                    q.gemv(mats[s][0], self.xs[s], self.ys[s])
+                    CENSUS.note(q)
+                self.warm_graphs.append(Graph(qmv, warm, R))
+        self.paths = [g.labels[-1] for g in self.shape_graphs]
+        self.runs = {"step": [], "shape": [[] for _ in shapes], "warm": [[] for _ in shapes],
+                     "ceil": [[] for _ in shapes]}
 
-    def step_quant(i):
-        for s in range(len(shapes)):
-            qmv.quant_act(xs[s], qs[s][0], qs[s][1])
-            qmv.gemv_q8(mats[s][i % copies], qs[s][0], qs[s][1], ys[s])
+    def measure(self):
+        self.runs["step"].append(self.step_graph.time())
+        for s in range(len(self.shapes)):
+            self.runs["shape"][s].append(self.shape_graphs[s].time())
+            if self.warm_graphs:
+                self.runs["warm"][s].append(self.warm_graphs[s].time())
+            if self.ceiling is not None:
+                self.runs["ceil"][s].append(self.ceiling.ms(self.algo[s]))
 
-    ms = time_graph(graph_of(step, steps), steps)
-    ms_q = time_graph(graph_of(step_quant, steps), steps)
-    per_shape = []
-    for s, (n, k) in enumerate(shapes):
-        R = max(steps, 40)
-        avg = time_graph(graph_of(lambda i, s=s: qmv.gemv_q8(mats[s][i % copies], qs[s][0], qs[s][1], ys[s]), R), R)
-        qmv.gemv_q8(mats[s][0], qs[s][0], qs[s][1], ys[s])
-        per_shape.append({"shape": f"{n}x{k}", "bytes": algo[s], "avg_launch_ms": round(avg, 5),
-                          "GBps": round(algo[s] / avg / 1e6, 1), "path": qmv.last_path()})
-    path = qmv.last_path()
-    add_ceiling(qmv, per_shape, steps)
-    gbs = sum(algo) / ms / 1e6
-    return {"workload": label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "ms_per_step": round(ms, 5), "bytes_per_step": sum(algo), "pool_copies": copies,
-            "with_quant_act": {"ms_per_step": round(ms_q, 5), "GBps": round(sum(algo) / ms_q / 1e6, 1)},
-            "path": path, "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
-            "shapes": per_shape}
+    def result(self):
+        ms = med(self.runs["step"])
+        gbs = sum(self.algo) / ms / 1e6
+        shapes = []
+        for s, (n, k) in enumerate(self.shapes):
+            avg = med(self.runs["shape"][s])
+            sh = {"shape": f"{n}x{k}", "bytes": self.algo[s], "avg_launch_ms": round(avg, 5),
+                  "runs_ms": [round(v, 5) for v in self.runs["shape"][s]],
+                  "GBps": round(self.algo[s] / avg / 1e6, 1), "frac": round(self.algo[s] / avg / 1e6 / HBM_PEAK_GBS, 4),
+                  "path": self.paths[s]}
+            if self.warm_graphs:
+                sh["warm_one_copy_GBps"] = round(self.algo[s] / med(self.runs["warm"][s]) / 1e6, 1)
+            if self.runs["ceil"][s]:
+                c = med(self.runs["ceil"][s])
+                sh["read_ceiling_ms"] = round(c, 5)
+                sh["frac_of_read_ceiling"] = round(c / avg, 4)
+            shapes.append(sh)
+        return {"workload": self.label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "ms_per_step": round(ms, 5), "step_runs_ms": [round(v, 5) for v in self.runs["step"]],
+                "bytes_per_step": sum(self.algo), "pool_copies": self.copies, "batch": self.batch,
+                "path": self.paths[-1], "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+                "shapes": shapes}
+
+    def brief(self):
+        r = self.result()
+        return [r["value"], r["frac_of_peak"]]
 
 
-def add_ceiling(qmv, per_shape, steps):
-    """Per shape: the stream-read ceiling for its bytes and the kernel's fraction of it."""
-    rc = read_ceiling(qmv, [sh["bytes"] for sh in per_shape], steps, large=False)
-    for sh, c in zip(per_shape, rc["sizes"]):
-        sh["read_ceiling_ms"] = c["avg_launch_ms"]
-        sh["frac_of_read_ceiling"] = round(c["avg_launch_ms"] / sh["avg_launch_ms"], 4)
+class Q8Workload(GemvWorkload):
+    """The GEMV over per-32 int8 activations (q4_0 or q6_K) on the three decode shapes,
+    activations quantized beforehand (once per activation vector for every GEMV that reads it)."""
+
+    def __init__(self, qmv, name, label, fmt, batch, steps, ceiling):
+        import torch
+        self.qmv, self.name, self.label, self.shapes, self.batch = qmv, name, label, LLAMA, batch
+        copies, mats = shared_pool(qmv, fmt, LLAMA)
+        self.copies = copies
+        self.qs = [qmv.quant_act(x_dev(batch, k, synth.DT_F32, seed=i)) for i, (n, k) in enumerate(LLAMA)]
+        self.ys = [torch.empty((batch, n), dtype=torch.float32, device="cuda") for n, k in LLAMA]
+        self.algo = [qmv.weight_bytes(fmt, n, k) + batch * (k + k // 8) + 4 * batch * n for n, k in LLAMA]
+        self.ceiling, self.warm_graphs = ceiling, []
+        q = qmv
+
+        def step(i):
+            for s in range(len(LLAMA)):
+                q.gemv_q8(mats[s][i % copies], self.qs[s][0], self.qs[s][1], self.ys[s])
+                CENSUS.note(q)
+        self.step_graph = Graph(qmv, step, steps)
+        self.shape_graphs = []
+        for s in range(len(LLAMA)):
+            def one(i, s=s):
+                q.gemv_q8(mats[s][i % copies], self.qs[s][0], self.qs[s][1], self.ys[s])
+                CENSUS.note(q)
+            self.shape_graphs.append(Graph(qmv, one, max(steps, 40)))
+        self.paths = [g.labels[-1] for g in self.shape_graphs]
+        self.runs = {"step": [], "shape": [[] for _ in LLAMA], "warm": [[] for _ in LLAMA], "ceil": [[] for _ in LLAMA]}
 
 
-def moe_workload(qmv, tokens, label):
+class MoeWorkload:
     """Routed-expert FFN, batch 1: 256 experts of gate/up 2048x7168 and down 7168x2048
-    (4-bit codebook, one 16-entry fp16 codebook per 128 weights), top-8 per token.
-    The 8.46 GB expert set is resident; its bytes are drawn on the device with a seeded
+    (4-bit codebook, one 16-entry fp16 codebook per 128 weights), top-8 per token.  The
+    8.46 GB expert set is resident; its bytes are drawn on the device with a seeded
     generator (throughput does not depend on the values; parity is tested elsewhere)."""
-    import torch
-    E, dm, dff = 256, 7168, 2048
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(0)
 
-    def planes(n, k):
-        idx = torch.randint(0, 256, (E, n, k // 2), dtype=torch.uint8, device="cuda", generator=gen)
-        cb = torch.randn((E, n, k // 128, 16), device="cuda", generator=gen) * 0.02
-        cb = torch.sort(cb, dim=-1).values.to(torch.float16)
-        return {"idx": idx, "cb": cb}
+    def __init__(self, qmv, tokens):
+        import torch
+        E, dm, dff = 256, 7168, 2048
+        self.name, self.tokens = "cb4_moe", tokens
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(0)
 
-    G = qmv.QWeights(qmv.CB4, dff, dm, planes(dff, dm))
-    U = qmv.QWeights(qmv.CB4, dff, dm, planes(dff, dm))
-    D = qmv.QWeights(qmv.CB4, dm, dff, planes(dm, dff))
-    ids = torch.from_numpy(synth.gen_moe_ids(tokens, E, 8, seed=0)).cuda()
-    x = torch.from_numpy(synth.gen_x(tokens, dm, synth.DT_BF16, seed=0).view(np.int16).copy()).view(torch.bfloat16).cuda()
-    h = torch.empty((8, dff), dtype=torch.float32, device="cuda")
-    y = torch.empty((8, dm), dtype=torch.float32, device="cuda")
-    per_tok = 8 * (qmv.weight_bytes(qmv.CB4, dff, dm) * 2 + qmv.weight_bytes(qmv.CB4, dm, dff)) + 2 * dm + \
-        8 * dff * 4 * 2 + 8 * dm * 4
+        def planes(n, k):
+            idx = torch.randint(0, 256, (E, n, k // 2), dtype=torch.uint8, device="cuda", generator=gen)
+            cb = torch.randn((E, n, k // 128, 16), device="cuda", generator=gen) * 0.02
+            return {"idx": idx, "cb": torch.sort(cb, dim=-1).values.to(torch.float16)}
 
-    def step(i):
-        qmv.moe_ffn(G, U, D, E, ids[i % tokens], x[i % tokens], h, y)
+        self.W = [qmv.QWeights(qmv.CB4, dff, dm, planes(dff, dm)), qmv.QWeights(qmv.CB4, dff, dm, planes(dff, dm)),
+                  qmv.QWeights(qmv.CB4, dm, dff, planes(dm, dff))]
+        ids = torch.from_numpy(synth.gen_moe_ids(tokens, E, 8, seed=0)).cuda()
+        x = torch.from_numpy(synth.gen_x(tokens, dm, synth.DT_BF16, seed=0).view(np.int16).copy()).view(torch.bfloat16).cuda()
+        h = torch.empty((8, dff), dtype=torch.float32, device="cuda")
+        y = torch.empty((8, dm), dtype=torch.float32, device="cuda")
+        self.per_tok = 8 * (qmv.weight_bytes(qmv.CB4, dff, dm) * 2 + qmv.weight_bytes(qmv.CB4, dm, dff)) + 2 * dm + \
+            8 * dff * 4 * 2 + 8 * dm * 4
+        q, G, U, D = qmv, *self.W
 
-    g = graph_of(step, tokens)
-    ms = time_graph(g, tokens)
-    gbs = per_tok / ms / 1e6
-    return {"workload": label, "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "ms_per_token": round(ms, 5), "bytes_per_token": per_tok, "tokens": tokens,
-            "path": qmv.last_path(), "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"}}
+        def step(i):
+            q.moe_ffn(G, U, D, E, ids[i % tokens], x[i % tokens], h, y)
+            CENSUS.note(q)
+        self.g = Graph(qmv, step, tokens)
+        self.runs = []
+
+    def measure(self):
+        self.runs.append(self.g.time())
+
+    def result(self):
+        ms = med(self.runs)
+        gbs = self.per_tok / ms / 1e6
+        return {"workload": "4-bit codebook MoE FFN, batch 1, 256 experts top-8, gate/up 2048x7168 + down 7168x2048, bf16 x",
+                "value": round(gbs, 1), "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "ms_per_token": round(ms, 5), "runs_ms": [round(v, 5) for v in self.runs],
+                "bytes_per_token": self.per_tok, "tokens": self.tokens, "path": self.g.labels[-1],
+                "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"}}
+
+    def brief(self):
+        r = self.result()
+        return [r["value"], r["frac_of_peak"]]
 
 
-def gemm_workload(qmv, steps, label):
+class GemmWorkload:
     """q6_K prefill GEMM, M = 512 tokens, W 11008x4096 and 4096x11008: TOPS = 2 M N K / time
-    for the int8 contraction alone (activations already quantized) and end to end.  The
-    weights are registered with their pre-expanded planes (the default-on registration the
-    method describes), and the in-kernel expansion of the same calls is timed beside it."""
-    import torch
-    M = 512
-    out = {"workload": label, "unit": "TOPS", "shapes": []}
-    tot_ops, tot_ms, tot_ms_e2e, tot_ms_raw = 0, 0.0, 0.0, 0.0
-    for i, (n, k) in enumerate([(11008, 4096), (4096, 11008)]):
-        _, pool = make_pool(qmv, synth.FMT_Q6_K, n, k, seed=i, copies=4)
-        x = torch.from_numpy(synth.gen_x(M, k, seed=i)).cuda()
-        xq, xs = qmv.quant_act(x)
-        y = torch.empty((M, n), dtype=torch.float32, device="cuda")
-        ws = torch.empty(qmv.workspace_bytes(pool[0], M), dtype=torch.uint8, device="cuda")
-        R = max(8, steps // 4)
-        ms_raw = time_graph(graph_of(lambda j: qmv.gemm_q8(pool[j % 4], xq, xs, y), R), R)
-        path_raw = qmv.last_path()
-        for W in pool:
-            qmv.register_plane(W)
-        ms = time_graph(graph_of(lambda j: qmv.gemm_q8(pool[j % 4], xq, xs, y), R), R)
-        path = qmv.last_path()
-        ms2 = time_graph(graph_of(lambda j: qmv.gemm(pool[j % 4], x, y, ws), R), R)
-        for W in pool:
-            qmv.unregister_plane(W)
-        ops = 2 * M * n * k
-        tot_ops += ops
-        tot_ms += ms
-        tot_ms_e2e += ms2
-        tot_ms_raw += ms_raw
-        out["shapes"].append({"shape": f"{n}x{k}", "M": M, "ms": round(ms, 5), "TOPS": round(ops / ms / 1e9, 1),
-                              "ms_with_quantizer": round(ms2, 5), "path": path,
-                              "ms_in_kernel_expand": round(ms_raw, 5),
-                              "TOPS_in_kernel_expand": round(ops / ms_raw / 1e9, 1), "path_in_kernel_expand": path_raw})
-    tops = tot_ops / tot_ms / 1e9
-    out.update({"value": round(tops, 1), "frac_of_peak": round(tops / INT8_PEAK_TOPS, 4),
-                "TOPS_with_quantizer": round(tot_ops / tot_ms_e2e / 1e9, 1),
-                "TOPS_in_kernel_expand": round(tot_ops / tot_ms_raw / 1e9, 1),
-                "roofline": {"bound": "mfma", "peak": INT8_PEAK_TOPS, "unit": "TOPS"}})
-    return out
+    for the int8 contraction alone (activations already quantized) with registered
+    pre-expanded planes (the default-on registration the method describes), end to end
+    with the quantizer, and with the in-kernel expansion (no plane)."""
 
+    def __init__(self, qmv, steps):
+        import torch
+        self.name, M = "q6_K_gemm", 512
+        self.M = M
+        self.shapes = [(11008, 4096), (4096, 11008)]
+        self.g, self.ops = [], []
+        self.keep = []
+        q = qmv
+        R = max(8, steps // 4)
+        for i, (n, k) in enumerate(self.shapes):
+            raw = make_pool(qmv, synth.FMT_Q6_K, n, k, seed=i, copies=4)
+            exp = make_pool(qmv, synth.FMT_Q6_K, n, k, seed=i, copies=4)
+            for W in exp:
+                qmv.register_plane(W)
+            x = x_dev(M, k, synth.DT_F32, seed=i)
+            xq, xs = qmv.quant_act(x)
+            y = torch.empty((M, n), dtype=torch.float32, device="cuda")
+            ws = torch.empty(qmv.workspace_bytes(raw[0], M), dtype=torch.uint8, device="cuda")
+            self.keep += [raw, exp, x, xq, xs, y, ws]
+
+            def plane(j, exp=exp, xq=xq, xs=xs, y=y):
+                q.gemm_q8(exp[j % 4], xq, xs, y)
+                CENSUS.note(q)
+
+            def e2e(j, exp=exp, x=x, y=y, ws=ws):
+                q.gemm(exp[j % 4], x, y, ws)
+                CENSUS.note(q)
+
+            def inkernel(j, raw=raw, xq=xq, xs=xs, y=y):
+                q.gemm_q8(raw[j % 4], xq, xs, y)
+                CENSUS.note(q)
+            self.g.append((Graph(qmv, plane, R), Graph(qmv, e2e, R), Graph(qmv, inkernel, R)))
+            self.ops.append(2 * M * n * k)
+        self.runs = [[[], [], []] for _ in self.shapes]
+
+    def measure(self):
+        for s, gs in enumerate(self.g):
+            for j, g in enumerate(gs):
+                self.runs[s][j].append(g.time())
+
+    def result(self):
+        out = {"workload": "q6_K prefill GEMM, M=512, 11008x4096 + 4096x11008", "unit": "TOPS", "shapes": []}
+        tot = [0.0, 0.0, 0.0]
+        for s, (n, k) in enumerate(self.shapes):
+            ms = [med(r) for r in self.runs[s]]
+            for j in range(3):
+                tot[j] += ms[j]
+            ops = self.ops[s]
+            out["shapes"].append({"shape": f"{n}x{k}", "M": self.M, "ms": round(ms[0], 5), "TOPS": round(ops / ms[0] / 1e9, 1),
+                                  "runs_ms": [round(v, 5) for v in self.runs[s][0]],
+                                  "path": self.g[s][0].labels[-1], "ms_with_quantizer": round(ms[1], 5),
+                                  "ms_in_kernel_expand": round(ms[2], 5),
+                                  "TOPS_in_kernel_expand": round(ops / ms[2] / 1e9, 1),
+                                  "path_in_kernel_expand": self.g[s][2].labels[-1]})
+        ops = sum(self.ops)
+        tops = ops / tot[0] / 1e9
+        out.update({"value": round(tops, 1), "frac_of_peak": round(tops / INT8_PEAK_TOPS, 4),
+                    "TOPS_with_quantizer": round(ops / tot[1] / 1e9, 1),
+                    "TOPS_in_kernel_expand": round(ops / tot[2] / 1e9, 1),
+                    "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                                 "frac": round(tops / INT8_PEAK_TOPS, 4)}})
+        return out
+
+    def brief(self):
+        r = self.result()
+        return [r["value"], r["frac_of_peak"], r["TOPS_with_quantizer"], r["TOPS_in_kernel_expand"]]
+
+
+# ------------------------------------------------------------------ CPU baseline
 
 def recorded_traffic():
     """HBM bytes per launch of the dominant kernel from the committed PMC record, or None
@@ -374,28 +464,70 @@ def recorded_traffic():
     return rec["traffic_bytes_per_launch"] if h == rec["sources_sha256"] else None
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(seconds):
-    """The oracle on the same three matrices (all rows), repeated until `seconds` of work."""
+    """The oracle as it stands on the host cores: the q4_0 decode step (all rows of the three
+    matrices, repeated for about `seconds`) on one thread and on all threads, and the q6_K
+    prefill GEMM (quantizer over all 512 x 4096 activations, then a bounded sample of
+    (token, row) outputs of the 11008 x 4096 product) on all threads."""
     import oracle
-    nth = max(1, min(16, os.cpu_count() or 1))
-    shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]
+    nth = oracle.max_threads()
     mats, xs, nbytes = [], [], 0
-    for i, (n, k) in enumerate(shapes):
+    for i, (n, k) in enumerate(LLAMA):
         mats.append(oracle.Mat(synth.FMT_Q4_0, n, k, synth.gen_weights(synth.FMT_Q4_0, n, k, seed=i)))
         xs.append(synth.gen_x(1, k, seed=i))
         nbytes += (n * k // 32) * 18 + 4 * k + 4 * n
-    done, t0 = 0, time.perf_counter()
-    while True:
-        for m, x in zip(mats, xs):
-            oracle.gemv(m, x, oracle.F32, nthreads=nth)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": nbytes * done / el / 1e9, "unit": "GB/s", "cores": nth, "kind": "oracle",
-            "sample": f"{done} full pass(es) of the three q4_0 GEMVs (all rows), fp64 oracle, "
-                      f"{el:.1f} s, OpenMP over rows"}
 
+    def leg(threads):
+        done, t0 = 0, time.perf_counter()
+        while True:
+            for m, x in zip(mats, xs):
+                oracle.gemv(m, x, oracle.F32, nthreads=threads)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return nbytes * done / el / 1e9, done, el
+
+    v_all, d_all, e_all = leg(nth)
+    v_one, d_one, e_one = leg(1)
+    # prefill GEMM leg: TOPS over the sampled outputs (2 K int ops each), quantizer included
+    n, k, M = 11008, 4096, 512
+    gm = oracle.Mat(synth.FMT_Q6_K, n, k, synth.gen_weights(synth.FMT_Q6_K, n, k, seed=0))
+    x = synth.gen_x(M, k, seed=0)
+    t0 = time.perf_counter()
+    xq, xsc = oracle.quant_act(x)
+    tq = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    pairs, tg = 0, 0.0
+    while tg < seconds:
+        mm = rng.integers(0, M, 8192)
+        nn = rng.integers(0, n, 8192)
+        t0 = time.perf_counter()
+        oracle.q6k_gemm_pairs(gm, xq, xsc, mm, nn, nthreads=nth)
+        tg += time.perf_counter() - t0
+        pairs += len(mm)
+    gemm_tops = 2 * k * pairs / tg / 1e12
+    return {"value": round(v_all, 3), "unit": "GB/s", "cores": nth, "kind": "oracle",
+            "sample": f"{d_all} full pass(es) of the three q4_0 GEMVs (all rows), fp64 oracle, OpenMP over rows, "
+                      f"{e_all:.1f} s",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "one_thread": {"value": round(v_one, 3), "unit": "GB/s", "cores": 1,
+                           "sample": f"{d_one} full pass(es), {e_one:.1f} s"},
+            "gemm": {"value": round(gemm_tops, 4), "unit": "TOPS", "cores": nth,
+                     "sample": f"{pairs} (token, row) outputs of the 11008x4096 q6_K GEMM at M=512, {tg:.1f} s",
+                     "quantizer_ms_512x4096": round(tq * 1e3, 1)}}
+
+
+# ------------------------------------------------------------------ main
 
 def main():
     a = parse()
@@ -415,98 +547,135 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-    prim = q4_0_workload(qmv, a.steps, a.warmup)
-    dom = max(prim["shapes"], key=lambda s: s["avg_launch_ms"])
-    out = {
+        del src, dst
+
+    t_start = time.perf_counter()
+    ceiling = None if a.only_primary else ReadCeiling(qmv)
+    # the primary workload: warm-up steps, then `steps` timed steps per round
+    prim = GemvWorkload(qmv, "q4_0_step", "q4_0 GEMV batch 1, Llama-7B decode shapes 4096x4096 + 11008x4096 + "
+                        "4096x11008, fp32 x, rotating HBM pool", synth.FMT_Q4_0, LLAMA, 1, synth.DT_F32,
+                        a.steps, ceiling, warm_contrast=True)
+    copies, mats = shared_pool(qmv, synth.FMT_Q4_0, LLAMA)
+    xw = prim.xs
+
+    def warm_step(i):
+        for s in range(len(LLAMA)):
+            qmv.gemv(mats[s][(i + 1000) % copies], xw[s], prim.ys[s])
+            CENSUS.note(qmv)
+    Graph(qmv, warm_step, max(1, a.warmup)).time(warm=False)
+    say(f"bench: primary set up ({copies} pool copies)")
+
+    work = [prim]
+    want = set() if a.only_primary else set(a.secondary.split(","))
+    steps2 = 50
+
+    def add(w):
+        work.append(w)
+        say(f"bench: set up {w.name}")
+
+    if "q6_K_gemv" in want:
+        add(GemvWorkload(qmv, "q6_K_gemv", "q6_K GEMV batch 1, 256x1024, fp32 x", synth.FMT_Q6_K, [(256, 1024)], 1,
+                         synth.DT_F32, 200, ceiling))
+    if "q6_K_decode" in want:
+        for b in (1, 4, 8) if "batch8_other" in want else (1, 4):
+            add(GemvWorkload(qmv, f"q6_K_gemv_b{b}", f"q6_K GEMV batch {b}, Llama-7B decode shapes, fp32 x",
+                             synth.FMT_Q6_K, LLAMA, b, synth.DT_F32, steps2, ceiling))
+    if "q4_0_batch" in want:
+        for b in (2, 4, 8):
+            add(GemvWorkload(qmv, f"q4_0_gemv_b{b}", f"q4_0 GEMV batch {b}, Llama-7B decode shapes, fp32 x",
+                             synth.FMT_Q4_0, LLAMA, b, synth.DT_F32, steps2, ceiling))
+    if "q4_0_q8" in want:
+        for b in (1, 4):
+            add(Q8Workload(qmv, f"q4_0_q8_gemv_b{b}", f"q4_0 GEMV over per-32 int8 activations, batch {b}, "
+                           "Llama-7B decode shapes", synth.FMT_Q4_0, b, steps2, ceiling))
+    if "cb4_moe" in want:
+        add(MoeWorkload(qmv, 64))
+    for fmt, nm, label in ((synth.FMT_AQ2X8, "aq2x8", "2-bit additive"), (synth.FMT_AQ3X8, "aq3x8", "3-bit additive")):
+        if nm in want:
+            bs = (1, 4, 8) if (nm == "aq2x8" and "batch8_other" in want) else (1, 4)
+            for b in bs:
+                add(GemvWorkload(qmv, f"{nm}_gemv_b{b}", f"{label} GEMV batch {b}, 14336x4096 + 4096x14336, bf16 x",
+                                 fmt, AQ_SHAPES, b, synth.DT_BF16, steps2, ceiling))
+    for fmt, nm, label in ((synth.FMT_CB4, "cb4", "4-bit codebook"), (synth.FMT_CB8, "cb8", "8-bit codebook")):
+        for b in [b for b, tag in ((4, "batch4_other"), (8, "batch8_other")) if tag in want]:
+            add(GemvWorkload(qmv, f"{nm}_gemv_b{b}", f"{label} GEMV batch {b}, 2048x7168 + 7168x2048, bf16 x",
+                             fmt, EXPERT, b, synth.DT_BF16, steps2, ceiling))
+    if "cb8" in want:
+        add(GemvWorkload(qmv, "cb8_gemv", "8-bit codebook GEMV batch 1, shared expert gate/up 2048x7168 + down "
+                         "7168x2048 and output head 129280x7168, bf16 x", synth.FMT_CB8,
+                         [(2048, 7168), (2048, 7168), (7168, 2048), (129280, 7168)], 1, synth.DT_BF16, 20, ceiling))
+    if "q6_K_gemm" in want:
+        add(GemmWorkload(qmv, a.steps))
+
+    # interleaved rounds: every workload once per round, in the same order
+    for r in range(max(1, a.repeats)):
+        for w in work:
+            w.measure()
+        say(f"bench: round {r + 1}/{a.repeats} done, primary {sum(prim.algo) / prim.runs['step'][-1] / 1e6:.1f} GB/s")
+    gpu_s = time.perf_counter() - t_start
+
+    pr = prim.result()
+    dom = max(pr["shapes"], key=lambda s: s["avg_launch_ms"])
+    full = {
         "metric": METRIC,
-        "value": round(prim["GBps"], 1),
+        "value": pr["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(prim["ms_per_step"], 5),
+        "repeats": a.repeats,
+        "ms_per_step": pr["ms_per_step"],
+        "step_runs_ms": pr["step_runs_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "q4_0 GEMV batch 1, Llama-7B decode shapes 4096x4096 + 11008x4096 + "
-                               "4096x11008, fp32 x, rotating HBM pool",
-                   "batch": 1, "pool_bytes": prim["pool_bytes"], "pool_copies": prim["copies"],
-                   "bytes_per_step": prim["bytes_per_step"]},
-        "frac_of_peak": round(prim["GBps"] / HBM_PEAK_GBS, 4),
+        "config": {"workload": pr["workload"], "batch": 1, "pool_copies": pr["pool_copies"],
+                   "bytes_per_step": pr["bytes_per_step"]},
+        "frac_of_peak": pr["frac_of_peak"],
         "roofline": {"bound": "hbm", "kernel": f"q4_0 GEMV {dom['shape']} ({dom['path']})",
-                     "achieved": round(dom["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom["frac"], 4),
-                     "traffic": recorded_traffic() if dom["shape"] == "4096x11008" else None},
-        "shapes": prim["shapes"],
+                     "achieved": dom["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["frac"],
+                     "traffic": recorded_traffic() if dom["shape"] == "4096x11008" else None,
+                     "read_ceiling_frac": dom.get("frac_of_read_ceiling")},
+        "shapes": pr["shapes"],
+        "secondary": {w.name: w.result() for w in work[1:]},
+        "census": {"counts": CENSUS.counts, **CENSUS.summary()},
+        "gpu_seconds": round(gpu_s, 1),
     }
-    if not a.only_primary:
-        # the plain-read floor for each primary shape's bytes, same pool protocol
-        rc = read_ceiling(qmv, [sh["bytes"] for sh in prim["shapes"]], a.steps)
-        for sh, c in zip(out["shapes"], rc["sizes"]):
-            sh["read_ceiling_ms"] = c["avg_launch_ms"]
-            sh["frac_of_read_ceiling"] = round(c["avg_launch_ms"] / sh["avg_launch_ms"], 4)
-        out["read_ceiling"] = rc
-        sec = {}
-        want = set(a.secondary.split(","))
-        if "q6_K_gemv" in want:
-            sec["q6_K_gemv"] = gemv_workload(qmv, synth.FMT_Q6_K, [(256, 1024)], 1, synth.DT_F32, 200,
-                                             "q6_K GEMV batch 1, 256x1024, fp32 x")
-        for b in ((2, 4, 8) if "q4_0_batch" in want else ()):
-            sec[f"q4_0_gemv_b{b}"] = gemv_workload(qmv, synth.FMT_Q4_0, [(4096, 4096), (11008, 4096), (4096, 11008)],
-                                                   b, synth.DT_F32, 50,
-                                                   f"q4_0 GEMV batch {b}, Llama-7B decode shapes, fp32 x")
-        for b in ((1, 4) if "q4_0_q8" in want else ()):
-            sec[f"q4_0_q8_gemv_b{b}"] = q8_workload(
-                qmv, synth.FMT_Q4_0, b, 50, f"q4_0 GEMV over per-32 int8 activations, batch {b}, Llama-7B decode shapes")
-        if "q6_K_decode" in want:
-            sec["q6_K_gemv_llama"] = gemv_workload(qmv, synth.FMT_Q6_K, [(4096, 4096), (11008, 4096), (4096, 11008)],
-                                                   1, synth.DT_F32, 50,
-                                                   "q6_K GEMV batch 1, Llama-7B decode shapes, fp32 x")
-        for b in ((1, 4) if "q6_K_decode" in want else ()):
-            sec[f"q6_K_q8_gemv_b{b}"] = q8_workload(
-                qmv, synth.FMT_Q6_K, b, 50, f"q6_K GEMV over per-32 int8 activations, batch {b}, Llama-7B decode shapes")
-        if "batch4_other" in want:
-            # batch 4 for the formats the other batch lines do not cover
-            sec["q6_K_gemv_b4"] = gemv_workload(qmv, synth.FMT_Q6_K, [(4096, 4096), (11008, 4096), (4096, 11008)],
-                                                4, synth.DT_F32, 50, "q6_K GEMV batch 4, Llama-7B decode shapes, fp32 x")
-            sec["cb4_gemv_b4"] = gemv_workload(qmv, synth.FMT_CB4, [(2048, 7168), (7168, 2048)], 4, synth.DT_BF16, 50,
-                                               "4-bit codebook GEMV batch 4, 2048x7168 + 7168x2048, bf16 x")
-            sec["cb8_gemv_b4"] = gemv_workload(qmv, synth.FMT_CB8, [(2048, 7168), (7168, 2048)], 4, synth.DT_BF16, 50,
-                                               "8-bit codebook GEMV batch 4, 2048x7168 + 7168x2048, bf16 x")
-        if "batch8_other" in want:
-            # batch 8 for the formats the q4_0 batch lines do not cover
-            sec["q6_K_gemv_b8"] = gemv_workload(qmv, synth.FMT_Q6_K, [(4096, 4096), (11008, 4096), (4096, 11008)],
-                                                8, synth.DT_F32, 50, "q6_K GEMV batch 8, Llama-7B decode shapes, fp32 x")
-            sec["cb4_gemv_b8"] = gemv_workload(qmv, synth.FMT_CB4, [(2048, 7168), (7168, 2048)], 8, synth.DT_BF16, 50,
-                                               "4-bit codebook GEMV batch 8, 2048x7168 + 7168x2048, bf16 x")
-            sec["cb8_gemv_b8"] = gemv_workload(qmv, synth.FMT_CB8, [(2048, 7168), (7168, 2048)], 8, synth.DT_BF16, 50,
-                                               "8-bit codebook GEMV batch 8, 2048x7168 + 7168x2048, bf16 x")
-            sec["aq2x8_gemv_b8"] = gemv_workload(qmv, synth.FMT_AQ2X8, [(14336, 4096), (4096, 14336)], 8,
-                                                 synth.DT_BF16, 50, "2-bit additive GEMV batch 8, 14336x4096 + 4096x14336, bf16 x")
-        if "cb4_moe" in want:
-            sec["cb4_moe"] = moe_workload(qmv, 64, "4-bit codebook MoE FFN, batch 1, 256 experts top-8, "
-                                                   "gate/up 2048x7168 + down 7168x2048, bf16 x")
-        for b in ((1, 4) if "aq2x8" in want else ()):
-            sec[f"aq2x8_gemv_b{b}"] = gemv_workload(qmv, synth.FMT_AQ2X8, [(14336, 4096), (4096, 14336)], b,
-                                                    synth.DT_BF16, 50,
-                                                    f"2-bit additive GEMV batch {b}, 14336x4096 + 4096x14336, bf16 x")
-        for b in ((1, 4) if "aq3x8" in want else ()):
-            sec[f"aq3x8_gemv_b{b}"] = gemv_workload(qmv, synth.FMT_AQ3X8, [(14336, 4096), (4096, 14336)], b,
-                                                    synth.DT_BF16, 50,
-                                                    f"3-bit additive GEMV batch {b}, 14336x4096 + 4096x14336, bf16 x")
-        if "cb8" in want:
-            sec["cb8_gemv"] = gemv_workload(qmv, synth.FMT_CB8, [(2048, 7168), (2048, 7168), (7168, 2048),
-                                                                 (129280, 7168)], 1, synth.DT_BF16, 20,
-                                            "8-bit codebook GEMV batch 1, shared expert gate/up 2048x7168 + "
-                                            "down 7168x2048 and output head 129280x7168, bf16 x")
-        if "q6_K_gemm" in want:
-            sec["q6_K_gemm"] = gemm_workload(qmv, a.steps, "q6_K prefill GEMM, M=512, 11008x4096 + 4096x11008")
-        out["secondary"] = sec
+    if ceiling is not None:
+        big = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+        def rd(i):
+            qmv.read_ceiling(big, sink)
+            CENSUS.note(qmv)
+        ms = med([Graph(qmv, rd, 5).time() for _ in range(3)])
+        full["read_ceiling_4GiB_GBps"] = round(big.numel() / ms / 1e6, 1)
+        del big
     if not a.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
-    print(json.dumps(out))
+        say("bench: timing the CPU oracle")
+        full["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as f:
+        json.dump(full, f, indent=1)
+
+    # the compact record, last line of stdout
+    line = {k: full[k] for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                                 "frac_of_peak", "roofline")}
+    line["repeats"] = a.repeats
+    line["shapes_GBps"] = {s["shape"]: s["GBps"] for s in pr["shapes"]}
+    if "cpu_baseline" in full:
+        cb = full["cpu_baseline"]
+        line["cpu_baseline"] = {"value": cb["value"], "unit": cb["unit"], "cores": cb["cores"], "kind": cb["kind"],
+                                "sample": "q4_0 step, all rows, fp64 oracle", "cpu_model": cb["cpu_model"],
+                                "one_thread_GBps": cb["one_thread"]["value"], "gemm_TOPS": cb["gemm"]["value"]}
+    line["census"] = CENSUS.summary()
+    line["secondary"] = {"fields": "GB/s, frac of 8 TB/s (GEMM: TOPS, frac of 5 POPS, TOPS with the quantizer, "
+                                   "TOPS without planes)", **{w.name: w.brief() for w in work[1:]}}
+    line["full_record"] = os.path.relpath(os.path.abspath(a.out), ROOT)
+    print(json.dumps(line, separators=(",", ":")))
 
 
 if __name__ == "__main__":
