@@ -14,7 +14,7 @@ import weakref
 __all__ = [
     "Q4_0", "Q6_K", "CB4", "AQ2X8", "CB8", "AQ3X8", "F32", "BF16", "QmvError", "QWeights", "lib", "plane_bytes",
     "weight_bytes", "validate", "gemv", "dequant", "quant_act", "workspace_bytes", "gemm",
-    "gemm_q8", "partials", "plane_bytes_of", "register_plane", "unregister_plane", "moe_ffn", "last_path",
+    "gemm_q8", "gemm_noalloc", "partials", "plane_bytes_of", "register_plane", "unregister_plane", "moe_ffn", "last_path",
     "strerror", "PLANES",
 ]
 
@@ -90,6 +90,8 @@ def lib():
         L.qmm_gemm_q8.argtypes = [P, I32, P, P, P, P]
         L.qmm_partials.restype = C.c_int
         L.qmm_partials.argtypes = [P, I32, P, P, P]
+        L.qmm_gemm_noalloc.restype = C.c_int
+        L.qmm_gemm_noalloc.argtypes = [P, I32, P, P, P]
         L.qmm_plane_bytes.restype = I64
         L.qmm_plane_bytes.argtypes = [P]
         L.qmm_register_plane.restype = C.c_int
@@ -284,6 +286,17 @@ def gemm(w: QWeights, x, y=None, ws=None, stream=None):
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     _need(ws, (torch.uint8,), None, "ws")
     _check(lib().qmm_gemm(w.ref, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)), "qmm_gemm")
+    return y
+
+
+def gemm_noalloc(w: QWeights, x, y, stream=None):
+    """qmm_gemm_noalloc: the q6_K GEMM with the library's own per-GPU scratch instead of a
+    workspace; y (fp32 [m][n]) must be given, nothing is allocated."""
+    import torch
+    m = x.shape[0]
+    _need(x, (torch.float32,), (m, w.k), "x")
+    _need(y, (torch.float32,), (m, w.n), "y")
+    _check(lib().qmm_gemm_noalloc(w.ref, m, _ptr(x), _ptr(y), _stream(stream)), "qmm_gemm_noalloc")
     return y
 
 

@@ -220,6 +220,23 @@ int64_t qmm_workspace_bytes(const qmv_weights *w, int32_t m);
 int qmm_gemm(const qmv_weights *w, int32_t m, const float *x, float *y, void *ws, int64_t ws_bytes,
              void *stream);
 
+/*
+ * qmm_gemm without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The same kernels as qmm_gemm; the quantized activations go to a library-owned device
+ * array of QMV_NOALLOC_SCRATCH_BYTES (16 MiB), one per GPU, held until the process ends.
+ *   w, m, x, y, stream: as qmm_gemm.  Nothing is allocated.
+ *   Limit: qmm_workspace_bytes(w, m) <= QMV_NOALLOC_SCRATCH_BYTES (about 1.125 * m * k bytes;
+ *   e.g. m = 512 tokens up to k = 28,928), else QMV_ERR_LIMIT.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ *   streams or threads) race and must be ordered by the caller.  Nothing in the array needs
+ *   to start at zero.
+ *   Errors: as qmm_gemm (except QMV_ERR_WORKSPACE); QMV_ERR_HIP when the array's device
+ *   address cannot be looked up.
+ */
+#define QMV_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int qmm_gemm_noalloc(const qmv_weights *w, int32_t m, const float *x, float *y, void *stream);
+
 /* The contraction of qmm_gemm alone, on already quantized activations
  * (xq int8 [m][k], xs fp32 [m][k/32]). */
 int qmm_gemm_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *xs, float *y,

@@ -186,3 +186,19 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in (r.stdout + r.stderr)
+
+
+def test_gemm_noalloc_argument_errors_before_any_gpu_work():
+    # the no-allocation GEMM checks everything on the host before it looks up its scratch
+    L = qmv.lib()
+    nz = 1 << 20
+    assert L.qmm_gemm_noalloc(None, 4, nz, nz, None) == -1
+    assert L.qmm_gemm_noalloc(_fake(qmv.Q4_0, 8, 256).ref, 4, nz, nz, None) == -3   # q6_K only
+    assert L.qmm_gemm_noalloc(_fake(qmv.Q6_K, 8, 300).ref, 4, nz, nz, None) == -2   # k % 256
+    assert L.qmm_gemm_noalloc(_fake(qmv.Q6_K, 8, 256).ref, 0, nz, nz, None) == -6
+    assert L.qmm_gemm_noalloc(_fake(qmv.Q6_K, 8, 256).ref, 4, None, nz, None) == -1
+    assert L.qmm_gemm_noalloc(_fake(qmv.Q6_K, 8, 256).ref, 4, nz + 4, nz, None) == -5
+    # beyond the 16 MiB scratch: 512 tokens of k = 29184 need 16,809,984 bytes
+    assert qmv.workspace_bytes(_fake(qmv.Q6_K, 8, 29184), 512) > 16 * 1024 * 1024
+    assert L.qmm_gemm_noalloc(_fake(qmv.Q6_K, 8, 29184).ref, 512, nz, nz, None) == -9
+    assert qmv.workspace_bytes(_fake(qmv.Q6_K, 8, 28928), 512) <= 16 * 1024 * 1024
