@@ -10,7 +10,8 @@ cannot serve repeated reads (the weights come from HBM, as in decode).
 Protocol: every workload is set up first; then `--repeats` rounds each measure every
 workload once, in the same order (interleaved), and each figure is the median over
 the rounds.  Times come from HIP events recorded on the stream the kernels run on,
-around replays of HIP graphs that hold the launches.
+around replays of HIP graphs that hold the launches; a short spin kernel ahead of the
+start event keeps the host's graph submission out of the timed window.
 
 Output: one short progress line per workload while it runs, the full record written to
 `--out` (JSON), and as the LAST stdout line a compact JSON record (value = algorithmic
@@ -39,6 +40,7 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
 POOL_BYTES = 1 << 30           # rotating pool: 4x the 256 MB Infinity Cache
+SPIN_CYCLES = 2_000_000        # ~1 ms of GPU spin ahead of each timed replay
 LLAMA = [(4096, 4096), (11008, 4096), (4096, 11008)]
 EXPERT = [(2048, 7168), (7168, 2048)]
 AQ_SHAPES = [(14336, 4096), (4096, 14336)]
@@ -52,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--repeats", type=int, default=3, help="interleaved rounds; figures are medians")
+    ap.add_argument("--repeats", type=int, default=5, help="interleaved rounds; figures are medians")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="per CPU leg")
     ap.add_argument("--only-primary", action="store_true", help="skip the secondary workloads")
@@ -65,8 +67,11 @@ def parse():
     return ap.parse_args()
 
 
+T0 = time.perf_counter()
+
+
 def say(msg: str):
-    print(msg, flush=True)
+    print(f"[{time.perf_counter() - T0:6.1f} s] {msg}", flush=True)
 
 
 # ------------------------------------------------------------------ graphs and census
@@ -120,13 +125,17 @@ class Graph:
         torch.cuda.synchronize()
 
     def time(self, warm=True):
-        """Milliseconds per item of one replay (HIP events on the replay stream)."""
+        """Milliseconds per item of one replay (HIP events on the replay stream).  A short
+        spin kernel runs ahead of the start event, so the host has submitted the whole graph
+        before the first timed launch: the events then bracket the launches' execution, not
+        the host's submission of them."""
         import torch
         if warm:
             self.g.replay()
             CENSUS.add(self.labels)
             torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(SPIN_CYCLES)
         s.record()
         self.g.replay()
         e.record()
