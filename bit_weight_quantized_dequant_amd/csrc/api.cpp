@@ -320,7 +320,7 @@ int64_t qmm_plane_bytes(const qmv_weights *w) {
     int rc = qmv_validate(w, 1, QMV_F32);
     if (rc) return rc;
     if (w->fmt != QMV_Q6_K) return QMV_ERR_FORMAT;
-    return 2 * w->n * w->k;
+    return gemm_plane_bytes(w->n, w->k);
 }
 
 int qmm_register_plane(const qmv_weights *w, void *plane, int64_t plane_bytes, void *stream) {

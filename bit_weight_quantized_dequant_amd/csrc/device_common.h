@@ -22,6 +22,17 @@ QMV_DEV uint4 lds_ld16(uint32_t a) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Workgroup barrier that orders LDS only: this wave's LDS operations complete, then
+// s_barrier.  __syncthreads() also waits for every outstanding global load of the wave
+// (its workgroup-scope fence covers global memory), so loads issued ahead for a later step
+// would be waited for at every barrier; here they stay in flight across it.  Only for
+// kernels whose waves exchange data through LDS alone.
+QMV_DEV void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // IEEE binary16 bits -> float (exact; subnormals kept).
 QMV_DEV float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 

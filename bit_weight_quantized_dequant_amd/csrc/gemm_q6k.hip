@@ -7,36 +7,44 @@
 // values are expanded into centred integers for an int8 contraction; §2.3: that
 // expansion is an integer transform, so the partials are exact).
 //
-// Design for gfx950 (the page's NB-BT CUDA kernel stages raw or pre-expanded int8 B
+// Design for gfx950 (the page's NB-BT CUDA kernel stages raw or pre-expanded int8 weight
 // tiles with cp.async; here):
-//   * Orientation: MFMA rows are weight rows n (operand A), columns are tokens m
-//     (operand B = int8 activations), so each lane's column has one activation scale
-//     xs[m][c] per block: the block epilogue is one convert and one FMA per value.
-//   * The sub-scale is folded into the weights: w' = sc * (q - 32) lies in
-//     [-4064, 4096] and is split exactly as w' = 64 h + l with l = w' & 63 in [0, 63]
-//     and h = w' >> 6 in [-64, 64], two int8 planes.  Two MFMAs per 32-block give
-//     I32 = 64 C_H + C_L exactly in int32: the first gives C_H, which is shifted by 6 and
-//     handed to the second as its accumulator input.
-//   * K advances in steps of 64 (two activation blocks) through double-buffered LDS:
-//     the raw codes and activation bytes of a later step are fetched into registers while
-//     this step runs on the matrix cores, then expanded (6-bit code -> w' = sc (q - 32)
-//     by one packed 16-bit multiply-add -> h, l bytes) into the other buffer; one barrier
-//     per step.  Loads are unconditional (row and token indices clamped), so no branch
-//     makes the compiler wait for them early.
-//   * fp32 partial sums per super-block are scaled by d once.
-// Tiles: 256 threads = 4 waves; 128 token columns per workgroup.  Wide matrices use
-// 64-row tiles (waves 2 (n) x 2 (m), wave tile 32 n x 64 m = two 32x32 MFMA tiles sharing
-// the A fragments; three workgroups per CU); narrow ones, which would leave CUs idle with
-// 64-row tiles, use 32-row tiles (waves 1 x 4, wave tile 32 x 32) with loads two steps
-// ahead.  The per-block epilogue (shift-add, convert, FMA on every 32x32 value) is the
-// VALU cost that bounds this kernel, not the matrix cores.
+//   * Orientation: MFMA rows are weight rows n (operand A), columns are tokens m (operand
+//     B = int8 activations), so each lane's column has one activation scale xs[m][c] per
+//     block: the block epilogue is a shift, a convert and an FMA per value.
+//   * The sub-scale is folded into the weights: w' = sc * (q - 32) lies in [-4064, 4096]
+//     and is split exactly as w' = 64 h + l (l = w' & 63 in [0, 63], h = w' >> 6 in
+//     [-64, 64]), two int8 operands.  Two MFMAs per 32-block give I32 = 64 C_H + C_L
+//     exactly: C_H is shifted by 6 and handed to the second MFMA as its accumulator.
+//   * Every operand tile sits in LDS in MFMA fragment order: a 32 x 32 int8 block is 64
+//     lanes x 16 bytes, lane l holding row l % 32 and k 16 (l / 32) .. + 15.  Fragment
+//     reads are then lane-linear ds_read_b128 (no bank conflicts), and so are the direct
+//     global-to-LDS loads that fill them (global_load_lds_dwordx4: lane l's 16 bytes land
+//     at the chunk base + 16 l), so activations and registered weight planes reach LDS
+//     without passing through registers.
+//   * K advances 64 per stage through a ring of four LDS stages (one per stage of a
+//     super-block, so every slot address is an immediate): the loads of stage st + 3 are
+//     issued right after the barrier of stage st and land while st .. st + 2 are computed.  Waits are explicit (s_waitcnt vmcnt on this stage's loads, then an
+//     LDS-only barrier), so loads for later stages stay in flight across barriers.
+//   * Each wave software-pipelines its 32-blocks: the previous block's epilogue (convert
+//     and FMA, VALU) is interleaved with this block's MFMAs, so the matrix cores and the
+//     VALU work on different blocks at the same time.
+//   * fp32 sums per super-block are scaled by d once; the workgroup's d values are staged
+//     in LDS once.
+// Tiles: 64 weight rows x 128 tokens per workgroup.  Four waves (2 row groups x 2 token
+// pairs), each 32 rows x 64 tokens (two MFMA tiles sharing the weight fragments).  When
+// there are too few tiles to give every CU several workgroups, eight waves split K by the
+// parity of the 32-block (KSPLIT = 2) and add their sums through LDS at the end, so a CU
+// still holds two waves per SIMD.
+// Weights come either from registered pre-expanded planes (EXP: the h and l bytes already in
+// fragment order, loaded straight into LDS) or from the codes, expanded by the threads into
+// the same LDS image.
 //
-// MFMA operand layout used (32x32x32 i8): lane l supplies row (or column) l % 32 and
-// the 16 consecutive k of group l / 32; the accumulator's value v of lane l is
-// C[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32].  A debug entry point writes the exact
-// I32 partials from this same code path, which pins the layout against the oracle.
+// MFMA operand layout (32x32x32 i8): lane l supplies row (or column) l % 32 and the 16
+// consecutive k of group l / 32; accumulator value v of lane l is
+// C[8 (v / 4) + 4 (l / 32) + (v % 4)][l % 32].  A debug entry point writes the exact I32
+// partials from this same code path, which pins the layout against the oracle.
 #include <cstring>
-#include <type_traits>
 
 #include "device_common.h"
 #include "qmv_internal.h"
@@ -47,27 +55,16 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int TB = 256;       // 4 waves
-constexpr int BM = 128;       // token columns per workgroup tile
-constexpr int KS = 64;        // k per step: two 32-activation blocks
-constexpr int RS = KS + 16;   // LDS row stride (bytes) of the staged int8 planes
+constexpr int BN = 64;     // weight rows per workgroup tile
+constexpr int BM = 128;    // tokens per workgroup tile
+constexpr int NSTAGE = 4;  // LDS ring depth: one slot per stage of a super-block
+constexpr int MAXSB = 80;  // super-blocks (k / 256) whose d values fit the workgroup's table
 
-// Tile geometry: WN wave rows of 32 weight rows each, 4 / WN wave columns; a wave covers
-// 32 rows x TPW 32-token MFMA tiles (sharing its A fragments).
-template <int WN>
-struct Geo {
-    static constexpr int BN = 32 * WN;                 // weight rows per workgroup
-    static constexpr int WMC = 4 / WN;                 // wave columns
-    static constexpr int TPW = BM / (32 * WMC);        // token tiles per wave
-    static constexpr int TPR = TB / BN;                // expanding threads per row
-    static constexpr int W = KS / TPR;                 // weights each thread expands per step
-    static constexpr int LDS = 2 * (2 * BN + BM) * RS; // two buffers of sH, sL, sB
-};
-
-// Four 6-bit codes (bytes of q) of one sub-block -> w' = sc * (q - 32) in [-4064, 4096],
-// split exactly as w' = 64 h + l (h = w' >> 6 in [-64, 64], l = w' & 63), packed as four h
-// bytes and four l bytes.  (w' << 2) keeps h in the high byte of each 16-bit lane.
+// Four 6-bit codes (bytes of q) -> w' = sc * (q - 32) in [-4064, 4096], split exactly as
+// w' = 64 h + l, packed as four h bytes and four l bytes.  (w' << 2) keeps h in the high byte
+// of each 16-bit lane.
 QMV_DEV void expand4(uint32_t q, uint32_t sc2, uint32_t c2, uint32_t &hb, uint32_t &lb) {
     const uint32_t q01 = __builtin_amdgcn_perm(0u, q, 0x0C010C00u);  // (q0, q1) as 16-bit lanes
     const uint32_t q23 = __builtin_amdgcn_perm(0u, q, 0x0C030C02u);
@@ -80,36 +77,88 @@ QMV_DEV void expand4(uint32_t q, uint32_t sc2, uint32_t c2, uint32_t &hb, uint32
          0x3F3F3F3Fu;
 }
 
-template <int NW> struct RawA;
-template <> struct RawA<16> { uint4 ql, qh; };
-template <> struct RawA<8> { uint2 ql, qh; };
-// The same thread's share of a step from the pre-expanded planes: its h and l bytes.
-template <int NW> struct RawE;
-template <> struct RawE<16> { uint4 h, l; };
-template <> struct RawE<8> { uint2 h, l; };
+// s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt left unlimited).
+template <int N>
+QMV_DEV void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
-// Step st = 4 s + j covers weights [64 j, 64 j + 64) of super-block s: half h = j >> 1,
-// runs t = 2 (j & 1) + {0, 1}, each run 32 consecutive l.  Weight (h, t, l) has its low
-// nibble in ql[64 h + 32 (t & 1) + l] (bits 4 (t >> 1)..) and its high bits in
-// qh[32 h + l] (bits 2 t..); ql/qh bytes of a half serve both of its steps.  Tile byte
-// 32 tt + l of the step is weight 64 st + 32 tt + l of the row: natural k order, which
-// is also the order of the pre-expanded planes (EXP: the thread copies its h and l bytes
-// instead of expanding codes).
-template <int WN, bool PARTIALS, int PD, bool EXP>
-__global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh,
-                                                         const int8_t *__restrict__ scp, const uint16_t *__restrict__ dp,
-                                                         const int8_t *__restrict__ ph, const int8_t *__restrict__ pl,
-                                                         const int8_t *__restrict__ xq, const float *__restrict__ xs,
-                                                         float *__restrict__ y, int32_t *__restrict__ part,
-                                                         int M, int N, int K) {
-    using G = Geo<WN>;
-    constexpr int BN = G::BN, TPW = G::TPW, NWT = G::W;
-    using RA = std::conditional_t<EXP, RawE<NWT>, RawA<NWT>>;
+// The ring's barrier: this wave's LDS operations complete (its reads of the stage about to
+// be refilled, its expanded-weight writes), then s_barrier.  The direct loads of the stage
+// are waited for separately (wait_vmcnt): a workgroup fence here would also wait for the
+// loads already issued for later stages, since they write LDS too.  The empty asm
+// statements keep the compiler from moving memory accesses across the barrier.
+QMV_DEV void ring_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unlimited
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS at chunk + 16 * lane.
+QMV_DEV void dma16(const void *src, uint8_t *chunk) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)chunk, 16, 0, 0);
+}
+// 4 bytes per lane into LDS at chunk + 4 * lane.
+QMV_DEV void dma4(const void *src, uint8_t *chunk) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)chunk, 4, 0, 0);
+}
+
+// Raw codes of one thread's share of a stage's weight tile (in-kernel expansion): NW
+// consecutive weights of one row.
+template <int NW> struct Raw;
+template <> struct Raw<16> { uint4 ql, qh; int sc; };
+template <> struct Raw<8> { uint2 ql, qh; int sc; };
+template <> struct Raw<4> { uint32_t ql, qh; int sc; };
+
+// Waits until at most n of this wave's vector-memory operations are outstanding (n is
+// wave-uniform and at most 10; the count is an immediate, hence the switch).
+QMV_DEV void wait_vmcnt_le(int n) {
+    switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    default: wait_vmcnt<10>(); break;
+    }
+}
+
+// Workgroup: 8 * KSPLIT waves.  Wave w computes MFMA tile (row group w & 1, token group
+// (w >> 1) & 3) of the 64 x 128 workgroup tile, over the 32-blocks of its K part
+// kh = w >> 3 (block b of a stage when b % KSPLIT == kh).  A stage holds KB 32-blocks.
+template <int KSPLIT, int KB>
+struct Lay {
+    static constexpr int WAVES = 8 * KSPLIT, THREADS = 64 * WAVES;
+    static constexpr int KS = 32 * KB;                        // k per stage
+    static constexpr int A = 0;                               // [row group 2][block KB][h, l][64][16 B]
+    static constexpr int B = A + 2 * KB * 2048;               // [token group 4][block KB][64][16 B]
+    static constexpr int XS = B + 4 * KB * 1024;              // [block KB][128 tokens] fp32
+    static constexpr int STAGE = XS + KB * 512;
+    static constexpr int RING = NSTAGE * STAGE;
+    static constexpr int NA = 4 * KB, NB = 4 * KB, NX = 2 * KB;  // direct-load jobs per stage
+    static constexpr int NW = 16 * 2 * KB * 64 / THREADS;     // weights each thread expands
+};
+
+template <int KSPLIT, int KB, bool EXP, bool PARTIALS>
+__global__ void __launch_bounds__(512 * KSPLIT, 1)
+gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh, const int8_t *__restrict__ scp,
+                const uint16_t *__restrict__ dp, const int8_t *__restrict__ plane, const int8_t *__restrict__ xq,
+                const float *__restrict__ xs, float *__restrict__ y, int32_t *__restrict__ part, int M, int N, int K) {
+    using L = Lay<KSPLIT, KB>;
+    constexpr int WAVES = L::WAVES, NW = L::NW, KS = L::KS;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    __shared__ float sD[2][BN];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave % WN, wm = wave / WN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches, scalar offsets
+    const int rg = wave & 1, tg = (wave >> 1) & 3, kh = wave >> 3;
+    const int li = lane & 31, lg = lane >> 5;
     // Workgroups are dealt to the eight XCDs round-robin in dispatch order (x fastest).
     // Remap so that XCD x takes one contiguous run of row tiles with all their column
     // tiles: the column tiles that share a weight tile then share one L2.
@@ -122,329 +171,360 @@ __global__ void __launch_bounds__(TB, PD == 1 ? 3 : 2) gemm_q6k_kernel(const uin
         n0 = (t / nct) * BN;
         m0 = (t % nct) * BM;
     }
-    const int nsteps = K / KS, nblk = K >> 5;
-    const int li = lane & 31, lg = lane >> 5;
+    const int nst = K / KS, nblk = K >> 5, nsb = K >> 8, G = (N + 31) >> 5;
 
-    // expansion role: row er, run tt of the step, first l of this thread's NWT weights
-    const int er = tid / G::TPR, ep = tid % G::TPR;
-    const int tt = (ep * NWT) >> 5, l0 = (ep * NWT) & 31;
-    const int erow = min(n0 + er, N - 1);
-    const uint8_t *qlr = ql + (int64_t)erow * (K >> 1) + 32 * tt + l0;
-    const uint8_t *qhr = qh + (int64_t)erow * (K >> 2) + l0;
-    const int8_t *scr = scp + (int64_t)erow * (K >> 4) + 2 * tt + (l0 >> 4);
-    const uint16_t *dr = dp + (int64_t)erow * (K >> 8);
-    const int8_t *phr = ph + (int64_t)erow * K + 32 * tt + l0;  // EXP: this thread's h, l bytes
-    const int8_t *plr = pl + (int64_t)erow * K + 32 * tt + l0;
-    // activation staging role: token bt, bytes [32 bo, 32 bo + 32) of the step
-    const int bt = tid >> 1, bo = tid & 1;
-    const int8_t *xr = xq + (int64_t)min(m0 + bt, M - 1) * K + 32 * bo;
-    // epilogue: the lane's token of each tile
-    int tok[TPW];
+    // ---- this wave's direct-load jobs of a stage (job j goes to wave j % WAVES): weight
+    // chunks (EXP), activation chunks, activation-scale words.  Sources are for stage 0.
+    constexpr int NJ = (EXP ? L::NA : 0) + L::NB + (PARTIALS ? 0 : L::NX);
+    constexpr int MAXJ = (NJ + WAVES - 1) / WAVES;
+    const int8_t *jsrc[MAXJ];
+    int jlds[MAXJ], jstep[MAXJ];
+    bool jword[MAXJ];
+    int njobs = 0;
 #pragma unroll
-    for (int t = 0; t < TPW; t++) tok[t] = m0 + 32 * (wm * TPW + t) + li;
-
-    uint8_t *const sbase = smem;
-    auto sH = [&](int b) { return sbase + b * (2 * BN + BM) * RS; };
-    auto sL = [&](int b) { return sbase + b * (2 * BN + BM) * RS + BN * RS; };
-    auto sB = [&](int b) { return sbase + b * (2 * BN + BM) * RS + 2 * BN * RS; };
-
-    // raw inputs of one step, held in registers from the prefetch to the expansion; with a
-    // prefetch distance of 2 there are two sets, used by even and odd steps
-    struct Raw {
-        RA ra;
-        int scb;
-        uint32_t dbits;
-        uint4 rb0, rb1;
-        float2 xsv[TPW];
-    };
-
-    auto fetch = [&](int st, Raw &r) {
-        auto &ra = r.ra;
-        auto &scb = r.scb;
-        auto &dbits = r.dbits;
-        auto &rb0 = r.rb0;
-        auto &rb1 = r.rb1;
-        auto &xsv = r.xsv;
-        const int s = st >> 2, j = st & 3, h = j >> 1;
-        // Plain (cached) loads for the weights: every column tile of a row tile reads the
-        // same weight bytes on the same XCD (see the tile order above), and with cached
-        // loads the later ones hit in its L2 (nontemporal loads measured 2-10 % slower).
-        if constexpr (EXP) {
-            if constexpr (NWT == 16) {
-                ra.h = *(const uint4 *)(phr + st * KS);
-                ra.l = *(const uint4 *)(plr + st * KS);
-            } else {
-                ra.h = *(const uint2 *)(phr + st * KS);
-                ra.l = *(const uint2 *)(plr + st * KS);
-            }
-        } else {
-            if ((j & 1) == 0) {  // a new half: its ql/qh bytes
-                if constexpr (NWT == 16) {
-                    ra.ql = *(const uint4 *)(qlr + 128 * s + 64 * h);
-                    ra.qh = *(const uint4 *)(qhr + 64 * s + 32 * h);
-                } else {
-                    ra.ql = *(const uint2 *)(qlr + 128 * s + 64 * h);
-                    ra.qh = *(const uint2 *)(qhr + 64 * s + 32 * h);
-                }
-            }
-            scb = scr[16 * s + 8 * h + 4 * (j & 1)];
+    for (int i = 0; i < MAXJ; i++) {
+        int j = wave + i * WAVES;
+        jsrc[i] = nullptr;
+        jlds[i] = 0;
+        jstep[i] = 0;
+        jword[i] = false;
+        if (j >= NJ) continue;
+        njobs++;
+        if (EXP && j < L::NA) {  // weight chunk [row group][block][h/l]
+            const int a = j, r = a / (2 * KB), blk = (a >> 1) % KB, p = a & 1;
+            const int g = min((n0 >> 5) + r, G - 1);
+            jsrc[i] = plane + ((int64_t)g * nblk + blk) * 2048 + p * 1024 + 16 * lane;
+            jlds[i] = L::A + a * 1024;
+            jstep[i] = KB * 2048;
+            continue;
         }
-        if (j == 0) dbits = dr[s];
-        rb0 = *(const uint4 *)(xr + st * KS);
-        rb1 = *(const uint4 *)(xr + st * KS + 16);
-        if (!PARTIALS) {
+        j -= EXP ? L::NA : 0;
+        if (j < L::NB) {  // activation chunk [token group][block]
+            const int t = j / KB, blk = j % KB;
+            const int tok = min(m0 + 32 * t + li, M - 1);
+            jsrc[i] = xq + (int64_t)tok * K + 32 * blk + 16 * lg;
+            jlds[i] = L::B + j * 1024;
+            jstep[i] = KS;
+            continue;
+        }
+        j -= L::NB;  // activation scales: entries 64 j + lane of [block][128 tokens]
+        const int e = 64 * j + lane;
+        jsrc[i] = (const int8_t *)(xs + (int64_t)min(m0 + (e & 127), M - 1) * nblk + (e >> 7));
+        jlds[i] = L::XS + 4 * 64 * j;
+        jstep[i] = 4 * KB;
+        jword[i] = true;
+    }
+    auto dma = [&](int st, int buf) {
+        uint8_t *s = smem + buf * L::STAGE;
 #pragma unroll
-            for (int t = 0; t < TPW; t++)
-                xsv[t] = *(const float2 *)(xs + (int64_t)min(tok[t], M - 1) * nblk + 2 * st);
+        for (int i = 0; i < MAXJ; i++) {
+            if (i >= njobs) break;
+            if (jword[i]) dma4(jsrc[i] + (int64_t)st * jstep[i], s + jlds[i]);
+            else dma16(jsrc[i] + (int64_t)st * jstep[i], s + jlds[i]);
         }
     };
 
-    // Stage step st into LDS buffer buf: the weight tile (expanded from the codes, or copied
-    // from the planes), the super-block's d once per super-block, the activation bytes.
-    auto store = [&](int st, int buf, const Raw &r) {
-        const RA ra = r.ra;
-        const uint32_t dbits = r.dbits;
-        const uint4 rb0 = r.rb0, rb1 = r.rb1;
-        uint8_t *dh = sH(buf) + er * RS + 32 * tt + l0;
-        uint8_t *dl = sL(buf) + er * RS + 32 * tt + l0;
-        if constexpr (EXP) {
-            if constexpr (NWT == 16) {
-                *(uint4 *)dh = make_uint4(ra.h.x, ra.h.y, ra.h.z, ra.h.w);
-                *(uint4 *)dl = make_uint4(ra.l.x, ra.l.y, ra.l.z, ra.l.w);
-            } else {
-                *(uint2 *)dh = make_uint2(ra.h.x, ra.h.y);
-                *(uint2 *)dl = make_uint2(ra.l.x, ra.l.y);
-            }
+    // ---- in-kernel expansion role (no EXP): lane chunk eu of the stage's weight tile
+    // ([row group][block] x 64 lanes), NW weights from sub-offset esub
+    constexpr int TPC = 16 / NW;  // threads per lane chunk
+    const int eu = tid / TPC, esub = NW * (tid % TPC);
+    const int ea = eu >> 6, el = eu & 63;  // chunk [row group ea / KB][block ea % KB]
+    const int erg = ea / KB, eblk = ea % KB;
+    const int erow = min(n0 + 32 * erg + (el & 31), N - 1);
+    const int ek = 16 * (el >> 5) + esub;  // k within the block
+    auto load_raw = [&](int st, Raw<NW> &r) {
+        const int kk = KS * st + 32 * eblk + ek;  // k of the first weight
+        const int s = kk >> 8, e0 = kk & 255;
+        const int h = e0 >> 7, t = (e0 >> 5) & 3, lo = e0 & 31;
+        const uint8_t *a = ql + (int64_t)erow * (K >> 1) + 128 * s + 64 * h + 32 * (t & 1) + lo;
+        const uint8_t *b = qh + (int64_t)erow * (K >> 2) + 64 * s + 32 * h + lo;
+        if constexpr (NW == 16) {
+            r.ql = *(const uint4 *)a;
+            r.qh = *(const uint4 *)b;
+        } else if constexpr (NW == 8) {
+            r.ql = *(const uint2 *)a;
+            r.qh = *(const uint2 *)b;
         } else {
-            const int scb = r.scb;
-            const int j = st & 3;
-            const int sh = 2 * (2 * (j & 1) + tt);  // qh bit offset of run t
-            const uint32_t sc16 = (uint32_t)scb & 0xFFFFu;
-            const uint32_t sc2 = sc16 | (sc16 << 16);
-            const uint32_t c16 = (uint32_t)(-32 * scb) & 0xFFFFu;
-            const uint32_t c2 = c16 | (c16 << 16);
-            constexpr int ND = NWT / 4;
-            uint32_t qlw[ND], qhw[ND], hv[ND], lv[ND];
-            if constexpr (NWT == 16) {
-                qlw[0] = ra.ql.x; qlw[1] = ra.ql.y; qlw[2] = ra.ql.z; qlw[3] = ra.ql.w;
-                qhw[0] = ra.qh.x; qhw[1] = ra.qh.y; qhw[2] = ra.qh.z; qhw[3] = ra.qh.w;
-            } else {
-                qlw[0] = ra.ql.x; qlw[1] = ra.ql.y;
-                qhw[0] = ra.qh.x; qhw[1] = ra.qh.y;
-            }
-#pragma unroll
-            for (int i = 0; i < ND; i++) {
-                const uint32_t nib = ((j & 1) ? qlw[i] >> 4 : qlw[i]) & 0x0F0F0F0Fu;
-                const uint32_t q = nib | (((qhw[i] >> sh) & 0x03030303u) << 4);
-                expand4(q, sc2, c2, hv[i], lv[i]);
-            }
-            if constexpr (NWT == 16) {
-                *(uint4 *)dh = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-                *(uint4 *)dl = make_uint4(lv[0], lv[1], lv[2], lv[3]);
-            } else {
-                *(uint2 *)dh = make_uint2(hv[0], hv[1]);
-                *(uint2 *)dl = make_uint2(lv[0], lv[1]);
-            }
+            r.ql = *(const uint32_t *)a;
+            r.qh = *(const uint32_t *)b;
         }
-        if ((st & 3) == 0 && ep == 0) sD[(st >> 2) & 1][er] = h2f((uint16_t)dbits);
-        uint8_t *db = sB(buf) + bt * RS + 32 * bo;
-        *(uint4 *)db = rb0;
-        *(uint4 *)(db + 16) = rb1;
+        r.sc = scp[(int64_t)erow * (K >> 4) + 16 * s + (e0 >> 4)];
+    };
+    auto expand = [&](int st, const Raw<NW> &r, int buf) {
+        const int e0 = (KS * st + 32 * eblk + ek) & 255, t = (e0 >> 5) & 3;
+        const int sh = 4 * (t >> 1), hs = 2 * t;
+        const uint32_t sc16 = (uint32_t)r.sc & 0xFFFFu, c16 = (uint32_t)(-32 * r.sc) & 0xFFFFu;
+        const uint32_t sc2 = sc16 | (sc16 << 16), c2 = c16 | (c16 << 16);
+        constexpr int ND = NW / 4;
+        uint32_t qlw[ND], qhw[ND], hv[ND], lv[ND];
+        if constexpr (NW == 16) {
+            qlw[0] = r.ql.x; qlw[1] = r.ql.y; qlw[2] = r.ql.z; qlw[3] = r.ql.w;
+            qhw[0] = r.qh.x; qhw[1] = r.qh.y; qhw[2] = r.qh.z; qhw[3] = r.qh.w;
+        } else if constexpr (NW == 8) {
+            qlw[0] = r.ql.x; qlw[1] = r.ql.y;
+            qhw[0] = r.qh.x; qhw[1] = r.qh.y;
+        } else {
+            qlw[0] = r.ql;
+            qhw[0] = r.qh;
+        }
+#pragma unroll
+        for (int i = 0; i < ND; i++) {
+            const uint32_t q = ((qlw[i] >> sh) & 0x0F0F0F0Fu) | (((qhw[i] >> hs) & 0x03030303u) << 4);
+            expand4(q, sc2, c2, hv[i], lv[i]);
+        }
+        uint8_t *dst = smem + buf * L::STAGE + L::A + ea * 2048 + 16 * el + esub;
+        if constexpr (NW == 16) {
+            *(uint4 *)dst = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+            *(uint4 *)(dst + 1024) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+        } else if constexpr (NW == 8) {
+            *(uint2 *)dst = make_uint2(hv[0], hv[1]);
+            *(uint2 *)(dst + 1024) = make_uint2(lv[0], lv[1]);
+        } else {
+            *(uint32_t *)dst = hv[0];
+            *(uint32_t *)(dst + 1024) = lv[0];
+        }
     };
 
-    float accf[TPW][16], Y[TPW][16];
-#pragma unroll
-    for (int t = 0; t < TPW; t++)
-#pragma unroll
-        for (int v = 0; v < 16; v++) { Y[t][v] = 0.f; accf[t][v] = 0.f; }
+    // ---- the workgroup's d values, [super-block][64 rows] fp16, staged once (an array of its
+    // own: its reads need not wait for the direct loads into the ring)
+    __shared__ __attribute__((aligned(16))) uint16_t sd[MAXSB * BN];
+    for (int i = tid; i < BN * nsb; i += L::THREADS) {
+        const int r = i / nsb, s = i - r * nsb;
+        sd[s * BN + r] = dp[(int64_t)min(n0 + r, N - 1) * nsb + s];
+    }
 
-    // One step: compute st from LDS buffer st & 1 while the loads of a later step are in
-    // flight, then expand step st + 1 into the other buffer.  With PD = 1 the loads of
-    // st + 1 are issued at the top of st (one set of registers); with PD = 2 the loads of
-    // st + 2 go into the set step st has just released (two sets, alternating by parity,
-    // so the set is chosen at compile time).  The ql/qh bytes of a half are loaded by its
-    // first step; its second step reuses them.
-    auto step = [&](int st, Raw &cur, Raw &nxt) {
-        const int buf = st & 1;
-        float xsc[TPW][2];
+    // ---- the pipelined contraction: this wave's one 32 x 32 tile
+    float acc[16], Y[16];
+    v16i Ip;         // I32 of the wave's previous block
+    float xsp = 0.f; // its activation scale
 #pragma unroll
-        for (int t = 0; t < TPW; t++) { xsc[t][0] = cur.xsv[t].x; xsc[t][1] = cur.xsv[t].y; }
-        // The prefetch is unconditional (past the end it re-reads the last step, unused): a
-        // branch around it would make the compiler wait for these loads at the join, i.e.
-        // before this step's MFMAs, costing a memory round trip per step.
-        if (PD == 1) {
-            fetch(st + 1 < nsteps ? st + 1 : nsteps - 1, cur);
+    for (int v = 0; v < 16; v++) { acc[v] = 0.f; Y[v] = 0.f; Ip[v] = 0; }
+    const int tok = m0 + 32 * tg + li;
+
+    // epilogue of the previous block (global block c): `first` when it starts a super-block
+    // (acc = ...); dsb >= 0 when it ends super-block dsb (then Y += d acc)
+    auto finish = [&](bool first, int c, int dsb) {
+        if constexpr (PARTIALS) {
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int n = n0 + 32 * rg + 8 * (v >> 2) + 4 * lg + (v & 3);
+                if (tok < M && n < N) part[((int64_t)tok * N + n) * nblk + c] = Ip[v];
+            }
         } else {
-            if (!EXP && (st & 1) == 1) cur.ra = nxt.ra;  // st + 2 odd: same half as st + 1
-            fetch(st + 2 < nsteps ? st + 2 : nsteps - 2 + (st & 1), cur);
-        }
-
 #pragma unroll
-        for (int cb = 0; cb < 2; cb++) {
-            const int ko = cb * 32 + 16 * lg;
-            const v4i aH = __builtin_bit_cast(v4i, *(const uint4 *)(sH(buf) + (32 * wn + li) * RS + ko));
-            const v4i aL = __builtin_bit_cast(v4i, *(const uint4 *)(sL(buf) + (32 * wn + li) * RS + ko));
+            for (int v = 0; v < 16; v++) acc[v] = first ? (float)Ip[v] * xsp : fmaf((float)Ip[v], xsp, acc[v]);
+            if (dsb >= 0) {
+                // the wave's 16 d values (rows 32 rg + 8 q + 4 lg + e).  Read in one asm block
+                // that also waits for them: compiled LDS reads here would be made to wait for
+                // every direct load in flight (the compiler cannot tell the table apart from
+                // the ring they fill)
+                const uint32_t da = (uint32_t)(uintptr_t)(sd + dsb * BN + 32 * rg + 4 * lg);
+                uint2 d4[4];
+                asm volatile(
+                    "ds_read_b64 %0, %4\n\t"
+                    "ds_read_b64 %1, %4 offset:16\n\t"
+                    "ds_read_b64 %2, %4 offset:32\n\t"
+                    "ds_read_b64 %3, %4 offset:48\n\t"
+                    "s_waitcnt lgkmcnt(0)"
+                    : "=&v"(d4[0]), "=&v"(d4[1]), "=&v"(d4[2]), "=&v"(d4[3])
+                    : "v"(da)
+                    : "memory");
 #pragma unroll
-            for (int t = 0; t < TPW; t++) {
-                const int mc = 32 * (wm * TPW + t) + li;  // tile-local token column of this lane
-                const v4i b = __builtin_bit_cast(v4i, *(const uint4 *)(sB(buf) + mc * RS + ko));
-                // I32 = 64 C_H + C_L: C_H is shifted (one VOP2 shift per value) and handed to
-                // the second MFMA as its accumulator input, which adds C_L exactly
-                const v16i z = {};
-                const v16i cH = __builtin_amdgcn_mfma_i32_32x32x32_i8(aH, b, z, 0, 0, 0);
-                const v16i i32 = __builtin_amdgcn_mfma_i32_32x32x32_i8(aL, b, cH << 6, 0, 0, 0);
-                if (PARTIALS) {
-                    const int m = tok[t], c = st * 2 + cb;
-#pragma unroll
-                    for (int v = 0; v < 16; v++) {
-                        const int n = n0 + 32 * wn + 8 * (v >> 2) + 4 * lg + (v & 3);
-                        if (m < M && n < N) part[((int64_t)m * N + n) * nblk + c] = i32[v];
-                    }
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 16; v++) accf[t][v] = fmaf((float)i32[v], xsc[t][cb], accf[t][v]);
+                for (int q = 0; q < 4; q++) {
+                    const uint2 dd = d4[q];
+                    Y[4 * q + 0] = fmaf(h2f((uint16_t)dd.x), acc[4 * q + 0], Y[4 * q + 0]);
+                    Y[4 * q + 1] = fmaf(h2f((uint16_t)(dd.x >> 16)), acc[4 * q + 1], Y[4 * q + 1]);
+                    Y[4 * q + 2] = fmaf(h2f((uint16_t)dd.y), acc[4 * q + 2], Y[4 * q + 2]);
+                    Y[4 * q + 3] = fmaf(h2f((uint16_t)(dd.y >> 16)), acc[4 * q + 3], Y[4 * q + 3]);
                 }
             }
         }
-        if (!PARTIALS && (st & 3) == 3) {  // end of a super-block: apply d once
-            const float *dcur = sD[(st >> 2) & 1];
-#pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const float4 dv = *(const float4 *)(&dcur[32 * wn + 8 * g + 4 * lg]);
-                const float d4[4] = {dv.x, dv.y, dv.z, dv.w};
-#pragma unroll
-                for (int t = 0; t < TPW; t++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        Y[t][4 * g + e] = fmaf(d4[e], accf[t][4 * g + e], Y[t][4 * g + e]);
-                        accf[t][4 * g + e] = 0.f;
-                    }
-            }
-        }
-        if (st + 1 < nsteps) store(st + 1, buf ^ 1, PD == 1 ? cur : nxt);
-        __syncthreads();
     };
 
-    Raw R0, R1;
-    fetch(0, R0);
-    if (PD == 2 && nsteps > 1) {
-        fetch(1, R1);
-        if (!EXP) R1.ra = R0.ra;  // step 1 is the second step of half 0
+    // one block: fragments, the H product, the previous block's epilogue, then the shifted H
+    // product handed to the L product
+    auto block = [&](int buf, int blk, bool fin, bool fin_first, int fin_c, int fin_dsb) {
+        const uint8_t *s = smem + buf * L::STAGE;
+        const v4i aH = *(const v4i *)(s + L::A + ((rg * KB + blk) * 2 + 0) * 1024 + 16 * lane);
+        const v4i aL = *(const v4i *)(s + L::A + ((rg * KB + blk) * 2 + 1) * 1024 + 16 * lane);
+        const v4i b = *(const v4i *)(s + L::B + (tg * KB + blk) * 1024 + 16 * lane);
+        const float x = *(const float *)(s + L::XS + (blk * 128 + 32 * tg + li) * 4);
+        const v16i z = {};
+        const v16i hp = __builtin_amdgcn_mfma_i32_32x32x32_i8(aH, b, z, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (fin) finish(fin_first, fin_c, fin_dsb);
+        __builtin_amdgcn_sched_barrier(0);
+        Ip = __builtin_amdgcn_mfma_i32_32x32x32_i8(aL, b, hp << 6, 0, 0, 0);
+        xsp = x;
+    };
+
+    Raw<NW> raw[2];
+    dma(0, 0);
+    dma(min(1, nst - 1), 1);
+    dma(min(2, nst - 1), 2);
+    if constexpr (!EXP) {
+        load_raw(0, raw[0]);
+        load_raw(min(1, nst - 1), raw[1]);
+        expand(0, raw[0], 0);
     }
-    store(0, 0, R0);
-    __syncthreads();
-    if (PD == 1) {
-        for (int st = 0; st < nsteps; st++) step(st, R0, R0);
-    } else {
-        for (int st = 0; st < nsteps; st += 2) {  // nsteps is a multiple of 4
-            step(st, R0, R1);
-            step(st + 1, R1, R0);
+
+    // this wave's blocks of a stage: b = kh, kh + KSPLIT, ... < KB; a super-block is SPS stages
+    constexpr int SPS = 256 / KS, JPS = KB / KSPLIT;
+    static_assert(SPS == NSTAGE, "one ring slot per stage of a super-block");
+    for (int S = 0; S < nsb; S++) {
+#pragma unroll
+        for (int sp = 0; sp < SPS; sp++) {
+            const int st = SPS * S + sp, buf = sp;  // slot: compile-time
+            // this wave's direct loads of stage st have landed (those of st + 1 and st + 2, issued
+            // after them, may still be in flight)
+            if (njobs) wait_vmcnt_le(2 * njobs);
+            ring_barrier();        // ... and every wave's, with the expanded weights of st
+            {
+                dma(min(st + 3, nst - 1), (sp + 3) % NSTAGE);  // the slot stage st - 1 used
+                if constexpr (!EXP) load_raw(min(st + 2, nst - 1), raw[sp & 1]);
+            }
+#pragma unroll
+            for (int j = 0; j < JPS; j++) {
+                const int blk = kh + KSPLIT * j;
+                // this wave's previous block and its place in its super-block
+                const bool prev_in_prev_sb = sp == 0 && j == 0;
+                const bool prev_first = JPS * sp + j == 1;
+                const int prev_c = KB * st + blk - KSPLIT;
+                block(buf, blk, !(S == 0 && prev_in_prev_sb), prev_first, prev_c, prev_in_prev_sb ? S - 1 : -1);
+            }
+            if constexpr (!EXP) {
+                if (st + 1 < nst) expand(st + 1, raw[(sp + 1) & 1], (sp + 1) % NSTAGE);
+            }
         }
     }
-    if (PARTIALS) return;
+    finish(false, KB * (nst - 1) + kh + KSPLIT * (JPS - 1), nsb - 1);
+    wait_vmcnt<0>();  // the clamped prefetches of the last stages still write the ring
+    if constexpr (PARTIALS) return;
+
+    if constexpr (KSPLIT == 2) {
+        // the two K parts of each tile are added through LDS (fixed order: kh 0 + kh 1)
+        lds_barrier();
+        float4 *red = (float4 *)smem + ((wave & 7) * 4) * 64 + lane;
+        if (kh == 1) {
 #pragma unroll
-    for (int t = 0; t < TPW; t++) {
-        const int m = tok[t];
-        if (m >= M) continue;
+            for (int q = 0; q < 4; q++) red[q * 64] = make_float4(Y[4 * q], Y[4 * q + 1], Y[4 * q + 2], Y[4 * q + 3]);
+        }
+        lds_barrier();
+        if (kh == 1) return;
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const int n = n0 + 32 * wn + 8 * g + 4 * lg;
-            float *dst = y + (int64_t)m * N + n;
-            if (n + 3 < N && (N & 3) == 0) {
-                *(float4 *)dst = make_float4(Y[t][4 * g], Y[t][4 * g + 1], Y[t][4 * g + 2], Y[t][4 * g + 3]);
-            } else {
+        for (int q = 0; q < 4; q++) {
+            const float4 o = red[q * 64];
+            Y[4 * q] += o.x;
+            Y[4 * q + 1] += o.y;
+            Y[4 * q + 2] += o.z;
+            Y[4 * q + 3] += o.w;
+        }
+    }
+    if (tok >= M) return;
 #pragma unroll
-                for (int e = 0; e < 4; e++)
-                    if (n + e < N) dst[e] = Y[t][4 * g + e];
-            }
+    for (int q = 0; q < 4; q++) {
+        const int n = n0 + 32 * rg + 8 * q + 4 * lg;
+        float *dst = y + (int64_t)tok * N + n;
+        if (n + 3 < N && (N & 3) == 0) {
+            *(float4 *)dst = make_float4(Y[4 * q], Y[4 * q + 1], Y[4 * q + 2], Y[4 * q + 3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                if (n + e < N) dst[e] = Y[4 * q + e];
         }
     }
 }
 
-template <int WN, bool PARTIALS, int PD, bool EXP>
+template <int KSPLIT, int KB>
+constexpr size_t gemm_lds(int64_t) { return Lay<KSPLIT, KB>::RING; }  // dynamic part (the ring)
+
+template <int KSPLIT, int KB, bool EXP, bool PARTIALS>
 void launch_tiles(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs, float *y,
                   int32_t *partials, hipStream_t s) {
-    using G = Geo<WN>;
+    using L = Lay<KSPLIT, KB>;
     const int64_t n = w->n, k = w->k;
-    const dim3 grid((unsigned)((n + G::BN - 1) / G::BN), (unsigned)((m + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm_q6k_kernel<WN, PARTIALS, PD, EXP>), grid, dim3(TB), G::LDS, s, (const uint8_t *)w->codes,
-                       (const uint8_t *)w->codes_hi, (const int8_t *)w->scales, (const uint16_t *)w->super, plane,
-                       plane ? plane + n * k : nullptr, xq, xs, y, partials, m, (int)n, (int)k);
+    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
+    const size_t lds = gemm_lds<KSPLIT, KB>(k);
+    hipLaunchKernelGGL((gemm_q6k_kernel<KSPLIT, KB, EXP, PARTIALS>), grid, dim3(L::THREADS), lds, s,
+                       (const uint8_t *)w->codes, (const uint8_t *)w->codes_hi, (const int8_t *)w->scales,
+                       (const uint16_t *)w->super, plane, xq, xs, y, partials, m, (int)n, (int)k);
 }
 
 template <bool EXP>
 const char *launch_gemm(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs,
                         float *y, int32_t *partials, hipStream_t s) {
-    const int64_t n = w->n;
-    // 64-row tiles when they give at least two workgroups per CU (one, when copying
-    // registered planes: 4096x11008 at M = 512 then runs 288-292 against 276-287 TOPS with
-    // 32-row tiles, while the in-kernel expansion keeps 32-row tiles there, 256-266 against
-    // 220-221), else 32-row tiles
-    const int64_t tiles64 = ((n + 63) / 64) * ((m + BM - 1) / BM);
-    const char *fp = forced_path();  // test-only overrides of the tile width and prefetch distance
-    const bool wide = strcmp(fp, "gemm.w64") == 0 ? true : strcmp(fp, "gemm.w32") == 0 ? false
-                                                      : tiles64 >= (EXP ? 1 : 2) * (int64_t)device_info().num_cus;
     if (partials) {
-        if (wide) launch_tiles<2, true, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
-        else launch_tiles<1, true, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
+        launch_tiles<1, 2, EXP, true>(w, m, plane, xq, xs, y, partials, s);
         return "gemm.q6k.mfma-i8-32x32x32.hl-split.partials";
     }
-    // 64-row tiles that expand codes keep the loads of the next step in flight (their
-    // register budget allows three workgroups per CU); 32-row tiles, and 64-row tiles that
-    // copy registered planes (fewer registers per step), fetch two steps ahead
-    const int pd = strcmp(fp, "gemm.pd1") == 0 ? 1 : strcmp(fp, "gemm.pd2") == 0 ? 2 : (wide && !EXP ? 1 : 2);
-    if (wide) {
-        if (pd == 1) launch_tiles<2, false, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
-        else launch_tiles<2, false, 2, EXP>(w, m, plane, xq, xs, y, partials, s);
-    } else {
-        if (pd == 1) launch_tiles<1, false, 1, EXP>(w, m, plane, xq, xs, y, partials, s);
-        else launch_tiles<1, false, 2, EXP>(w, m, plane, xq, xs, y, partials, s);
-    }
+    // 16-wave workgroups whose two halves take alternate 32-blocks (four waves per SIMD);
+    // "gemm.ks1" forces 8-wave workgroups over all of K.  The choice never depends on EXP, so
+    // the plane and the in-kernel expansion sum in the same order (byte-identical outputs).
+    const char *fp = forced_path();
+    if (strcmp(fp, "gemm.ks1") == 0) launch_tiles<1, 2, EXP, false>(w, m, plane, xq, xs, y, partials, s);
+    else launch_tiles<2, 2, EXP, false>(w, m, plane, xq, xs, y, partials, s);
     return "gemm.q6k.mfma-i8-32x32x32.hl-split";
 }
 
-// Pre-expansion of a q6_K matrix into the planes the EXP kernels copy: for every weight,
-// w' = sc * (q - 32) = 64 h + l with h = w' >> 6 (arithmetic) and l = w' & 63, stored
-// as int8 H[n][k] then L[n][k].  One thread per 64-weight unit (half h, offset 16 odd)
-// of a super-block, as in the dequantizer.
+// Pre-expansion of a q6_K matrix into the plane the EXP kernels load: for every weight,
+// w' = sc * (q - 32) = 64 h + l with h = w' >> 6 (arithmetic) and l = w' & 63, in MFMA
+// fragment order: [row group ceil(n/32)][32-block k/32][h, l][64 lanes][16 B], lane l
+// holding row 32 g + l % 32 and k = 32 c + 16 (l / 32) .. + 15 (rows past n are zero).
+// One thread per lane chunk (16 weights).
 __global__ void __launch_bounds__(256) expand_q6k_planes(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh,
-                                                         const int8_t *__restrict__ sc, int8_t *__restrict__ H,
-                                                         int8_t *__restrict__ L, int64_t nunits) {
+                                                         const int8_t *__restrict__ sc, int8_t *__restrict__ plane,
+                                                         int n, int k, int64_t nchunks) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= nunits) return;
-    const int64_t sb = i >> 2;
-    const int h = (int)((i >> 1) & 1), odd = (int)(i & 1);
-    const uint8_t *a = ql + sb * 128 + 64 * h + 16 * odd;
-    const uint8_t *hb = qh + sb * 64 + 32 * h + 16 * odd;
-    const int64_t e0 = sb * 256 + 128 * h + 16 * odd;
-#pragma unroll
-    for (int t = 0; t < 4; t++) {
-        const int s = sc[sb * 16 + 8 * h + 2 * t + odd];
+    if (i >= nchunks) return;
+    const int l = (int)(i & 63);
+    const int64_t gc = i >> 6;
+    const int nblk = k >> 5;
+    const int64_t g = gc / nblk;
+    const int c = (int)(gc - g * nblk);
+    const int64_t row = 32 * g + (l & 31);
+    uint8_t hb[16], lb[16];
+    if (row < n) {
+        const int k0 = 32 * c + 16 * (l >> 5), s = k0 >> 8, e0 = k0 & 255;
+        const int h = e0 >> 7, t = (e0 >> 5) & 3, lo = e0 & 31;
+        const uint8_t *a = ql + row * (k >> 1) + 128 * s + 64 * h + 32 * (t & 1) + lo;
+        const uint8_t *b = qh + row * (k >> 2) + 64 * s + 32 * h + lo;
+        const int scv = sc[row * (k >> 4) + 16 * s + (e0 >> 4)];
         for (int j = 0; j < 16; j++) {
-            const int q = ((a[j + 32 * (t & 1)] >> (4 * (t >> 1))) & 15) | (((hb[j] >> (2 * t)) & 3) << 4);
-            const int wv = s * (q - 32);
-            H[e0 + 32 * t + j] = (int8_t)(wv >> 6);
-            L[e0 + 32 * t + j] = (int8_t)(wv & 63);
+            const int q = ((a[j] >> (4 * (t >> 1))) & 15) | (((b[j] >> (2 * t)) & 3) << 4);
+            const int wv = scv * (q - 32);
+            hb[j] = (uint8_t)(wv >> 6);
+            lb[j] = (uint8_t)(wv & 63);
         }
+    } else {
+        for (int j = 0; j < 16; j++) hb[j] = lb[j] = 0;
+    }
+    int8_t *dst = plane + gc * 2048 + 16 * l;
+    for (int j = 0; j < 16; j++) {
+        dst[j] = (int8_t)hb[j];
+        dst[1024 + j] = (int8_t)lb[j];
     }
 }
 
 }  // namespace
 
+int64_t gemm_plane_bytes(int64_t n, int64_t k) { return 2 * ((n + 31) / 32) * 32 * k; }
+
 const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs,
                             float *y, int32_t *partials, hipStream_t s) {
     const int64_t n = w->n, k = w->k;
-    if (n > INT32_MAX || k > INT32_MAX || (int64_t)m * k > INT32_MAX) return nullptr;
+    if (n > INT32_MAX - 64 || k > INT32_MAX || (int64_t)m * k > INT32_MAX || (m + BM - 1) / BM > 65535) return nullptr;
+    // the workgroup's d values are staged in LDS once: 64 rows x k/256 fp16
+    if (k / 256 > MAXSB) return nullptr;
     return plane ? launch_gemm<true>(w, m, plane, xq, xs, y, partials, s)
                  : launch_gemm<false>(w, m, nullptr, xq, xs, y, partials, s);
 }
 
 const char *launch_expand_q6k(const qmv_weights *w, int8_t *plane, hipStream_t s) {
-    const int64_t nunits = w->n * w->k / 64;
-    if (nunits > (int64_t)INT32_MAX * 256) return nullptr;
-    hipLaunchKernelGGL(expand_q6k_planes, dim3((unsigned)((nunits + 255) / 256)), dim3(256), 0, s,
+    const int64_t nchunks = gemm_plane_bytes(w->n, w->k) / 32;
+    if (nchunks > (int64_t)INT32_MAX * 256) return nullptr;
+    hipLaunchKernelGGL(expand_q6k_planes, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, s,
                        (const uint8_t *)w->codes, (const uint8_t *)w->codes_hi, (const int8_t *)w->scales, plane,
-                       plane + w->n * w->k, nunits);
+                       (int)w->n, (int)w->k, nchunks);
     return "plane.q6k.expand";
 }
 

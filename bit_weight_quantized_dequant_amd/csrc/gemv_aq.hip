@@ -222,9 +222,9 @@ __global__ void __launch_bounds__(WG) aq_ragged_kernel(const uint8_t *__restrict
 
     for (int k0 = 0; k0 < k; k0 += KC) {
         const int kc = min(KC, k - k0);
-        if (k0) __syncthreads();  // previous chunk fully consumed
+        if (k0) lds_barrier();  // previous chunk fully consumed
         stage_chunk<M, XT>(x, k, k0, kc, sx);
-        __syncthreads();
+        lds_barrier();
         const int e0 = lane * 64;  // first weight of this lane's unit within the chunk
         if (row < n && e0 < kc) {
             const int ng = min(8, (kc - e0) >> 3);

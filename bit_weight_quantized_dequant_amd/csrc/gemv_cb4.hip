@@ -193,7 +193,7 @@ __global__ void __launch_bounds__(WG) cb4_kernel(Cb4Args a) {
     for (int j = 0; j < XPT; j++) dst[j * (WG / 8) * (XS / 4)] = xv[j];
     store_tables<CPL>(r0, tab0, nchunk, lane);
     if (NT == 2) store_tables<CPL>(r1, tab1, nchunk, lane);
-    __syncthreads();
+    lds_barrier();
 
     if (JOB == JOB_GEMV) {
 #pragma unroll
@@ -349,12 +349,12 @@ __global__ void __launch_bounds__(WG) cb4_chunked_kernel(const uint8_t *__restri
         for (int m = 0; m < M; m++) xv[m] = ld_act4<XT>(x, (int64_t)m * k + k0 + 4 * t);
         load_step(fill, idx_row, cb_row, c + 1, nchunk, lane);
         __builtin_amdgcn_sched_barrier(0);  // every load is issued before the LDS writes wait
-        if (c) __syncthreads();  // the previous step's activations and tables are consumed
+        if (c) lds_barrier();  // the previous step's activations and tables are consumed
 #pragma unroll
         for (int m = 0; m < M; m++)
             *(float4 *)(sx + m * RXS + (threadIdx.x >> 3) * XS + (threadIdx.x & 7) * 4) = xv[m];
         *(float4 *)(tab + 4 * lane) = make_float4(lo_h(use.t.x), hi_h(use.t.x), lo_h(use.t.y), hi_h(use.t.y));
-        __syncthreads();
+        lds_barrier();
         const int ci = c * 64 + lane;
         const int lc = ci < nchunk ? lane : nchunk - 1 - c * 64;
         float s[M];

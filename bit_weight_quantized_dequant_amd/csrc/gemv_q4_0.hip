@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_kernel(const uint8_t *
     float4 *dst = sx4 + (threadIdx.x >> 3) * XS4 + (threadIdx.x & 7);
 #pragma unroll
     for (int j = 0; j < XPT; j++) dst[j * (WG / 8) * XS4] = xv[j];
-    __syncthreads();
+    lds_barrier();
 
     // each block's 32 activations are read from LDS once per batch row and used for all R rows
     float acc[R][M];
@@ -281,13 +281,13 @@ __global__ void __launch_bounds__(WG) gemv_q4_0_chunked_kernel(const uint8_t *__
         const uint4 qn = ld_stream16(qr + bn);
         const uint16_t dn = dr[bn];
         __builtin_amdgcn_sched_barrier(0);
-        if (c) __syncthreads();  // the previous chunk's activations are consumed
+        if (c) lds_barrier();  // the previous chunk's activations are consumed
 #pragma unroll
         for (int j = 0; j < XPT; j++) {
             const int cc = threadIdx.x + j * WG, m = cc >> 9, e = cc & 511;
             if (XPT * WG == NX || cc < NX) sx4[(m * 64 + (e >> 3)) * XS4 + (e & 7)] = xv[j];
         }
-        __syncthreads();
+        lds_barrier();
         const int b = c * 64 + lane;
         const float d = h2f(dc);
         if constexpr (M <= 2) {

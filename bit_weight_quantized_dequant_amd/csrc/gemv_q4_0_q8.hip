@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(WG, 512 / WG) gemv_q4_0_q8_kernel(const uint8_
         xhi[slot] = xb[j];
         meta[slot] = make_float2(sv[j], __int_as_float(-8 * sum));
     }
-    __syncthreads();
+    lds_barrier();
 
     float acc[M];
 #pragma unroll

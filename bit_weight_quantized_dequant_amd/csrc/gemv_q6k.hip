@@ -191,14 +191,14 @@ __global__ void __launch_bounds__(WGT, M == 4 ? 4 : 2) gemv_q6k_kernel(const uin
         const int un = (c + 1) * CU + ul;
         load_unit(fill, ql, qh, scp, dp, rowc, k, un < nu ? un : nu - 1);
         __builtin_amdgcn_sched_barrier(0);  // every load is issued before the LDS writes wait
-        if (c) __syncthreads();  // the previous chunk's activations are consumed
+        if (c) lds_barrier();  // the previous chunk's activations are consumed
 #pragma unroll
         for (int j = 0; j < XPT; j++) {
             const int p = threadIdx.x + j * WGT, m = p / (CU * 16), e = 4 * (p % (CU * 16));
             const int slot = 4 * (e >> 8) + 2 * ((e >> 7) & 1) + ((e >> 4) & 1);
             *(float4 *)(sx + (m * CU + slot) * US + 16 * ((e >> 5) & 3) + (e & 15)) = xv[j];
         }
-        __syncthreads();
+        lds_barrier();
         const int u = c * CU + ul;
         const int uc = u < nu ? u : nu - 1;
         if constexpr (M >= 3) {

@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(WG, 512 / WG) gemv_q6k_q8_kernel(const uint8_t
         xr16[slot] = xv[j];
         meta[slot] = make_float2(sv[j], __int_as_float(-32 * sum));
     }
-    __syncthreads();
+    lds_barrier();
 
     float acc[M];
 #pragma unroll

@@ -93,7 +93,7 @@ QMV_DEV void walk_row(const P &pol, const void *x, int k, float *sx, float (&acc
     pol.load(c0, lane < nunits ? lane : nunits - 1);
     __builtin_amdgcn_sched_barrier(0);
     store_x<M, L>(xv, sx);
-    __syncthreads();
+    lds_barrier();
 
     // One step; MORE = there is a next step to prefetch.  The choice is made outside the
     // step so that each step is straight-line code: a branch around the prefetch loads
@@ -118,9 +118,9 @@ QMV_DEV void walk_row(const P &pol, const void *x, int k, float *sx, float (&acc
 #pragma unroll
         for (int m = 0; m < RM; m++) acc[m] = u < nunits ? acc[m] + s[m] : acc[m];
         if (MORE) {
-            if (!TWO) __syncthreads();  // every wave is done with the only buffer
+            if (!TWO) lds_barrier();  // every wave is done with the only buffer
             store_x<M, L>(xv, sx + (TWO ? ((c + 1) & 1) * M * XB : 0));
-            __syncthreads();
+            lds_barrier();
         }
     };
     using Y = std::true_type;

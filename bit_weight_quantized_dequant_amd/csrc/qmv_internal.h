@@ -44,11 +44,14 @@ const char *launch_dequant(const qmv_weights *w, float *out, hipStream_t s);
 // The stream-read ceiling: reads `bytes` (a multiple of 16) from p and nothing else.
 const char *launch_read_ceiling(const void *p, int64_t bytes, uint32_t *sink, hipStream_t s);
 const char *launch_quant_act(const float *x, int m, int64_t k, int8_t *xq, float *xs, hipStream_t s);
-// plane: the registered pre-expanded H/L planes of w (int8 [n][k] each, H then L), or
-// nullptr for the in-kernel expansion of the codes.
+// plane: the registered pre-expanded plane of w (h and l bytes in MFMA fragment order, see
+// qmm_plane_bytes), or nullptr for the in-kernel expansion of the codes.
 const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs,
                             float *y, int32_t *partials, hipStream_t s);
 const char *launch_expand_q6k(const qmv_weights *w, int8_t *plane, hipStream_t s);
+// Bytes of the pre-expanded q6_K plane of an n x k matrix (32-row groups in MFMA fragment
+// order, h and l bytes).
+int64_t gemm_plane_bytes(int64_t n, int64_t k);
 const char *launch_moe_cb4(const qmv_weights *gate, const qmv_weights *up, const qmv_weights *down,
                            int n_experts, const int32_t *ids, int n_ids, const void *x, int xt,
                            float *h, float *y, hipStream_t s);

@@ -215,7 +215,9 @@ int64_t qmm_workspace_bytes(const qmv_weights *w, int32_t m);
  * in-kernel ql/qh expansion into centred int8).
  *   w: QMV_Q6_K only; x: fp32 [m][k]; y: fp32 [m][n]; ws: device workspace of at least
  *   qmm_workspace_bytes(w, m) bytes (holds xq and xs; contents on return unspecified).
- *   Runs qmm_quant_act, then the contraction.  m >= 1; k % 256 == 0.
+ *   Runs qmm_quant_act, then the contraction.  m >= 1 (at most 65535 * 128); k % 256 == 0
+ *   and k <= 20480 (each workgroup stages its 64 rows' d values for all of k in LDS beside
+ *   a 54 KiB operand ring); QMV_ERR_LIMIT beyond.
  */
 int qmm_gemm(const qmv_weights *w, int32_t m, const float *x, float *y, void *ws, int64_t ws_bytes,
              void *stream);
@@ -253,10 +255,14 @@ int qmm_partials(const qmv_weights *w, int32_t m, const int8_t *xq, int32_t *i32
  * and without it, §2.3; default on with an explicit "0" opt-out and a label that tells
  * the cases apart, §2.4 and §3.1).
  *
- * The planes: for every weight, w' = sc * (q - 32) = 64 H + L with H in [-64, 64] and L in
- * [0, 63]; H int8 [n][k], then L int8 [n][k] (k order), 2 bytes per weight.
+ * The plane: for every weight, w' = sc * (q - 32) = 64 H + L with H in [-64, 64] and L in
+ * [0, 63], 2 bytes per weight, laid out in the int8 MFMA's fragment order so that the GEMM
+ * loads it straight into LDS: [row group g < ceil(n/32)][32-block c < k/32][H, L][lane 64]
+ * [16 bytes], lane l holding row 32 g + l % 32 and k = 32 c + 16 (l / 32) .. + 15 (rows past
+ * n hold 0).
  *
- * qmm_plane_bytes: 2 * n * k for a valid QMV_Q6_K descriptor, else a QMV_ERR_* code.
+ * qmm_plane_bytes: 2 * 32 * ceil(n / 32) * k for a valid QMV_Q6_K descriptor, else a
+ *   QMV_ERR_* code.
  * qmm_register_plane: fills `plane` (device memory owned by the caller, at least
  *   qmm_plane_bytes(w) bytes, 256-byte aligned) from w's codes on `stream`, and records it
  *   for w, keyed by w->codes together with n, k and w's other plane pointers.  qmm_gemm,

@@ -112,18 +112,20 @@ def test_calls_reject_bad_arguments_before_any_gpu_work():
 def test_plane_calls_check_arguments_before_any_gpu_work(monkeypatch):
     L = qmv.lib()
     q6 = _fake(qmv.Q6_K, 8, 512)
-    assert qmv.plane_bytes_of(q6) == 2 * 8 * 512
+    # 2 bytes per weight in whole 32-row groups (fragment order)
+    assert qmv.plane_bytes_of(q6) == 2 * 32 * 512
+    assert qmv.plane_bytes_of(_fake(qmv.Q6_K, 33, 256)) == 2 * 64 * 256
     assert qmv.plane_bytes_of(_fake(qmv.CB4, 8, 512)) == -3        # only q6_K has planes
     assert qmv.plane_bytes_of(_fake(qmv.Q6_K, 8, 300)) == -2
     assert L.qmm_plane_bytes(None) == -1
     base = 1 << 24
-    assert L.qmm_register_plane(q6.ref, None, 8192, None) == -1
-    assert L.qmm_register_plane(q6.ref, base, 8191, None) == -7     # too small
-    assert L.qmm_register_plane(q6.ref, base + 16, 8192, None) == -5  # not 256-byte aligned
+    assert L.qmm_register_plane(q6.ref, None, 32768, None) == -1
+    assert L.qmm_register_plane(q6.ref, base, 32767, None) == -7     # too small
+    assert L.qmm_register_plane(q6.ref, base + 16, 32768, None) == -5  # not 256-byte aligned
     assert L.qmm_register_plane(_fake(qmv.AQ2X8, 8, 512).ref, base, 1 << 20, None) == -3
     # explicit opt-out: nothing is written or recorded, and no GPU work is issued
     monkeypatch.setenv("QMV_Q6K_EXP", "0")
-    assert L.qmm_register_plane(q6.ref, base, 8192, None) == 0
+    assert L.qmm_register_plane(q6.ref, base, 32768, None) == 0
     assert qmv.last_path() == "plane.q6k(exp=off)"
     assert L.qmm_unregister_plane(q6.ref) == 0
     assert L.qmm_unregister_plane(None) == -1

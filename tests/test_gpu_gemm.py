@@ -153,7 +153,13 @@ def test_plane_holds_the_exact_hi_lo_split(qmv):
         p = plane.cpu().numpy().view(np.int8).astype(np.int64)
     finally:
         qmv.unregister_plane(W)
-    H, L = p[: n * k].reshape(n, k), p[n * k: 2 * n * k].reshape(n, k)
+    # [row group][32-block][H, L][lane][16]: lane l holds row 32 g + l % 32, k 32 c + 16 (l / 32) ..
+    G = -(-n // 32)
+    assert p.size == 2 * 32 * G * k
+    f = p.reshape(G, k // 32, 2, 2, 32, 16)            # [g][c][H/L][l // 32][l % 32][16]
+    f = f.transpose(2, 0, 4, 1, 3, 5).reshape(2, G * 32, k)
+    H, L = f[0][:n], f[1][:n]
+    assert not f[:, n:].any()
     q = oracle.codes(oracle.Mat(oracle.Q6_K, n, k, w)).astype(np.int64)
     sc = np.repeat(w["sc"].reshape(n, k // 16).astype(np.int64), 16, axis=1)
     assert np.array_equal(64 * H + L, sc * (q - 32))
@@ -162,11 +168,12 @@ def test_plane_holds_the_exact_hi_lo_split(qmv):
 
 @pytest.mark.parametrize("n,k,m", [(64, 512, 128), (70, 768, 45), (257, 2048, 130), (4096, 1024, 512), (3, 256, 1),
                                    (8192, 256, 512)])
-@pytest.mark.parametrize("force", ["", "gemm.pd1", "gemm.pd2", "gemm.w64", "gemm.w32"])
+@pytest.mark.parametrize("force", ["", "gemm.ks1", "gemm.ks2"])
 def test_gemm_with_plane_is_byte_identical(qmv, monkeypatch, n, k, m, force):
     # outputs and int32 partials with the plane equal those of the in-kernel expansion bit
-    # for bit (the expansion is an integer transform), for both tile widths (forced either
-    # way on every shape) and both prefetch distances; the partials also equal the oracle's
+    # for bit (the expansion is an integer transform), with four-wave workgroups and with
+    # eight-wave K-split ones (forced either way on every shape); the partials also equal the
+    # oracle's
     import torch
     monkeypatch.setenv("QMV_FORCE_PATH", force)
     w, x, W, xd = _setup(qmv, n, k, m, seed=n + 7 * m)
