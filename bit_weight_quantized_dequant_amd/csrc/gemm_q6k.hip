@@ -84,16 +84,26 @@ QMV_DEV void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Pins 16 VALU results at this point of the program: without it the compiler sinks a block's
+// epilogue arithmetic towards its next use, behind later blocks' MFMAs, undoing the
+// interleaving of one block's epilogue with the next block's matrix work.
+QMV_DEV void pin16(float (&v)[16]) {
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+                 "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
+}
+
 // The ring's barrier: this wave's LDS operations complete (its reads of the stage about to
 // be refilled, its expanded-weight writes), then s_barrier.  The direct loads of the stage
 // are waited for separately (wait_vmcnt): a workgroup fence here would also wait for the
 // loads already issued for later stages, since they write LDS too.  The empty asm
 // statements keep the compiler from moving memory accesses across the barrier.
 QMV_DEV void ring_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unlimited
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // 16 bytes per lane from global memory straight into LDS at chunk + 16 * lane.
@@ -111,24 +121,6 @@ template <int NW> struct Raw;
 template <> struct Raw<16> { uint4 ql, qh; int sc; };
 template <> struct Raw<8> { uint2 ql, qh; int sc; };
 template <> struct Raw<4> { uint32_t ql, qh; int sc; };
-
-// Waits until at most n of this wave's vector-memory operations are outstanding (n is
-// wave-uniform and at most 10; the count is an immediate, hence the switch).
-QMV_DEV void wait_vmcnt_le(int n) {
-    switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    default: wait_vmcnt<10>(); break;
-    }
-}
 
 // Workgroup: 8 * KSPLIT waves.  Wave w computes MFMA tile (row group w & 1, token group
 // (w >> 1) & 3) of the 64 x 128 workgroup tile, over the 32-blocks of its K part
@@ -173,55 +165,45 @@ gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh, 
     }
     const int nst = K / KS, nblk = K >> 5, nsb = K >> 8, G = (N + 31) >> 5;
 
-    // ---- this wave's direct-load jobs of a stage (job j goes to wave j % WAVES): weight
-    // chunks (EXP), activation chunks, activation-scale words.  Sources are for stage 0.
-    constexpr int NJ = (EXP ? L::NA : 0) + L::NB + (PARTIALS ? 0 : L::NX);
-    constexpr int MAXJ = (NJ + WAVES - 1) / WAVES;
-    const int8_t *jsrc[MAXJ];
-    int jlds[MAXJ], jstep[MAXJ];
-    bool jword[MAXJ];
-    int njobs = 0;
+    // ---- this wave's direct loads of a stage: D16 chunks of 16 bytes per lane (weight chunks
+    // with EXP, then activation chunks; waves past their number repeat one, the same bytes to
+    // the same LDS address) and, on the first NX waves, one word per lane of activation
+    // scales (unless PARTIALS: each such load touches 64 rows, so they are not repeated).
+    // Sources are for stage 0.
+    constexpr int N16 = (EXP ? L::NA : 0) + L::NB;
+    constexpr int D16 = (N16 + WAVES - 1) / WAVES;
+    const bool has_x = !PARTIALS && wave < L::NX;  // wave-uniform
+    const int8_t *src16[D16];
+    int lds16[D16], step16[D16];
 #pragma unroll
-    for (int i = 0; i < MAXJ; i++) {
-        int j = wave + i * WAVES;
-        jsrc[i] = nullptr;
-        jlds[i] = 0;
-        jstep[i] = 0;
-        jword[i] = false;
-        if (j >= NJ) continue;
-        njobs++;
+    for (int i = 0; i < D16; i++) {
+        const int j = (wave + i * WAVES) % N16;
         if (EXP && j < L::NA) {  // weight chunk [row group][block][h/l]
-            const int a = j, r = a / (2 * KB), blk = (a >> 1) % KB, p = a & 1;
+            const int r = j / (2 * KB), blk = (j >> 1) % KB, p = j & 1;
             const int g = min((n0 >> 5) + r, G - 1);
-            jsrc[i] = plane + ((int64_t)g * nblk + blk) * 2048 + p * 1024 + 16 * lane;
-            jlds[i] = L::A + a * 1024;
-            jstep[i] = KB * 2048;
-            continue;
+            src16[i] = plane + ((int64_t)g * nblk + blk) * 2048 + p * 1024 + 16 * lane;
+            lds16[i] = L::A + j * 1024;
+            step16[i] = KB * 2048;
+        } else {  // activation chunk [token group][block]
+            const int b = j - (EXP ? L::NA : 0), t = b / KB, blk = b % KB;
+            const int tk = min(m0 + 32 * t + li, M - 1);
+            src16[i] = xq + (int64_t)tk * K + 32 * blk + 16 * lg;
+            lds16[i] = L::B + b * 1024;
+            step16[i] = KS;
         }
-        j -= EXP ? L::NA : 0;
-        if (j < L::NB) {  // activation chunk [token group][block]
-            const int t = j / KB, blk = j % KB;
-            const int tok = min(m0 + 32 * t + li, M - 1);
-            jsrc[i] = xq + (int64_t)tok * K + 32 * blk + 16 * lg;
-            jlds[i] = L::B + j * 1024;
-            jstep[i] = KS;
-            continue;
-        }
-        j -= L::NB;  // activation scales: entries 64 j + lane of [block][128 tokens]
-        const int e = 64 * j + lane;
-        jsrc[i] = (const int8_t *)(xs + (int64_t)min(m0 + (e & 127), M - 1) * nblk + (e >> 7));
-        jlds[i] = L::XS + 4 * 64 * j;
-        jstep[i] = 4 * KB;
-        jword[i] = true;
+    }
+    const float *srcx = nullptr;  // entries 64 jx + lane of [block][128 tokens]
+    int ldsx = 0;
+    if constexpr (!PARTIALS) {
+        const int jx = wave % L::NX, e = 64 * jx + lane;
+        srcx = xs + (int64_t)min(m0 + (e & 127), M - 1) * nblk + (e >> 7);
+        ldsx = L::XS + 256 * jx;
     }
     auto dma = [&](int st, int buf) {
         uint8_t *s = smem + buf * L::STAGE;
 #pragma unroll
-        for (int i = 0; i < MAXJ; i++) {
-            if (i >= njobs) break;
-            if (jword[i]) dma4(jsrc[i] + (int64_t)st * jstep[i], s + jlds[i]);
-            else dma16(jsrc[i] + (int64_t)st * jstep[i], s + jlds[i]);
-        }
+        for (int i = 0; i < D16; i++) dma16(src16[i] + (int64_t)st * step16[i], s + lds16[i]);
+        if (has_x) dma4(srcx + KB * st, s + ldsx);
     };
 
     // ---- in-kernel expansion role (no EXP): lane chunk eu of the stage's weight tile
@@ -293,26 +275,34 @@ gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh, 
         sd[s * BN + r] = dp[(int64_t)min(n0 + r, N - 1) * nsb + s];
     }
 
-    // ---- the pipelined contraction: this wave's one 32 x 32 tile
+    // ---- the pipelined contraction: this wave's one 32 x 32 tile.  Two blocks are in flight:
+    // at the wave's block j it reads j's fragments, issues the L product of block j - 1 (whose
+    // H product was issued a stage earlier), forms the epilogue of block j - 2 (whose L product
+    // was issued a stage earlier), and issues the H product of block j.  Every matrix result
+    // is read one barrier interval after it was issued.
     float acc[16], Y[16];
-    v16i Ip;         // I32 of the wave's previous block
-    float xsp = 0.f; // its activation scale
+    v16i Hs = {};       // H product of block j - 1
+    v16i I2 = {};       // I32 of block j - 2
+    v4i aLp = {}, bp = {};
+    float x1 = 0.f, x2 = 0.f;  // activation scales of blocks j - 1 and j - 2
 #pragma unroll
-    for (int v = 0; v < 16; v++) { acc[v] = 0.f; Y[v] = 0.f; Ip[v] = 0; }
+    for (int v = 0; v < 16; v++) { acc[v] = 0.f; Y[v] = 0.f; }
     const int tok = m0 + 32 * tg + li;
 
-    // epilogue of the previous block (global block c): `first` when it starts a super-block
-    // (acc = ...); dsb >= 0 when it ends super-block dsb (then Y += d acc)
-    auto finish = [&](bool first, int c, int dsb) {
+    // epilogue of block c: `first` when it starts a super-block (acc = ...); dsb >= 0 when
+    // it ends super-block dsb (then Y += d acc)
+    auto finish = [&](const v16i &I, float xv, bool first, int c, int dsb) {
         if constexpr (PARTIALS) {
+            if (c < 0) return;
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int n = n0 + 32 * rg + 8 * (v >> 2) + 4 * lg + (v & 3);
-                if (tok < M && n < N) part[((int64_t)tok * N + n) * nblk + c] = Ip[v];
+                if (tok < M && n < N) part[((int64_t)tok * N + n) * nblk + c] = I[v];
             }
         } else {
 #pragma unroll
-            for (int v = 0; v < 16; v++) acc[v] = first ? (float)Ip[v] * xsp : fmaf((float)Ip[v], xsp, acc[v]);
+            for (int v = 0; v < 16; v++) acc[v] = first ? (float)I[v] * xv : fmaf((float)I[v], xv, acc[v]);
+            pin16(acc);
             if (dsb >= 0) {
                 // the wave's 16 d values (rows 32 rg + 8 q + 4 lg + e).  Read in one asm block
                 // that also waits for them: compiled LDS reads here would be made to wait for
@@ -337,25 +327,33 @@ gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh, 
                     Y[4 * q + 2] = fmaf(h2f((uint16_t)dd.y), acc[4 * q + 2], Y[4 * q + 2]);
                     Y[4 * q + 3] = fmaf(h2f((uint16_t)(dd.y >> 16)), acc[4 * q + 3], Y[4 * q + 3]);
                 }
+                pin16(Y);
             }
         }
     };
 
-    // one block: fragments, the H product, the previous block's epilogue, then the shifted H
-    // product handed to the L product
-    auto block = [&](int buf, int blk, bool fin, bool fin_first, int fin_c, int fin_dsb) {
+    // the wave's block j (its q-th of super-block S; global block c) in ring slot buf.  Block
+    // j - 2 is the first of its super-block when q == 2 and the last when q == 1.
+    constexpr int BPS = 8 / KSPLIT;  // the wave's blocks per super-block
+    auto block = [&](int buf, int blk, int q, int S, int c) {
         const uint8_t *s = smem + buf * L::STAGE;
         const v4i aH = *(const v4i *)(s + L::A + ((rg * KB + blk) * 2 + 0) * 1024 + 16 * lane);
         const v4i aL = *(const v4i *)(s + L::A + ((rg * KB + blk) * 2 + 1) * 1024 + 16 * lane);
         const v4i b = *(const v4i *)(s + L::B + (tg * KB + blk) * 1024 + 16 * lane);
         const float x = *(const float *)(s + L::XS + (blk * 128 + 32 * tg + li) * 4);
+        __builtin_amdgcn_sched_barrier(0);
+        const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(aLp, bp, Hs << 6, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(I2, x2, q == 2, c - 2 * KSPLIT, q == 1 ? max(S - 1, 0) : (BPS == 2 && q == 0 ? max(S - 1, 0) : -1));
+        __builtin_amdgcn_sched_barrier(0);
         const v16i z = {};
-        const v16i hp = __builtin_amdgcn_mfma_i32_32x32x32_i8(aH, b, z, 0, 0, 0);
+        Hs = __builtin_amdgcn_mfma_i32_32x32x32_i8(aH, b, z, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (fin) finish(fin_first, fin_c, fin_dsb);
-        __builtin_amdgcn_sched_barrier(0);
-        Ip = __builtin_amdgcn_mfma_i32_32x32x32_i8(aL, b, hp << 6, 0, 0, 0);
-        xsp = x;
+        I2 = I1;
+        x2 = x1;
+        x1 = x;
+        aLp = aL;
+        bp = b;
     };
 
     Raw<NW> raw[2];
@@ -371,14 +369,16 @@ gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh, 
     // this wave's blocks of a stage: b = kh, kh + KSPLIT, ... < KB; a super-block is SPS stages
     constexpr int SPS = 256 / KS, JPS = KB / KSPLIT;
     static_assert(SPS == NSTAGE, "one ring slot per stage of a super-block");
+    static_assert(BPS == JPS * SPS && BPS >= 3, "blocks per super-block");
     for (int S = 0; S < nsb; S++) {
 #pragma unroll
         for (int sp = 0; sp < SPS; sp++) {
             const int st = SPS * S + sp, buf = sp;  // slot: compile-time
             // this wave's direct loads of stage st have landed (those of st + 1 and st + 2, issued
             // after them, may still be in flight)
-            if (njobs) wait_vmcnt_le(2 * njobs);
-            ring_barrier();        // ... and every wave's, with the expanded weights of st
+            if (has_x) wait_vmcnt<2 * (D16 + 1)>();
+            else wait_vmcnt<2 * D16>();
+            ring_barrier();  // ... and every wave's, with the expanded weights of st
             {
                 dma(min(st + 3, nst - 1), (sp + 3) % NSTAGE);  // the slot stage st - 1 used
                 if constexpr (!EXP) load_raw(min(st + 2, nst - 1), raw[sp & 1]);
@@ -386,18 +386,20 @@ gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh, 
 #pragma unroll
             for (int j = 0; j < JPS; j++) {
                 const int blk = kh + KSPLIT * j;
-                // this wave's previous block and its place in its super-block
-                const bool prev_in_prev_sb = sp == 0 && j == 0;
-                const bool prev_first = JPS * sp + j == 1;
-                const int prev_c = KB * st + blk - KSPLIT;
-                block(buf, blk, !(S == 0 && prev_in_prev_sb), prev_first, prev_c, prev_in_prev_sb ? S - 1 : -1);
+                block(buf, blk, JPS * sp + j, S, KB * st + blk);
             }
             if constexpr (!EXP) {
                 if (st + 1 < nst) expand(st + 1, raw[(sp + 1) & 1], (sp + 1) % NSTAGE);
             }
         }
     }
-    finish(false, KB * (nst - 1) + kh + KSPLIT * (JPS - 1), nsb - 1);
+    // drain: the last block's L product, then the epilogues of the last two blocks
+    {
+        const int clast = KB * (nst - 1) + kh + KSPLIT * (JPS - 1);
+        const v16i I1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(aLp, bp, Hs << 6, 0, 0, 0);
+        finish(I2, x2, false, clast - KSPLIT, -1);
+        finish(I1, x1, false, clast, nsb - 1);
+    }
     wait_vmcnt<0>();  // the clamped prefetches of the last stages still write the ring
     if constexpr (PARTIALS) return;
 
