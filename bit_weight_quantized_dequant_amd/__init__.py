@@ -14,7 +14,7 @@ import weakref
 __all__ = [
     "Q4_0", "Q6_K", "CB4", "AQ2X8", "CB8", "AQ3X8", "F32", "BF16", "QmvError", "QWeights", "lib", "plane_bytes",
     "weight_bytes", "validate", "gemv", "dequant", "quant_act", "workspace_bytes", "gemm",
-    "gemm_q8", "gemm_noalloc", "partials", "plane_bytes_of", "register_plane", "unregister_plane", "moe_ffn", "last_path",
+    "gemm_q8", "gemm_ws", "gemm_noalloc", "partials", "plane_bytes_of", "register_plane", "unregister_plane", "moe_ffn", "last_path",
     "strerror", "PLANES",
 ]
 
@@ -90,6 +90,8 @@ def lib():
         L.qmm_gemm_q8.argtypes = [P, I32, P, P, P, P]
         L.qmm_partials.restype = C.c_int
         L.qmm_partials.argtypes = [P, I32, P, P, P]
+        L.qmm_gemm_ws.restype = C.c_int
+        L.qmm_gemm_ws.argtypes = [P, I32, P, I64, P, P]
         L.qmm_gemm_noalloc.restype = C.c_int
         L.qmm_gemm_noalloc.argtypes = [P, I32, P, P, P]
         L.qmm_plane_bytes.restype = I64
@@ -286,6 +288,20 @@ def gemm(w: QWeights, x, y=None, ws=None, stream=None):
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     _need(ws, (torch.uint8,), None, "ws")
     _check(lib().qmm_gemm(w.ref, m, _ptr(x), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)), "qmm_gemm")
+    return y
+
+
+def gemm_ws(w: QWeights, ws, y=None, m=None, stream=None):
+    """qmm_gemm_ws: the contraction alone, on the activations a previous gemm() with the same
+    m and k quantized into ws (uint8 device tensor); y fp32 [m][n] allocated unless given."""
+    import torch
+    if m is None:
+        m = y.shape[0]
+    _need(ws, (torch.uint8,), None, "ws")
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=ws.device)
+    _need(y, (torch.float32,), (m, w.n), "y")
+    _check(lib().qmm_gemm_ws(w.ref, m, _ptr(ws), ws.numel(), _ptr(y), _stream(stream)), "qmm_gemm_ws")
     return y
 
 

@@ -263,9 +263,17 @@ int64_t qmm_workspace_bytes(const qmv_weights *w, int32_t m) {
     if (w->fmt != QMV_Q6_K) return QMV_ERR_FORMAT;
     if (w->n <= 0 || w->k <= 0 || w->k % 256) return QMV_ERR_SHAPE;
     if (m < 1) return QMV_ERR_BATCH;
-    // xq int8 [m][k], then xs fp32 [m][k/32] at a 256-byte aligned offset.
-    const int64_t xq = ((int64_t)m * w->k + 255) / 256 * 256;
-    return xq + (int64_t)m * (w->k / 32) * 4;
+    // the GEMM's activation layout for mp = m rounded up to 128 tokens: xq int8 in MFMA
+    // fragment order (mp * k bytes), then xs fp32 [k/32][mp] at a 256-byte aligned offset
+    const int64_t mp = gemm_tokens(m);
+    return (mp * w->k + 255) / 256 * 256 + mp * (w->k / 32) * 4;
+}
+
+// The quantized activations' place in a qmm_gemm workspace.
+static void ws_parts(const qmv_weights *w, int32_t m, void *ws, int8_t **xq, float **xs) {
+    const int64_t mp = gemm_tokens(m);
+    *xq = (int8_t *)ws;
+    *xs = (float *)((char *)ws + (mp * w->k + 255) / 256 * 256);
 }
 
 static int check_gemm(const qmv_weights *w, int32_t m) {
@@ -283,7 +291,22 @@ int qmm_gemm_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *
     if (!xq || !xs || !y) return QMV_ERR_NULL;
     if (!aligned16(xq) || !aligned16(xs) || !aligned16(y)) return QMV_ERR_ALIGN;
     return gemm_with_plane("qmm_gemm_q8", w, m, [&](const int8_t *plane) {
-        return launch_gemm_q6k(w, m, plane, xq, xs, y, nullptr, (hipStream_t)stream);
+        return launch_gemm_q6k(w, m, plane, xq, xs, y, nullptr, (hipStream_t)stream, false);
+    });
+}
+
+int qmm_gemm_ws(const qmv_weights *w, int32_t m, const void *ws, int64_t ws_bytes, float *y, void *stream) {
+    int rc = check_gemm(w, m);
+    if (rc) return rc;
+    if (!y) return QMV_ERR_NULL;
+    const int64_t need = qmm_workspace_bytes(w, m);
+    if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
+    if (!aligned16(y) || ((uintptr_t)ws & 255u)) return QMV_ERR_ALIGN;
+    int8_t *xq;
+    float *xs;
+    ws_parts(w, m, (void *)ws, &xq, &xs);
+    return gemm_with_plane("qmm_gemm_ws", w, m, [&](const int8_t *plane) {
+        return launch_gemm_q6k(w, m, plane, xq, xs, y, nullptr, (hipStream_t)stream, true);
     });
 }
 
@@ -305,14 +328,15 @@ int qmm_gemm(const qmv_weights *w, int32_t m, const float *x, float *y, void *ws
     const int64_t need = qmm_workspace_bytes(w, m);
     if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
     if (!aligned16(x) || !aligned16(y) || ((uintptr_t)ws & 255u)) return QMV_ERR_ALIGN;
-    int8_t *xq = (int8_t *)ws;
-    float *xs = (float *)((char *)ws + ((int64_t)m * w->k + 255) / 256 * 256);
-    const char *p1 = launch_quant_act(x, m, w->k, xq, xs, (hipStream_t)stream);
+    int8_t *xq;
+    float *xs;
+    ws_parts(w, m, ws, &xq, &xs);
+    const char *p1 = launch_quant_act(x, m, w->k, xq, xs, (hipStream_t)stream, (int)gemm_tokens(m));
     if (!p1) return QMV_ERR_LIMIT;
     rc = finish_launch("qmm_quant_act", w, m, p1);
     if (rc) return rc;
     return gemm_with_plane("qmm_gemm", w, m, [&](const int8_t *plane) {
-        return launch_gemm_q6k(w, m, plane, xq, xs, y, nullptr, (hipStream_t)stream);
+        return launch_gemm_q6k(w, m, plane, xq, xs, y, nullptr, (hipStream_t)stream, true);
     });
 }
 

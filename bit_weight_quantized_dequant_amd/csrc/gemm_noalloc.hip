@@ -2,8 +2,9 @@
 // cannot allocate device memory (code under HIP graph capture, tight serving loops,
 // harnesses that forbid hipMalloc).
 //
-// qmm_gemm quantizes the activations into a workspace (xq int8 [m][k], then xs fp32
-// [m][k/32] at a 256-byte aligned offset) and contracts against it.  Here that workspace is
+// qmm_gemm quantizes the activations into a workspace (int8 codes in MFMA fragment order,
+// then the fp32 block scales at a 256-byte aligned offset, both padded to whole 128-token
+// tiles) and contracts against it.  Here that workspace is
 // a file-scope device array of QMV_NOALLOC_SCRATCH_BYTES.  Every GPU the library runs on
 // holds its own copy until the process ends.  Host code never passes the array's name to
 // a kernel (on the host it is only a stand-in symbol): the device address of each GPU's

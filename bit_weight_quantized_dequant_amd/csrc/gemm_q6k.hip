@@ -138,7 +138,11 @@ struct Lay {
     static constexpr int NW = 16 * 2 * KB * 64 / THREADS;     // weights each thread expands
 };
 
-template <int KSPLIT, int KB, bool EXP, bool PARTIALS>
+// FA: the activations are in the quantizer's GEMM layout (xq in fragment order, xs
+// [k/32][tokens rounded up to 128]), so every activation chunk and a stage's scales are each
+// one contiguous 1 KiB load; otherwise they are read from row-major xq [m][k], xs [m][k/32]
+// (32 rows per activation chunk, 64 per scale load).
+template <int KSPLIT, int KB, bool EXP, bool PARTIALS, bool FA>
 __global__ void __launch_bounds__(512 * KSPLIT, 1)
 gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh, const int8_t *__restrict__ scp,
                 const uint16_t *__restrict__ dp, const int8_t *__restrict__ plane, const int8_t *__restrict__ xq,
@@ -172,7 +176,7 @@ gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh, 
     // Sources are for stage 0.
     constexpr int N16 = (EXP ? L::NA : 0) + L::NB;
     constexpr int D16 = (N16 + WAVES - 1) / WAVES;
-    const bool has_x = !PARTIALS && wave < L::NX;  // wave-uniform
+    const bool has_x = !PARTIALS && wave < (FA ? 1 : L::NX);  // wave-uniform
     const int8_t *src16[D16];
     int lds16[D16], step16[D16];
 #pragma unroll
@@ -186,24 +190,43 @@ gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh, 
             step16[i] = KB * 2048;
         } else {  // activation chunk [token group][block]
             const int b = j - (EXP ? L::NA : 0), t = b / KB, blk = b % KB;
-            const int tk = min(m0 + 32 * t + li, M - 1);
-            src16[i] = xq + (int64_t)tk * K + 32 * blk + 16 * lg;
+            if constexpr (FA) {
+                src16[i] = xq + ((int64_t)((m0 >> 5) + t) * nblk + blk) * 1024 + 16 * lane;
+                step16[i] = KB * 1024;
+            } else {
+                const int tk = min(m0 + 32 * t + li, M - 1);
+                src16[i] = xq + (int64_t)tk * K + 32 * blk + 16 * lg;
+                step16[i] = KS;
+            }
             lds16[i] = L::B + b * 1024;
-            step16[i] = KS;
         }
     }
-    const float *srcx = nullptr;  // entries 64 jx + lane of [block][128 tokens]
-    int ldsx = 0;
+    // activation scales of a stage, [block KB][128 tokens]: with FA one 16-byte load per lane
+    // on wave 0 (lane l: block l / 32, tokens 4 (l % 32) ..); else entries 64 jx + lane, one
+    // word per lane, on waves jx < NX
+    const int mp = (M + BM - 1) / BM * BM;
+    const int8_t *srcx = nullptr;
+    int ldsx = 0, stepx = 0;
     if constexpr (!PARTIALS) {
-        const int jx = wave % L::NX, e = 64 * jx + lane;
-        srcx = xs + (int64_t)min(m0 + (e & 127), M - 1) * nblk + (e >> 7);
-        ldsx = L::XS + 256 * jx;
+        if constexpr (FA) {
+            srcx = (const int8_t *)(xs + (int64_t)(lane >> 5) * mp + m0 + 4 * (lane & 31));
+            ldsx = L::XS;
+            stepx = KB * mp * 4;
+        } else {
+            const int jx = wave % L::NX, e = 64 * jx + lane;
+            srcx = (const int8_t *)(xs + (int64_t)min(m0 + (e & 127), M - 1) * nblk + (e >> 7));
+            ldsx = L::XS + 256 * jx;
+            stepx = KB * 4;
+        }
     }
     auto dma = [&](int st, int buf) {
         uint8_t *s = smem + buf * L::STAGE;
 #pragma unroll
         for (int i = 0; i < D16; i++) dma16(src16[i] + (int64_t)st * step16[i], s + lds16[i]);
-        if (has_x) dma4(srcx + KB * st, s + ldsx);
+        if (has_x) {
+            if constexpr (FA) dma16(srcx + (int64_t)st * stepx, s + ldsx);
+            else dma4(srcx + (int64_t)st * stepx, s + ldsx);
+        }
     };
 
     // ---- in-kernel expansion role (no EXP): lane chunk eu of the stage's weight tile
@@ -440,32 +463,36 @@ gemm_q6k_kernel(const uint8_t *__restrict__ ql, const uint8_t *__restrict__ qh, 
 template <int KSPLIT, int KB>
 constexpr size_t gemm_lds(int64_t) { return Lay<KSPLIT, KB>::RING; }  // dynamic part (the ring)
 
-template <int KSPLIT, int KB, bool EXP, bool PARTIALS>
+template <int KSPLIT, int KB, bool EXP, bool PARTIALS, bool FA>
 void launch_tiles(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs, float *y,
                   int32_t *partials, hipStream_t s) {
     using L = Lay<KSPLIT, KB>;
     const int64_t n = w->n, k = w->k;
     const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
     const size_t lds = gemm_lds<KSPLIT, KB>(k);
-    hipLaunchKernelGGL((gemm_q6k_kernel<KSPLIT, KB, EXP, PARTIALS>), grid, dim3(L::THREADS), lds, s,
+    hipLaunchKernelGGL((gemm_q6k_kernel<KSPLIT, KB, EXP, PARTIALS, FA>), grid, dim3(L::THREADS), lds, s,
                        (const uint8_t *)w->codes, (const uint8_t *)w->codes_hi, (const int8_t *)w->scales,
                        (const uint16_t *)w->super, plane, xq, xs, y, partials, m, (int)n, (int)k);
 }
 
-template <bool EXP>
+template <bool EXP, bool FA>
 const char *launch_gemm(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs,
                         float *y, int32_t *partials, hipStream_t s) {
     if (partials) {
-        launch_tiles<1, 2, EXP, true>(w, m, plane, xq, xs, y, partials, s);
+        launch_tiles<1, 2, EXP, true, false>(w, m, plane, xq, xs, y, partials, s);
         return "gemm.q6k.mfma-i8-32x32x32.hl-split.partials";
     }
-    // 16-wave workgroups whose two halves take alternate 32-blocks (four waves per SIMD);
-    // "gemm.ks1" forces 8-wave workgroups over all of K.  The choice never depends on EXP, so
-    // the plane and the in-kernel expansion sum in the same order (byte-identical outputs).
+    // Eight-wave workgroups over all of K when there are tiles for two per CU; else 16-wave
+    // workgroups whose two halves take alternate 32-blocks.  The choice never depends on EXP
+    // or on the activation layout, so every form sums in the same order (byte-identical
+    // outputs).  Test overrides: "gemm.ks1", "gemm.ks2".
+    const int64_t tiles = ((w->n + BN - 1) / BN) * ((m + BM - 1) / BM);
     const char *fp = forced_path();
-    if (strcmp(fp, "gemm.ks1") == 0) launch_tiles<1, 2, EXP, false>(w, m, plane, xq, xs, y, partials, s);
-    else launch_tiles<2, 2, EXP, false>(w, m, plane, xq, xs, y, partials, s);
-    return "gemm.q6k.mfma-i8-32x32x32.hl-split";
+    const bool ks1 = strcmp(fp, "gemm.ks1") == 0 ? true : strcmp(fp, "gemm.ks2") == 0 ? false
+                                                     : tiles >= 2 * (int64_t)device_info().num_cus;
+    if (ks1) launch_tiles<1, 2, EXP, false, FA>(w, m, plane, xq, xs, y, partials, s);
+    else launch_tiles<2, 2, EXP, false, FA>(w, m, plane, xq, xs, y, partials, s);
+    return FA ? "gemm.q6k.mfma-i8-32x32x32.hl-split" : "gemm.q6k.mfma-i8-32x32x32.hl-split.rowmajor-act";
 }
 
 // Pre-expansion of a q6_K matrix into the plane the EXP kernels load: for every weight,
@@ -512,13 +539,16 @@ __global__ void __launch_bounds__(256) expand_q6k_planes(const uint8_t *__restri
 int64_t gemm_plane_bytes(int64_t n, int64_t k) { return 2 * ((n + 31) / 32) * 32 * k; }
 
 const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs,
-                            float *y, int32_t *partials, hipStream_t s) {
+                            float *y, int32_t *partials, hipStream_t s, bool frag) {
     const int64_t n = w->n, k = w->k;
     if (n > INT32_MAX - 64 || k > INT32_MAX || (int64_t)m * k > INT32_MAX || (m + BM - 1) / BM > 65535) return nullptr;
     // the workgroup's d values are staged in LDS once: 64 rows x k/256 fp16
     if (k / 256 > MAXSB) return nullptr;
-    return plane ? launch_gemm<true>(w, m, plane, xq, xs, y, partials, s)
-                 : launch_gemm<false>(w, m, nullptr, xq, xs, y, partials, s);
+    if (frag && !partials)
+        return plane ? launch_gemm<true, true>(w, m, plane, xq, xs, y, nullptr, s)
+                     : launch_gemm<false, true>(w, m, nullptr, xq, xs, y, nullptr, s);
+    return plane ? launch_gemm<true, false>(w, m, plane, xq, xs, y, partials, s)
+                 : launch_gemm<false, false>(w, m, nullptr, xq, xs, y, partials, s);
 }
 
 const char *launch_expand_q6k(const qmv_weights *w, int8_t *plane, hipStream_t s) {

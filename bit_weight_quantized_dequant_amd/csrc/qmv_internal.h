@@ -43,11 +43,16 @@ const char *launch_gemv_cb8(const qmv_weights *w, int m, const void *x, int xt, 
 const char *launch_dequant(const qmv_weights *w, float *out, hipStream_t s);
 // The stream-read ceiling: reads `bytes` (a multiple of 16) from p and nothing else.
 const char *launch_read_ceiling(const void *p, int64_t bytes, uint32_t *sink, hipStream_t s);
-const char *launch_quant_act(const float *x, int m, int64_t k, int8_t *xq, float *xs, hipStream_t s);
+// mp > 0: the prefill GEMM's operand layout (xq in MFMA fragment order, xs [k/32][mp]);
+// else row-major xq [m][k], xs [m][k/32].
+const char *launch_quant_act(const float *x, int m, int64_t k, int8_t *xq, float *xs, hipStream_t s, int mp = 0);
+// Tokens of the prefill GEMM's activation layout: m rounded up to its 128-token tile.
+inline int64_t gemm_tokens(int64_t m) { return (m + 127) / 128 * 128; }
 // plane: the registered pre-expanded plane of w (h and l bytes in MFMA fragment order, see
 // qmm_plane_bytes), or nullptr for the in-kernel expansion of the codes.
+// frag: xq / xs are in the GEMM's operand layout (launch_quant_act with mp); else row-major.
 const char *launch_gemm_q6k(const qmv_weights *w, int m, const int8_t *plane, const int8_t *xq, const float *xs,
-                            float *y, int32_t *partials, hipStream_t s);
+                            float *y, int32_t *partials, hipStream_t s, bool frag = false);
 const char *launch_expand_q6k(const qmv_weights *w, int8_t *plane, hipStream_t s);
 // Bytes of the pre-expanded q6_K plane of an n x k matrix (32-row groups in MFMA fragment
 // order, h and l bytes).

@@ -200,11 +200,13 @@ int qmm_quant_act(const float *x, int32_t m, int64_t k, int8_t *xq, float *xs, v
 int qmv_read_ceiling(const void *p, int64_t bytes, uint32_t *sink, void *stream);
 
 /* Host only.  Workspace bytes qmm_gemm needs for m activation rows: the int8 activations
- * xq [m][k] and their per-32 scales xs [m][k/32] (at a 256-byte aligned offset), the
- * activation side of the q6_K int8 contraction ("57 · r54 — MINFER_MMQ_Q6K_EXP", §2.1:
- * the kernel contracts int8 weights against int8 activations).  The caller allocates
- * it; the library allocates nothing.  Negative QMV_ERR_* code (NULL, FORMAT for a format
- * other than q6_K, SHAPE, BATCH for m < 1) on a bad descriptor. */
+ * and their per-32 scales in the GEMM's operand layout (with mp = m rounded up to a multiple
+ * of 128: xq in int8 MFMA fragment order, [mp/32][k/32][64 lanes][16 B], lane l holding token
+ * 32 g + l % 32 and k = 32 c + 16 (l / 32) .. + 15, mp * k bytes; then at a 256-byte aligned
+ * offset xs fp32 [k/32][mp]), the activation side of the q6_K int8 contraction ("57 · r54 —
+ * MINFER_MMQ_Q6K_EXP", §2.1: the kernel contracts int8 weights against int8 activations).
+ * The caller allocates it; the library allocates nothing.  Negative QMV_ERR_* code (NULL,
+ * FORMAT for a format other than q6_K, SHAPE, BATCH for m < 1) on a bad descriptor. */
 int64_t qmm_workspace_bytes(const qmv_weights *w, int32_t m);
 
 /*
@@ -214,7 +216,8 @@ int64_t qmm_workspace_bytes(const qmv_weights *w, int32_t m);
  * then scaled and accumulated in fp32 ("57 · r54 — MINFER_MMQ_Q6K_EXP", §2.1: the
  * in-kernel ql/qh expansion into centred int8).
  *   w: QMV_Q6_K only; x: fp32 [m][k]; y: fp32 [m][n]; ws: device workspace of at least
- *   qmm_workspace_bytes(w, m) bytes (holds xq and xs; contents on return unspecified).
+ *   qmm_workspace_bytes(w, m) bytes, 256-byte aligned; on return it holds the quantized
+ *   activations in the layout qmm_workspace_bytes describes (see qmm_gemm_ws).
  *   Runs qmm_quant_act, then the contraction.  m >= 1 (at most 65535 * 128); k % 256 == 0
  *   and k <= 20480 (each workgroup stages its 64 rows' d values for all of k in LDS beside
  *   a 54 KiB operand ring); QMV_ERR_LIMIT beyond.
@@ -238,6 +241,15 @@ int qmm_gemm(const qmv_weights *w, int32_t m, const float *x, float *y, void *ws
  */
 #define QMV_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
 int qmm_gemm_noalloc(const qmv_weights *w, int32_t m, const float *x, float *y, void *stream);
+
+/*
+ * The contraction of qmm_gemm alone, on the quantized activations a previous qmm_gemm with
+ * the same m and k left in ws: one quantization of the activations serves every q6_K weight
+ * matrix that multiplies them (the projections of one layer).  ws is read only.
+ *   Errors: as qmm_gemm (QMV_ERR_WORKSPACE when ws is NULL or smaller than
+ *   qmm_workspace_bytes(w, m)).
+ */
+int qmm_gemm_ws(const qmv_weights *w, int32_t m, const void *ws, int64_t ws_bytes, float *y, void *stream);
 
 /* The contraction of qmm_gemm alone, on already quantized activations
  * (xq int8 [m][k], xs fp32 [m][k/32]). */

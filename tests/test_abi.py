@@ -98,8 +98,14 @@ def test_calls_reject_bad_arguments_before_any_gpu_work():
     assert L.qmm_gemm(w.ref, 4, 1 << 20, 1 << 20, 1 << 20, 1 << 20, None) == -3   # q4_0 has no GEMM
     q6 = _fake(qmv.Q6_K, 8, 256)
     need = L.qmm_workspace_bytes(q6.ref, 4)
-    assert need == 4 * 256 + 4 * 8 * 4
+    # the GEMM's activation layout pads the tokens to its 128-token tile: xq 128 x 256 int8,
+    # then xs fp32 [256 / 32][128]
+    assert need == 128 * 256 + 8 * 128 * 4
+    assert L.qmm_workspace_bytes(q6.ref, 129) == 256 * 256 + 8 * 256 * 4
     assert L.qmm_gemm(q6.ref, 4, 1 << 20, 1 << 20, 1 << 20, need - 1, None) == -7
+    assert L.qmm_gemm_ws(q6.ref, 4, 1 << 20, need - 1, 1 << 20, None) == -7
+    assert L.qmm_gemm_ws(q6.ref, 4, (1 << 20) + 16, need, 1 << 20, None) == -5   # ws not 256-aligned
+    assert L.qmm_gemm_ws(q6.ref, 4, 1 << 20, need, None, None) == -1
     assert L.qmm_quant_act(1 << 20, 2, 48, 1 << 20, 1 << 20, None) == -2
     assert L.qmv_moe_ffn(None, None, None, 1, None, 1, None, 0, None, None, None) == -1
     g, u, d = _fake(qmv.CB4, 256, 512), _fake(qmv.CB4, 256, 512), _fake(qmv.CB4, 512, 256)

@@ -179,12 +179,12 @@ def test_gemm_with_plane_is_byte_identical(qmv, monkeypatch, n, k, m, force):
     w, x, W, xd = _setup(qmv, n, k, m, seed=n + 7 * m)
     xq, xs = qmv.quant_act(xd)
     y0 = qmv.gemm_q8(W, xq, xs)
-    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split"
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.rowmajor-act"
     p0 = qmv.partials(W, xq)
     qmv.register_plane(W)
     try:
         y1 = qmv.gemm_q8(W, xq, xs)
-        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.rowmajor-act.plane"
         p1 = qmv.partials(W, xq)
         assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.partials.plane"
         y2 = qmv.gemm(W, xd)
@@ -192,7 +192,7 @@ def test_gemm_with_plane_is_byte_identical(qmv, monkeypatch, n, k, m, force):
     finally:
         qmv.unregister_plane(W)
     y3 = qmv.gemm_q8(W, xq, xs)
-    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split"
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.rowmajor-act"
     torch.cuda.synchronize()
     y0, y1, y2, y3 = (t.cpu().numpy().view(np.int32) for t in (y0, y1, y2, y3))
     assert np.array_equal(y0, y1) and np.array_equal(y0, y2) and np.array_equal(y0, y3)
@@ -215,16 +215,16 @@ def test_plane_labels_opt_out_and_fallback(qmv, monkeypatch):
     qmv.register_plane(W)
     assert qmv.last_path() == "plane.q6k(exp=off)"
     y_off = qmv.gemm_q8(W, xq, xs)
-    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split(exp=off)"
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.rowmajor-act(exp=off)"
     monkeypatch.delenv("QMV_Q6K_EXP")
     # registered for 96 rows; a descriptor over the same codes with 95 rows must not use it
     qmv.register_plane(W)
     try:
         W95 = qmv.QWeights(synth.FMT_Q6_K, n - 1, k, W.planes)
         y95 = qmv.gemm_q8(W95, xq, xs)
-        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split(fallback!)"
+        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.rowmajor-act(fallback!)"
         y_plane = qmv.gemm_q8(W, xq, xs)
-        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.rowmajor-act.plane"
     finally:
         qmv.unregister_plane(W)
     torch.cuda.synchronize()
@@ -276,9 +276,39 @@ def test_collected_weights_leave_no_stale_plane(qmv):
     w2 = synth.gen_weights(synth.FMT_Q6_K, n, k, seed=12)
     W2 = qweights(synth.FMT_Q6_K, n, k, w2)
     y = qmv.gemm_q8(W2, xq, xs)
-    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split"
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.rowmajor-act"
     torch.cuda.synchronize()
     yr, b = oracle.q6k_gemm_pairs(oracle.Mat(oracle.Q6_K, n, k, w2), *oracle.quant_act(x),
                                   *[a.ravel() for a in np.meshgrid(np.arange(m), np.arange(n), indexing="ij")])
     assert_parity(y.cpu().numpy().reshape(1, -1), yr[None, :], b[None, :], "gemm after a collected plane")
     print("codes address reused:", W2.planes["ql"].data_ptr() == addr)
+
+
+def test_gemm_ws_reuses_the_quantized_activations(qmv):
+    # one quantization serves a second matrix: gemm_ws on the workspace that gemm(W1, x) left
+    # equals gemm(W2, x) bit for bit, with and without W2's plane; row-major activations
+    # (gemm_q8) give the same bytes too
+    import torch
+    n, k, m = 200, 1024, 150
+    w1, x, W1, xd = _setup(qmv, n, k, m, seed=21)
+    w2 = synth.gen_weights(synth.FMT_Q6_K, n + 37, k, seed=22)
+    W2 = qweights(synth.FMT_Q6_K, n + 37, k, w2)
+    ws = torch.empty(qmv.workspace_bytes(W1, m), dtype=torch.uint8, device="cuda")
+    qmv.gemm(W1, xd, ws=ws)
+    y2 = qmv.gemm_ws(W2, ws, m=m)
+    assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split"
+    ref = qmv.gemm(W2, xd)
+    xq, xs = qmv.quant_act(xd)
+    y8 = qmv.gemm_q8(W2, xq, xs)
+    qmv.register_plane(W2)
+    try:
+        y3 = qmv.gemm_ws(W2, ws, m=m)
+        assert qmv.last_path() == "gemm.q6k.mfma-i8-32x32x32.hl-split.plane"
+    finally:
+        qmv.unregister_plane(W2)
+    torch.cuda.synchronize()
+    ref = ref.cpu().numpy().view(np.int32)
+    for y in (y2, y3, y8):
+        assert np.array_equal(y.cpu().numpy().view(np.int32), ref)
+    yr, b, _, _ = oracle.q6k_gemm(oracle.Mat(oracle.Q6_K, n + 37, k, w2), x, nthreads=oracle.max_threads())
+    assert_parity(y2.cpu().numpy(), yr, b, "gemm_ws")
