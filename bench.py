@@ -226,6 +226,17 @@ class ReadCeiling:
     def ms(self, nbytes):
         return self.graph(nbytes).time()
 
+    def graph_uncached(self, nbytes, count=60):
+        """A fresh graph (captured under the current forced path) over the same rotation."""
+        b16 = (nbytes + 15) // 16 * 16
+        copies = max(2, self.buf.numel() // b16)
+        q = self.qmv
+
+        def fn(i):
+            q.read_ceiling(self.buf[(i % copies) * b16:(i % copies + 1) * b16], self.sink)
+            CENSUS.note(q)
+        return Graph(q, fn, count)
+
 
 # ------------------------------------------------------------------ workloads
 
@@ -671,6 +682,21 @@ def main():
         ms = med([Graph(qmv, rd, 5).time() for _ in range(3)])
         full["read_ceiling_4GiB_GBps"] = round(big.numel() / ms / 1e6, 1)
         del big
+        # the ceiling's own check: persistent grids with 2 or 4 loads in flight per lane
+        # against one load per thread, at the primary shapes' sizes
+        sweep = {}
+        for n, k in LLAMA:
+            nb = qmv.weight_bytes(synth.FMT_Q4_0, n, k)
+            row = {}
+            for variant in ("", "read-ceiling.persistent-u2", "read-ceiling.persistent-u4"):
+                os.environ["QMV_FORCE_PATH"] = variant
+                try:
+                    g = ReadCeiling.graph_uncached(ceiling, nb)
+                    row[g.labels[-1]] = round(nb / med([g.time() for _ in range(3)]) / 1e6, 1)
+                finally:
+                    os.environ.pop("QMV_FORCE_PATH", None)
+            sweep[f"{n}x{k}"] = row
+        full["read_ceiling_variants_GBps"] = sweep
     if not a.no_cpu:
         say("bench: timing the CPU oracle")
         full["cpu_baseline"] = cpu_baseline(a.cpu_seconds)

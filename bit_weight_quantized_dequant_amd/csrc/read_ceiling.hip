@@ -10,6 +10,14 @@
 // Each thread issues U loads in a stride of WG (so a workgroup reads one contiguous
 // WG * U * 16-byte piece), XOR-folds them, and writes only if the fold equals a sentinel:
 // the stores almost never happen, but the loads cannot be removed.
+//
+// A persistent variant (a grid of 4 workgroups per CU walking the buffer with U = 2 or 4
+// 16-byte loads in flight per lane, chosen with the forced path "read-ceiling.persistent-u2"
+// or "-u4") serves as the check that more loads in flight do not raise the ceiling: on
+// MI355X at 9-60 MB it is never faster than one load per thread (both follow
+// about 1.8 us + bytes / 7.5 TB/s).
+#include <cstring>
+
 #include "device_common.h"
 #include "qmv_internal.h"
 
@@ -35,10 +43,39 @@ __global__ void __launch_bounds__(WG) read_ceiling_kernel(const uint4 *__restric
     if (f == 0x9E3779B9u) sink[0] = f;
 }
 
+template <int PU>
+__global__ void __launch_bounds__(WG) read_ceiling_persistent_kernel(const uint4 *__restrict__ p, int64_t n16,
+                                                                     uint32_t *__restrict__ sink) {
+    uint32_t f = 0;
+    const int64_t step = (int64_t)gridDim.x * WG * PU;
+    for (int64_t base = (int64_t)blockIdx.x * (WG * PU) + threadIdx.x; base < n16; base += step) {
+        uint4 v[PU];
+#pragma unroll
+        for (int u = 0; u < PU; u++) {
+            int64_t i = base + (int64_t)u * WG;
+            i = i < n16 ? i : n16 - 1;
+            v[u] = ld_stream16(p + i);
+        }
+#pragma unroll
+        for (int u = 0; u < PU; u++) f ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (f == 0x9E3779B9u) sink[0] = f;
+}
+
 }  // namespace
 
 const char *launch_read_ceiling(const void *p, int64_t bytes, uint32_t *sink, hipStream_t s) {
     const int64_t n16 = bytes / 16;
+    const char *fp = forced_path();
+    if (strncmp(fp, "read-ceiling.persistent-u", 25) == 0) {
+        const unsigned grid = (unsigned)device_info().num_cus * 4;
+        if (strcmp(fp + 25, "4") == 0) {
+            hipLaunchKernelGGL(read_ceiling_persistent_kernel<4>, dim3(grid), dim3(WG), 0, s, (const uint4 *)p, n16, sink);
+            return "read-ceiling.persistent-u4";
+        }
+        hipLaunchKernelGGL(read_ceiling_persistent_kernel<2>, dim3(grid), dim3(WG), 0, s, (const uint4 *)p, n16, sink);
+        return "read-ceiling.persistent-u2";
+    }
     const int64_t blocks = (n16 + WG * U - 1) / (WG * U);
     if (blocks > INT32_MAX) return nullptr;
     hipLaunchKernelGGL(read_ceiling_kernel, dim3((unsigned)blocks), dim3(WG), 0, s, (const uint4 *)p, n16, sink);
