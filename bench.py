@@ -64,7 +64,64 @@ def parse():
                     help="comma-separated secondary workloads (also: q4_0_q8)")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "bench_full.json"),
                     help="where the full record is written")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn the counter CSVs of two rocprofv3 --pmc runs (FETCH_SIZE, then "
+                         "WRITE_SIZE) of `bench.py --only-primary --copy-ref` into the dominant kernel's "
+                         "traffic record under profiles/")
     return ap.parse_args()
+
+
+TRAFFIC_RECORD = os.path.join("profiles", "q4_0_gemv_4096x11008_traffic.json")
+TRAFFIC_KERNEL = "gemv_q4_0_kernel<512, 1, 6, 0, true, 1>"  # the 4096x11008 batch-1 launch
+TRAFFIC_SOURCES = ["bit_weight_quantized_dequant_amd/csrc/gemv_q4_0.hip",
+                   "bit_weight_quantized_dequant_amd/csrc/device_common.h"]
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """HBM bytes per launch of the dominant kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch, averaged over its launches), each scaled by what the same counter reads for
+    the 256 MiB device copy of --copy-ref (256 MiB read, 256 MiB written)."""
+    import csv
+    import hashlib
+
+    def per_kernel(path, counter):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+    f, w = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    kern = [k for k in f if TRAFFIC_KERNEL in k.replace("void ", "").replace("qmv::(anonymous namespace)::", "")]
+    copy = [k for k in f if "copy" in k.lower()]
+    if len(kern) != 1 or not copy:
+        raise SystemExit(f"traffic-summary: kernel {kern!r} / copy {copy!r} not found")
+    kern, copy = kern[0], max(copy, key=lambda k: f[k][0])
+    ref = 256 << 20
+    fetch_scale = ref / 1024 / f[copy][0]
+    write_scale = ref / 1024 / w[copy][0]
+    traffic = round((f[kern][0] * fetch_scale + w[kern][0] * write_scale) * 1024)
+    rec = {
+        "kernel": f"{TRAFFIC_KERNEL} at 4096x11008 (q4_0 GEMV, batch 1, fp32 x)",
+        "sources_sha256": hashlib.sha256(b"".join(open(os.path.join(ROOT, p), "rb").read()
+                                                  for p in TRAFFIC_SOURCES)).hexdigest(),
+        "sources": TRAFFIC_SOURCES,
+        "launches_sampled": [f[kern][1], w[kern][1]],
+        "FETCH_SIZE_KiB_per_launch": round(f[kern][0], 1),
+        "WRITE_SIZE_KiB_per_launch": round(w[kern][0], 1),
+        "copy_reference": {"bytes_read": ref, "bytes_written": ref, "FETCH_SIZE_KiB": round(f[copy][0], 3),
+                           "WRITE_SIZE_KiB": round(w[copy][0], 3)},
+        "fetch_scale": round(fetch_scale, 4),
+        "write_scale": round(write_scale, 4),
+        "traffic_bytes_per_launch": traffic,
+        "algorithmic_bytes_per_launch": 4096 * 11008 // 32 * 18 + 11008 * 4 + 4096 * 4,
+        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 bench.py "
+                   "--only-primary --copy-ref --steps 8 --warmup 2 --repeats 1 --no-cpu",
+    }
+    with open(os.path.join(ROOT, TRAFFIC_RECORD), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
 
 
 T0 = time.perf_counter()
@@ -484,7 +541,7 @@ def recorded_traffic():
     """HBM bytes per launch of the dominant kernel from the committed PMC record, or None
     when the kernel's sources changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "q4_0_gemv_4096x11008_traffic.json")
+    path = os.path.join(ROOT, TRAFFIC_RECORD)
     try:
         rec = json.load(open(path))
         h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])).hexdigest()
@@ -560,6 +617,9 @@ def cpu_baseline(seconds):
 
 def main():
     a = parse()
+    if a.traffic_summary:
+        traffic_summary(*a.traffic_summary)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
                           "(the path shards by output rows across GPUs, not measured here)"}))
