@@ -46,7 +46,7 @@ EXPERT = [(2048, 7168), (7168, 2048)]
 AQ_SHAPES = [(14336, 4096), (4096, 14336)]
 
 METRIC = "quantized GEMV HBM GB/s (% of peak); q6_K prefill GEMM int8 TOPS (% of peak)"
-DEFAULT_SECONDARY = "q6_K_gemv,q6_K_decode,q4_0_batch,batch4_other,batch8_other,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm"
+DEFAULT_SECONDARY = "q6_K_gemv,q6_K_decode,q4_0_batch,batch4_other,batch8_other,cb4_moe,aq2x8,aq3x8,aq_lut,cb8,q6_K_gemm"
 
 
 def parse():
@@ -301,7 +301,7 @@ class GemvWorkload:
     """Batch-`batch` GEMVs over `shapes` (one step = one GEMV per shape), rotating pool;
     per shape, the launch time over the cold pool and the read ceiling for its bytes."""
 
-    def __init__(self, qmv, name, label, fmt, shapes, batch, xt, steps, ceiling, warm_contrast=False):
+    def __init__(self, qmv, name, label, fmt, shapes, batch, xt, steps, ceiling, warm_contrast=False, ws=False):
         import torch
         self.qmv, self.name, self.label, self.shapes, self.batch = qmv, name, label, shapes, batch
         copies, mats = shared_pool(qmv, fmt, shapes)
@@ -312,23 +312,29 @@ class GemvWorkload:
         self.algo = [qmv.weight_bytes(fmt, n, k) + xb * batch * k + 4 * batch * n for n, k in shapes]
         self.ceiling = ceiling
         q = qmv
+        # ws: qmv_gemv_ws with a workspace per shape (the split-k kernels), else qmv_gemv
+        wss = [qmv.gemv_workspace(mats[s][0], batch) for s in range(len(shapes))] if ws else None
+
+        def gemv(s, mat):
+            if wss is not None:
+                q.gemv_ws(mat, self.xs[s], wss[s], self.ys[s])
+            else:
+                q.gemv(mat, self.xs[s], self.ys[s])
+            CENSUS.note(q)
 
         def step(i):
             for s in range(len(shapes)):
-                q.gemv(mats[s][i % copies], self.xs[s], self.ys[s])
-                CENSUS.note(q)
+                gemv(s, mats[s][i % copies])
         self.step_graph = Graph(qmv, step, steps)
         R = max(steps, 40)
         self.shape_graphs, self.warm_graphs = [], []
         for s in range(len(shapes)):
             def one(i, s=s):
-                q.gemv(mats[s][i % copies], self.xs[s], self.ys[s])
-                CENSUS.note(q)
+                gemv(s, mats[s][i % copies])
             self.shape_graphs.append(Graph(qmv, one, R))
             if warm_contrast:  # the same launches on one copy, which stays in the Infinity Cache
                 def warm(i, s=s):
-                    q.gemv(mats[s][0], self.xs[s], self.ys[s])
-                    CENSUS.note(q)
+                    gemv(s, mats[s][0])
                 self.warm_graphs.append(Graph(qmv, warm, R))
         self.paths = [g.labels[-1] for g in self.shape_graphs]
         self.runs = {"step": [], "shape": [[] for _ in shapes], "warm": [[] for _ in shapes],
@@ -685,6 +691,10 @@ def main():
             for b in bs:
                 add(GemvWorkload(qmv, f"{nm}_gemv_b{b}", f"{label} GEMV batch {b}, 14336x4096 + 4096x14336, bf16 x",
                                  fmt, AQ_SHAPES, b, synth.DT_BF16, steps2, ceiling))
+        if "aq_lut" in want:
+            add(GemvWorkload(qmv, f"{nm}_lut_gemv_b1", f"{label} GEMV batch 1 through per-slice lookup tables "
+                             "(qmv_gemv_ws, split k), 14336x4096 + 4096x14336, bf16 x",
+                             fmt, AQ_SHAPES, 1, synth.DT_BF16, steps2, ceiling, ws=True))
     for fmt, nm, label in ((synth.FMT_CB4, "cb4", "4-bit codebook"), (synth.FMT_CB8, "cb8", "8-bit codebook")):
         for b in [b for b, tag in ((4, "batch4_other"), (8, "batch8_other")) if tag in want]:
             add(GemvWorkload(qmv, f"{nm}_gemv_b{b}", f"{label} GEMV batch {b}, 2048x7168 + 7168x2048, bf16 x",

@@ -13,7 +13,7 @@ import weakref
 
 __all__ = [
     "Q4_0", "Q6_K", "CB4", "AQ2X8", "CB8", "AQ3X8", "F32", "BF16", "QmvError", "QWeights", "lib", "plane_bytes",
-    "weight_bytes", "validate", "gemv", "dequant", "quant_act", "workspace_bytes", "gemm",
+    "weight_bytes", "validate", "gemv", "gemv_workspace_bytes", "gemv_workspace", "gemv_ws", "dequant", "quant_act", "workspace_bytes", "gemm",
     "gemm_q8", "gemm_ws", "gemm_noalloc", "partials", "plane_bytes_of", "register_plane", "unregister_plane", "moe_ffn", "last_path",
     "strerror", "PLANES",
 ]
@@ -74,6 +74,10 @@ def lib():
         L.qmv_validate.argtypes = [P, I32, I32]
         L.qmv_gemv.restype = C.c_int
         L.qmv_gemv.argtypes = [P, I32, P, I32, P, P]
+        L.qmv_gemv_workspace_bytes.restype = I64
+        L.qmv_gemv_workspace_bytes.argtypes = [P, I32]
+        L.qmv_gemv_ws.restype = C.c_int
+        L.qmv_gemv_ws.argtypes = [P, I32, P, I32, P, P, I64, P]
         L.qmv_gemv_q8.restype = C.c_int
         L.qmv_read_ceiling.restype = C.c_int
         L.qmv_read_ceiling.argtypes = [P, I64, P, P]
@@ -219,6 +223,40 @@ def gemv(w: QWeights, x, y=None, stream=None):
         y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
     _need(y, (torch.float32,), (m, w.n), "y")
     _check(lib().qmv_gemv(w.ref, m, _ptr(x2), _xt_of(x2), _ptr(y), _stream(stream)), "qmv_gemv")
+    return y[0] if squeeze else y
+
+
+def gemv_workspace_bytes(w: QWeights, m: int = 1) -> int:
+    """qmv_gemv_workspace_bytes: bytes of the workspace gemv_ws needs for (w, m); 0 if none."""
+    need = lib().qmv_gemv_workspace_bytes(w.ref, m)
+    if need < 0:
+        raise QmvError(need, "qmv_gemv_workspace_bytes")
+    return need
+
+
+def gemv_workspace(w: QWeights, m: int = 1, device="cuda"):
+    """A workspace for gemv_ws (uint8 device tensor), or None if none is needed.  One
+    workspace serves any number of ordered calls of the same or smaller size."""
+    import torch
+    need = gemv_workspace_bytes(w, m)
+    return torch.empty(need, dtype=torch.uint8, device=device) if need else None
+
+
+def gemv_ws(w: QWeights, x, ws, y=None, stream=None):
+    """qmv_gemv_ws: y[m][n] = W x[m] with the split-k kernels that need the workspace ws (from
+    gemv_workspace; None when gemv_workspace_bytes is 0)."""
+    import torch
+    squeeze = x.dim() == 1
+    x2 = x.reshape(1, -1) if squeeze else x
+    m = x2.shape[0]
+    _need(x2, (torch.float32, torch.bfloat16), (m, w.k), "x")
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device=x.device)
+    _need(y, (torch.float32,), (m, w.n), "y")
+    if ws is not None:
+        _need(ws, (torch.uint8,), None, "ws")
+    wp, wn = (_ptr(ws), ws.numel()) if ws is not None else (None, 0)
+    _check(lib().qmv_gemv_ws(w.ref, m, _ptr(x2), _xt_of(x2), _ptr(y), wp, wn, _stream(stream)), "qmv_gemv_ws")
     return y[0] if squeeze else y
 
 

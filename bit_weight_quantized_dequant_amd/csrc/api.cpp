@@ -217,6 +217,32 @@ int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *
     return finish_launch("qmv_gemv", w, m, path);
 }
 
+int64_t qmv_gemv_workspace_bytes(const qmv_weights *w, int32_t m) {
+    if (!w) return QMV_ERR_NULL;
+    const int blk = block_of(w->fmt);
+    if (!blk) return QMV_ERR_FORMAT;
+    if (w->n <= 0 || w->k <= 0 || w->k % blk) return QMV_ERR_SHAPE;
+    if (m < 1 || m > QMV_MAX_BATCH) return QMV_ERR_BATCH;
+    if (w->n > INT32_MAX || w->k > INT32_MAX) return 0;
+    return aq_lut_workspace_bytes(w, m);
+}
+
+int qmv_gemv_ws(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *y, void *ws, int64_t ws_bytes,
+                void *stream) {
+    int rc = qmv_validate(w, m, xt);
+    if (rc) return rc;
+    const int64_t need = qmv_gemv_workspace_bytes(w, m);
+    if (need < 0) return (int)need;
+    if (need == 0) return qmv_gemv(w, m, x, xt, y, stream);
+    if (!x || !y) return QMV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y)) return QMV_ERR_ALIGN;
+    if (!ws || ws_bytes < need) return QMV_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QMV_ERR_ALIGN;
+    const char *path = launch_gemv_aq_lut(w, x, xt, y, ws, (hipStream_t)stream);
+    if (!path) return QMV_ERR_LIMIT;
+    return finish_launch("qmv_gemv_ws", w, m, path);
+}
+
 int qmv_gemv_q8(const qmv_weights *w, int32_t m, const int8_t *xq, const float *xs, float *y, void *stream) {
     int rc = qmv_validate(w, m, QMV_F32);
     if (rc) return rc;

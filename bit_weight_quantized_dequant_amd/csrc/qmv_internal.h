@@ -38,6 +38,11 @@ const char *launch_gemv_cb4(const qmv_weights *w, int m, const void *x, int xt, 
                             hipStream_t s);
 const char *launch_gemv_aq(const qmv_weights *w, int m, const void *x, int xt, float *y,
                            hipStream_t s);
+// Additive formats at batch 1 through per-slice lookup tables (split k, workspace ws as
+// qmv_gemv_ws describes).  aq_lut_workspace_bytes: its workspace size, 0 when (w, m) has no
+// such kernel.
+int64_t aq_lut_workspace_bytes(const qmv_weights *w, int m);
+const char *launch_gemv_aq_lut(const qmv_weights *w, const void *x, int xt, float *y, void *ws, hipStream_t s);
 const char *launch_gemv_cb8(const qmv_weights *w, int m, const void *x, int xt, float *y,
                             hipStream_t s);
 const char *launch_dequant(const qmv_weights *w, float *out, hipStream_t s);

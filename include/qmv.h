@@ -147,6 +147,36 @@ int qmv_validate(const qmv_weights *w, int32_t m, int32_t xt);
 int qmv_gemv(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *y, void *stream);
 
 /*
+ * Host only.  Workspace bytes qmv_gemv_ws needs for (w, m): 0 when its kernel for that
+ * format and batch needs none (then qmv_gemv_ws is qmv_gemv).  Today only the additive
+ * formats at m = 1 need one: one fp32 partial sum per k-slice and row, 4 * n * k / 256 bytes
+ * for AQ2X8 (k % 256 == 0) and 4 * n * k / 128 for AQ3X8 (k % 128 == 0); other k need none.
+ * Negative QMV_ERR_* code (NULL, FORMAT, SHAPE, BATCH) on a bad descriptor or m.
+ */
+int64_t qmv_gemv_workspace_bytes(const qmv_weights *w, int32_t m);
+
+/*
+ * Decode GEMV with a caller workspace: y as qmv_gemv computes it (fp32 accumulation; the
+ * order of the sums differs), by kernels that split k over workgroups.  For the additive
+ * formats at m = 1 ("Chasing x100", "The kernel is ready": the 2-bit and 3-bit additive
+ * GEMVs; "LLMs on the Xiaomi TV Box", §19.1: a lookup kernel over tables of partial dot
+ * products built from the activations): each workgroup builds, in LDS, the fp32 tables
+ * T_b[g][c] = sum_j C_b[c][j] x[8g + j] of its k-slice, sums T_b[g][code] over its rows'
+ * codes (one 4-byte lookup per code) and stores one partial per row and slice; a second
+ * kernel adds each row's partials in slice order (so the result does not depend on timing)
+ * and scales by s[n].  On MI355X this is slower than qmv_gemv's kernel at 14336 x 4096 and
+ * 4096 x 14336, which is why qmv_gemv does not use it.
+ *   w, m, x, xt, y, stream: as qmv_gemv.
+ *   ws: device, 16-byte aligned, at least qmv_gemv_workspace_bytes(w, m) bytes (NULL is
+ *   accepted when that is 0).  Nothing in it needs to start at zero.  Calls that share a
+ *   workspace must be ordered (one stream): overlapping calls race.
+ *   Errors: as qmv_gemv; QMV_ERR_WORKSPACE when the workspace is needed and ws is NULL or
+ *   ws_bytes is smaller; QMV_ERR_ALIGN when ws is not 16-byte aligned.
+ */
+int qmv_gemv_ws(const qmv_weights *w, int32_t m, const void *x, int32_t xt, float *y, void *ws, int64_t ws_bytes,
+                void *stream);
+
+/*
  * Decode GEMV over per-32 int8 activations (the integer-dot form; quantprobe LAWS.md,
  * Law 4's per-format amendment, L-15: integer dot products over quantized activations
  * recover most of the unpack cost on a standalone matvec).  xq / xs are what

@@ -210,3 +210,28 @@ def test_gemm_noalloc_argument_errors_before_any_gpu_work():
     assert qmv.workspace_bytes(_fake(qmv.Q6_K, 8, 29184), 512) > 16 * 1024 * 1024
     assert L.qmm_gemm_noalloc(_fake(qmv.Q6_K, 8, 29184).ref, 512, nz, nz, None) == -9
     assert qmv.workspace_bytes(_fake(qmv.Q6_K, 8, 28928), 512) <= 16 * 1024 * 1024
+
+
+def test_gemv_ws_sizes_and_argument_errors_before_any_gpu_work():
+    # the lookup-table GEMV's workspace: one fp32 partial per k-slice (256 weights for the
+    # 2-bit code, 128 for the 3-bit one) and row
+    L = qmv.lib()
+    nz = 1 << 20
+    a2, a3 = _fake(qmv.AQ2X8, 14336, 4096), _fake(qmv.AQ3X8, 14336, 4096)
+    assert qmv.gemv_workspace_bytes(a2, 1) == 14336 * 16 * 4
+    assert qmv.gemv_workspace_bytes(a3, 1) == 14336 * 32 * 4
+    assert qmv.gemv_workspace_bytes(a2, 4) == 0                          # batch 1 only
+    assert qmv.gemv_workspace_bytes(_fake(qmv.AQ2X8, 8, 128 * 3), 1) == 0  # k % 256
+    assert qmv.gemv_workspace_bytes(_fake(qmv.AQ3X8, 8, 128 * 3), 1) == 8 * 3 * 4
+    assert qmv.gemv_workspace_bytes(_fake(qmv.Q4_0, 8, 256), 1) == 0
+    assert L.qmv_gemv_workspace_bytes(None, 1) == -1
+    assert L.qmv_gemv_workspace_bytes(a2.ref, 0) == -6
+    assert L.qmv_gemv_workspace_bytes(_fake(qmv.AQ2X8, 8, 12).ref, 1) == -2
+    need = qmv.gemv_workspace_bytes(a2, 1)
+    assert L.qmv_gemv_ws(a2.ref, 1, nz, 0, nz, None, need, None) == -7
+    assert L.qmv_gemv_ws(a2.ref, 1, nz, 0, nz, nz, need - 1, None) == -7
+    assert L.qmv_gemv_ws(a2.ref, 1, nz, 0, nz, nz + 4, need, None) == -5   # ws not 16-byte aligned
+    assert L.qmv_gemv_ws(a2.ref, 1, nz + 4, 0, nz, nz, need, None) == -5
+    assert L.qmv_gemv_ws(a2.ref, 1, None, 0, nz, nz, need, None) == -1
+    assert L.qmv_gemv_ws(a2.ref, 1, nz, 7, nz, nz, need, None) == -4
+    assert L.qmv_gemv_ws(a2.ref, 9, nz, 0, nz, nz, need, None) == -6
