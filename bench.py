@@ -40,7 +40,7 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOPS
 POOL_BYTES = 1 << 30           # rotating pool: 4x the 256 MB Infinity Cache
-SPIN_CYCLES = 2_000_000        # ~1 ms of GPU spin ahead of each timed replay
+SPIN_CYCLES = 20_000_000       # ~10 ms of GPU spin ahead of each timed replay (a 150-launch graph takes ~1 ms to submit)
 LLAMA = [(4096, 4096), (11008, 4096), (4096, 11008)]
 EXPERT = [(2048, 7168), (7168, 2048)]
 AQ_SHAPES = [(14336, 4096), (4096, 14336)]
