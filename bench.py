@@ -46,7 +46,7 @@ EXPERT = [(2048, 7168), (7168, 2048)]
 AQ_SHAPES = [(14336, 4096), (4096, 14336)]
 
 METRIC = "quantized GEMV HBM GB/s (% of peak); q6_K prefill GEMM int8 TOPS (% of peak)"
-DEFAULT_SECONDARY = "q6_K_gemv,q6_K_decode,q4_0_batch,batch4_other,batch8_other,cb4_moe,aq2x8,aq3x8,aq_lut,cb8,q6_K_gemm"
+DEFAULT_SECONDARY = "q6_K_gemv,q6_K_decode,q4_0_batch,batch4_other,batch8_other,cb4_moe,aq2x8,aq3x8,cb8,q6_K_gemm"
 
 
 def parse():
@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--secondary", default=DEFAULT_SECONDARY,
-                    help="comma-separated secondary workloads (also: q4_0_q8)")
+                    help="comma-separated secondary workloads (also: q4_0_q8, aq_lut)")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "bench_full.json"),
                     help="where the full record is written")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
