@@ -6,7 +6,9 @@
 // with x regroups as
 //     y[n] = s[n] * sum_g sum_b T_b[g][c_b(n, g)],   T_b[g][c] = sum_{j<8} C_b[c][j] x[8g + j],
 // so with the tables T in LDS a group costs NC 4-byte lookups and NC adds, instead of NC
-// 16-byte codebook-row gathers, eight activation reads and 8 NC multiply-adds.  A table
+// 16-byte codebook-row gathers, eight activation reads and 8 NC multiply-adds ("LLMs on the
+// Xiaomi TV Box", §19.1: a lookup kernel over tables of partial dot products that are built
+// from the activations, there 16 entries per 4 activations for 1-bit weights).  A table
 // holds 256 entries per (codebook, group) and is shared by every row of the matrix: each
 // workgroup builds the part it needs, and the more rows it serves the less the build costs
 // per row.
