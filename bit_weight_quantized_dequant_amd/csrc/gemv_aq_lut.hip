@@ -30,8 +30,9 @@
 // adjacent slices share cache lines of the code rows.
 //
 // Measured on MI355X this is slower than the streaming kernel of gemv_aq.hip at the
-// 14336 x 4096 and 4096 x 14336 shapes (the partials' round trip costs more than the lookups
-// save), so qmv_gemv keeps that kernel; qmv_gemv_ws runs this one.
+// 14336 x 4096 and 4096 x 14336 shapes (table build, lookups and the partials' round trip
+// together take longer than decoding each group directly), so qmv_gemv keeps that kernel;
+// qmv_gemv_ws runs this one.
 #include "device_common.h"
 #include "qmv_internal.h"
 
