@@ -420,10 +420,11 @@ const char *launch_gemv_q4_0(const qmv_weights *w, int m, const void *x, int xt,
         return m >= 3 ? "q4_0.lds-x-chunked.fmac" : "q4_0.lds-x-chunked.fma-mix";
     }
     // batch 1: two rows per wave (each staged activation block read once for both) while both
-    // rows' blocks fit in registers (bpl <= 4); one row per wave otherwise, on request (test
-    // override) and for the reference variant
+    // rows' blocks fit in registers (bpl <= 4) and the matrix has at most 32 rows per CU; one
+    // row per wave otherwise (11008 x 4096: 7.71 against 7.85 us; 4096 x 4096: 4.26 against
+    // 4.21), on request (test override) and for the reference variant
     const bool cvt = strcmp(fp, "q4_0.cvt") == 0 && xt == QMV_F32;
-    const bool r1 = cvt || strcmp(fp, "q4_0.r1") == 0 || bpl > 4;
+    const bool r1 = cvt || strcmp(fp, "q4_0.r1") == 0 || bpl > 4 || n > 32 * (int64_t)device_info().num_cus;
     const size_t lds = bpl <= 2 ? lds_bytes(256, 1, bpl) : lds_bytes(512, 1, bpl);
     if ((int64_t)lds > device_info().lds_per_block) return nullptr;
     bool ok;

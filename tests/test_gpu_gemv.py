@@ -48,14 +48,17 @@ def run_case(qmv, fmt, n, k, m, xt, seed, rows=None, expect_path=None):
 Q4_SMALL = [(1, 32), (7, 64), (64, 2048 + 160), (130, 4096), (33, 11008), (300, 2048 * 8)]
 
 
-def q4_path(m, k):
+def q4_path(m, k, n=1):
     # batches and rows longer than 16384 go through the K-chunked kernel; batch 1 through the
-    # one-shot kernel, two rows per wave while the blocks per lane are at most 4
+    # one-shot kernel, two rows per wave while the blocks per lane are at most 4 and the
+    # matrix has at most 32 rows per CU
+    import torch
     bpl = -(-(k // 32) // 64)
     if bpl > 8 or m > 1:
         # from three batch rows up the weights are expanded to fp32 once per block
         return "q4_0.lds-x-chunked.fmac" if m >= 3 else "q4_0.lds-x-chunked.fma-mix"
-    return "q4_0.lds-x.fma-mix.2row" if bpl <= 4 else "q4_0.lds-x.fma-mix"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return "q4_0.lds-x.fma-mix.2row" if bpl <= 4 and n <= 32 * cus else "q4_0.lds-x.fma-mix"
 
 
 @pytest.mark.parametrize("n,k", Q4_SMALL)
@@ -82,7 +85,7 @@ def test_q4_0_two_rows_per_wave_tails(qmv, n, k, m):
 
 @pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096), (4096, 11008)])
 def test_q4_0_full_size_all_rows(qmv, n, k):
-    run_case(qmv, synth.FMT_Q4_0, n, k, 1, synth.DT_F32, seed=0)
+    run_case(qmv, synth.FMT_Q4_0, n, k, 1, synth.DT_F32, seed=0, expect_path=q4_path(1, k, n))
 
 
 @pytest.mark.parametrize("m", [2, 4, 8])
