@@ -159,3 +159,23 @@ def test_gemv_ws_without_a_lookup_kernel_is_gemv(qmv):
         torch.cuda.synchronize()
         assert qmv.last_path() == p0
         assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("scale", [1e-30, 1e-6, 1.0, 3e4, 1e7, 1e30])
+def test_lut_activation_magnitudes(qmv, fmt, scale):
+    # the tables are built from x scaled by a power of two per slice and split into two fp16
+    # halves: activations far outside fp16's range, a slice of zeros and a slice whose values
+    # span many binades must all stay within the bound
+    import torch
+    n, k = 600, 2048
+    w = synth.gen_weights(fmt, n, k, seed=21)
+    x = synth.gen_x(1, k, synth.DT_F32, seed=21) * np.float32(scale)
+    x[0, 256:512] = 0.0                                    # an all-zero slice
+    x[0, 512:768] *= np.logspace(-6, 6, 256).astype(np.float32)  # one slice over 12 decades
+    x = x.astype(np.float32)
+    W = qweights(fmt, n, k, w)
+    y = qmv.gemv_ws(W, torch.from_numpy(x).cuda(), qmv.gemv_workspace(W, 1))
+    torch.cuda.synchronize()
+    yr, b = oracle.gemv(oracle.Mat(fmt, n, k, w), x, synth.DT_F32, nthreads=oracle.max_threads())
+    assert_parity(y.cpu().numpy(), yr, b, f"fmt={fmt} x scale {scale:g}")
